@@ -1,0 +1,402 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for the INT4 group-quantized
+ * routed-expert MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library may link, load
+ * or call this file.  Only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no code, header, table
+ * or helper with the HIP path; the two meet only at the documented byte
+ * format of their inputs.
+ *
+ * Sources (the web pages this method is described on):
+ *   [VO]  "Running 125B MoE on Three 3090s - vLLM Optimization Edition",
+ *         section 3.3 (small GEMVs), sub-section "MoE block (decode-05)";
+ *         sub-section "Hyper-connection (decode-04)" for the pack-quantized
+ *         word layout.
+ *   [VE]  "Running 125B MoE on Three 3090s - vLLM Edition", section 1
+ *         (shape of the model) and section 2 (bit allocation).
+ *   [MC]  Model card "Qwen3.8-Flash-Next-INT4-Mixed-AutoRound", table
+ *         "What is quantized".
+ *
+ * Everything is computed straight from its definition, in double precision,
+ * one output at a time.  Weights are dequantized on the fly as
+ * code * scale for every multiply; nothing is blocked, fused or reordered.
+ * The only concession to run time is an OpenMP loop over independent
+ * (token, expert) pairs, which does not change any arithmetic.
+ *
+ * Readings where the pages leave a step open (each listed with its reason
+ * in the design notes of the repository):
+ *   - INT4 words hold 8 codes, element k of a row in nibble k%8 of word
+ *     k/8, least significant nibble first, stored as code+8 (by analogy
+ *     with the INT8 layout of [VO] decode-04: least significant byte
+ *     first, stored as value+128).
+ *   - Scales are bf16, one per (output row, 128 consecutive inputs),
+ *     symmetric, no zero point ([MC], group A).
+ *   - Logits are accumulated exactly enough in fp64 and then rounded once to
+ *     fp32; expert selection is made on those fp32 values (the GPU kernel's
+ *     precision).  Ties select the lower expert id ([VO] decode-05).
+ *   - Fused gate/up: rows [0, I) are the gate (SiLU applied), rows [I, 2I)
+ *     the up projection.
+ *   - INT6 (shared expert): 32 codes packed tightly in six 32-bit words,
+ *     code i in bits [6i, 6i+6) of the little-endian 192-bit block, stored
+ *     as code+32; group 64 ([VO] decode-05, [MC] group B).
+ *   - The shared expert is added as sigmoid(gate logit) * shared output,
+ *     the gate logit being one extra bf16 router row ([VO] decode-05).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 is the upper half of an IEEE-754 binary32; widening is exact. */
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------------
+ * Unpacking ([VO] decode-04 layout by analogy; [MC] group A)
+ * ------------------------------------------------------------------- */
+
+/* Signed INT4 code of element k of one packed row. */
+int oracle_int4_code(const int32_t *row_words, int64_t k)
+{
+    uint32_t word = (uint32_t)row_words[k / 8];
+    int nibble = (int)((word >> (4 * (k % 8))) & 0xFu);
+    return nibble - 8;
+}
+
+/* Signed INT6 code of element k of one packed row (32 codes per 6 words). */
+int oracle_int6_code(const int32_t *row_words, int64_t k)
+{
+    const uint32_t *block = (const uint32_t *)row_words + (k / 32) * 6;
+    int i = (int)(k % 32);
+    int bit = 6 * i;                 /* first bit inside the 192-bit block */
+    int value = 0;
+    for (int b = 0; b < 6; ++b) {    /* gather the six bits one at a time */
+        int pos = bit + b;
+        uint32_t w = block[pos / 32];
+        value |= (int)((w >> (pos % 32)) & 1u) << b;
+    }
+    return value - 32;
+}
+
+/* Dequantized weight W[n][k] = code * scale[n][k / group]. */
+static double int4_weight(const int32_t *packed, const uint16_t *scales,
+                          int64_t n, int64_t K, int64_t group, int64_t k)
+{
+    const int32_t *row = packed + n * (K / 8);
+    double scale = bf16_to_double(scales[n * (K / group) + k / group]);
+    return (double)oracle_int4_code(row, k) * scale;
+}
+
+static double int6_weight(const int32_t *packed, const uint16_t *scales,
+                          int64_t n, int64_t K, int64_t group, int64_t k)
+{
+    const int32_t *row = packed + n * (K / 32 * 6);
+    double scale = bf16_to_double(scales[n * (K / group) + k / group]);
+    return (double)oracle_int6_code(row, k) * scale;
+}
+
+/* Whole-matrix dequantization (used by the self-tests). W is [rows][K]. */
+void oracle_dequant_int4(const int32_t *packed, const uint16_t *scales,
+                         int64_t rows, int64_t K, int64_t group, double *W)
+{
+    for (int64_t n = 0; n < rows; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            W[n * K + k] = int4_weight(packed, scales, n, K, group, k);
+}
+
+void oracle_dequant_int6(const int32_t *packed, const uint16_t *scales,
+                         int64_t rows, int64_t K, int64_t group, double *W)
+{
+    for (int64_t n = 0; n < rows; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            W[n * K + k] = int6_weight(packed, scales, n, K, group, k);
+}
+
+/* ---------------------------------------------------------------------
+ * Router ([VE] section 2 and [MC]: the router stays bf16)
+ * ------------------------------------------------------------------- */
+
+/* logits[t][e] = sum_h x[t][h] * Wr[e][h], summed in fp64, then rounded
+ * once to fp32 (the precision the selection is made in). */
+void oracle_router_logits(const uint16_t *x, const uint16_t *router_w,
+                          int64_t T, int64_t H, int64_t E, float *logits)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h)
+                acc += bf16_to_double(x[t * H + h]) *
+                       bf16_to_double(router_w[e * H + h]);
+            logits[t * E + e] = (float)acc;
+        }
+}
+
+/* ---------------------------------------------------------------------
+ * Top-k selection and renormalised softmax ([VO] decode-05)
+ * ------------------------------------------------------------------- */
+
+/* Strict order on experts: larger logit first, equal logits by lower id. */
+static int ranks_before(float la, int a, float lb, int b)
+{
+    if (la != lb)
+        return la > lb;
+    return a < b;
+}
+
+/* For each token: ids[t][0..k) are the k highest logits, in descending
+ * order (ties to the lower id), found by brute force: an expert is chosen
+ * iff fewer than k experts rank before it; its position is that count.
+ * weights[t][j] = softmax over all E experts, renormalised over the chosen
+ * k (the page notes this equals a softmax over only the chosen logits). */
+void oracle_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t k,
+                         int32_t *ids, double *weights)
+{
+    double *p = (double *)malloc((size_t)E * sizeof(double));
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+
+        for (int64_t e = 0; e < E; ++e) {
+            int64_t before = 0;
+            for (int64_t o = 0; o < E; ++o)
+                if (o != e && ranks_before(l[o], (int)o, l[e], (int)e))
+                    ++before;
+            if (before < k)
+                ids[t * k + before] = (int32_t)e;
+        }
+
+        double lmax = -INFINITY;
+        for (int64_t e = 0; e < E; ++e)
+            if ((double)l[e] > lmax)
+                lmax = (double)l[e];
+        double denom = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - lmax);
+            denom += p[e];
+        }
+        for (int64_t e = 0; e < E; ++e)
+            p[e] /= denom;
+
+        double chosen = 0.0;
+        for (int64_t j = 0; j < k; ++j)
+            chosen += p[ids[t * k + j]];
+        for (int64_t j = 0; j < k; ++j)
+            weights[t * k + j] = p[ids[t * k + j]] / chosen;
+    }
+    free(p);
+}
+
+/* ---------------------------------------------------------------------
+ * Expert histogram, offsets and stable permutation ([VO] decode-05: the
+ * block-alignment step groups token slots by expert)
+ * ------------------------------------------------------------------- */
+
+/* slot s = t*k + j.  counts[e] = #slots routed to e; offsets = exclusive
+ * prefix sum (offsets[E] = T*k); sorted_slots lists, expert by expert, the
+ * slots routed to it in increasing slot order. */
+void oracle_permutation(const int32_t *ids, int64_t T, int64_t k, int64_t E,
+                        int32_t *counts, int32_t *offsets,
+                        int32_t *sorted_slots)
+{
+    int64_t S = T * k;
+    for (int64_t e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t s = 0; s < S; ++s)
+        counts[ids[s]] += 1;
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t pos = offsets[e];
+        for (int64_t s = 0; s < S; ++s)
+            if (ids[s] == e)
+                sorted_slots[pos++] = (int32_t)s;
+    }
+}
+
+/* ---------------------------------------------------------------------
+ * SwiGLU experts ([VO] decode-05; [VE] section 1 for the shapes)
+ * ------------------------------------------------------------------- */
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* One SwiGLU expert applied to one token, INT4 weights.
+ *   g[i] = sum_h W13[i][h] x[h],   u[i] = sum_h W13[I+i][h] x[h]
+ *   a[i] = silu(g[i]) * u[i]
+ *   y[r] = sum_i W2[r][i] a[i]
+ * w13 is [2I][H], w2 is [H][I], both packed, group `group` along inputs. */
+static void expert_int4(const uint16_t *xt, const int32_t *w13p,
+                        const uint16_t *w13s, const int32_t *w2p,
+                        const uint16_t *w2s, int64_t H, int64_t I,
+                        int64_t group, double *act, double *y)
+{
+    for (int64_t i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double xv = bf16_to_double(xt[h]);
+            g += int4_weight(w13p, w13s, i, H, group, h) * xv;
+            u += int4_weight(w13p, w13s, I + i, H, group, h) * xv;
+        }
+        act[i] = silu(g) * u;
+    }
+    for (int64_t r = 0; r < H; ++r) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i)
+            acc += int4_weight(w2p, w2s, r, I, group, i) * act[i];
+        y[r] = acc;
+    }
+}
+
+/* Same expert with INT6 weights (the shared expert). */
+static void expert_int6(const uint16_t *xt, const int32_t *w13p,
+                        const uint16_t *w13s, const int32_t *w2p,
+                        const uint16_t *w2s, int64_t H, int64_t I,
+                        int64_t group, double *act, double *y)
+{
+    for (int64_t i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            double xv = bf16_to_double(xt[h]);
+            g += int6_weight(w13p, w13s, i, H, group, h) * xv;
+            u += int6_weight(w13p, w13s, I + i, H, group, h) * xv;
+        }
+        act[i] = silu(g) * u;
+    }
+    for (int64_t r = 0; r < H; ++r) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i)
+            acc += int6_weight(w2p, w2s, r, I, group, i) * act[i];
+        y[r] = acc;
+    }
+}
+
+/* Routed experts combined for a chosen subset of tokens:
+ *   out[s][r] = sum_j weights[t][j] * expert_{ids[t][j]}(x[t])[r],
+ * t = tokens[s].  Expert e's weights start at e * (rows * words per row).
+ * `nthreads` <= 0 uses the OpenMP default. */
+void oracle_experts(const uint16_t *x, const int32_t *ids,
+                    const double *weights, const int32_t *w13_packed,
+                    const uint16_t *w13_scales, const int32_t *w2_packed,
+                    const uint16_t *w2_scales, int64_t H, int64_t I,
+                    int64_t k, int64_t group, int64_t n_sel,
+                    const int32_t *tokens, double *out, int nthreads)
+{
+    int64_t pairs = n_sel * k;
+    double *y = (double *)malloc((size_t)(pairs * H) * sizeof(double));
+    int64_t w13_words = 2 * I * (H / 8), w13_nsc = 2 * I * (H / group);
+    int64_t w2_words = H * (I / 8), w2_nsc = H * (I / group);
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *act = (double *)malloc((size_t)I * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t p = 0; p < pairs; ++p) {
+            int64_t t = tokens[p / k];
+            int64_t e = ids[t * k + p % k];
+            expert_int4(x + t * H, w13_packed + e * w13_words,
+                        w13_scales + e * w13_nsc, w2_packed + e * w2_words,
+                        w2_scales + e * w2_nsc, H, I, group, act, y + p * H);
+        }
+        free(act);
+    }
+    for (int64_t s = 0; s < n_sel; ++s) {
+        int64_t t = tokens[s];
+        for (int64_t r = 0; r < H; ++r) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += weights[t * k + j] * y[(s * k + j) * H + r];
+            out[s * H + r] = acc;
+        }
+    }
+    free(y);
+}
+
+/* Shared expert for a subset of tokens: ys[s][r] = expert_int6(x[t])[r] and
+ * its gate logit glogit[s] = sum_h x[t][h] gate_w[h] (fp64). */
+void oracle_shared_int6(const uint16_t *x, const uint16_t *gate_w,
+                        const int32_t *w13_packed, const uint16_t *w13_scales,
+                        const int32_t *w2_packed, const uint16_t *w2_scales,
+                        int64_t H, int64_t I, int64_t group, int64_t n_sel,
+                        const int32_t *tokens, double *ys, double *glogit,
+                        int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *act = (double *)malloc((size_t)I * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t s = 0; s < n_sel; ++s) {
+            int64_t t = tokens[s];
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h)
+                acc += bf16_to_double(x[t * H + h]) * bf16_to_double(gate_w[h]);
+            glogit[s] = acc;
+            expert_int6(x + t * H, w13_packed, w13_scales, w2_packed,
+                        w2_scales, H, I, group, act, ys + s * H);
+        }
+        free(act);
+    }
+}
+
+/* The whole layer for a subset of tokens (routing is computed for all T
+ * tokens, since it is cheap, and returned in full).
+ *   out[s] = sum_j w[t][j] expert_{id}(x[t])  (+ sigmoid(glogit) * shared)
+ * The shared-expert arguments may all be NULL. */
+void oracle_forward(const uint16_t *x, const uint16_t *router_w,
+                    const int32_t *w13_packed, const uint16_t *w13_scales,
+                    const int32_t *w2_packed, const uint16_t *w2_scales,
+                    int64_t T, int64_t H, int64_t E, int64_t I, int64_t k,
+                    int64_t group, const uint16_t *shared_gate_w,
+                    const int32_t *sh_w13_packed, const uint16_t *sh_w13_scales,
+                    const int32_t *sh_w2_packed, const uint16_t *sh_w2_scales,
+                    int64_t sh_inter, int64_t sh_group, int64_t n_sel,
+                    const int32_t *tokens, float *logits, int32_t *ids,
+                    double *weights, double *out, int nthreads)
+{
+    oracle_router_logits(x, router_w, T, H, E, logits);
+    oracle_topk_softmax(logits, T, E, k, ids, weights);
+    oracle_experts(x, ids, weights, w13_packed, w13_scales, w2_packed,
+                   w2_scales, H, I, k, group, n_sel, tokens, out, nthreads);
+    if (shared_gate_w != NULL) {
+        double *ys = (double *)malloc((size_t)(n_sel * H) * sizeof(double));
+        double *gl = (double *)malloc((size_t)n_sel * sizeof(double));
+        oracle_shared_int6(x, shared_gate_w, sh_w13_packed, sh_w13_scales,
+                           sh_w2_packed, sh_w2_scales, H, sh_inter, sh_group,
+                           n_sel, tokens, ys, gl, nthreads);
+        for (int64_t s = 0; s < n_sel; ++s) {
+            double gate = 1.0 / (1.0 + exp(-gl[s]));
+            for (int64_t r = 0; r < H; ++r)
+                out[s * H + r] += gate * ys[s * H + r];
+        }
+        free(ys);
+        free(gl);
+    }
+}
+
+/* Threads the OpenMP runtime will use by default (for reporting). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
