@@ -1,0 +1,146 @@
+/*
+ * moe_int4.h -- C ABI of libmoe_int4.so: the INT4 symmetric group-quantized
+ * routed-expert MoE layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (as described in "Running 125B MoE on Three 3090s - vLLM
+ * Optimization Edition", section 3.3, "MoE block (decode-05)", with the shapes
+ * of "Running 125B MoE on Three 3090s - vLLM Edition", section 1, and the
+ * weight format of the model card "Qwen3.8-Flash-Next-INT4-Mixed-AutoRound",
+ * table "What is quantized", group A):
+ *
+ *   logits[t][e] = sum_h x[t][h] * router_w[e][h]         (bf16 in, fp32 sum)
+ *   ids[t][0..k) = the k largest logits, descending, ties to the lower id
+ *   w[t][j]      = softmax over the k selected logits (equal to the full
+ *                  softmax renormalised over the selection)
+ *   for each (t, j), e = ids[t][j]:
+ *     g = W1_e x_t,  u = W3_e x_t,  a = silu(g) * u,  y = W2_e a
+ *   out[t] = sum_j w[t][j] * y_j   (+ sigmoid(x_t . gate_w) * shared(x_t))
+ *
+ * Conventions shared by every entry point
+ *   - bf16 values are passed as their uint16_t bit patterns.
+ *   - All tensors are dense, row-major, in DEVICE memory, owned by the caller,
+ *     and must be 16-byte aligned.  The library never allocates, frees,
+ *     synchronises, or reads device memory from the host.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream)
+ *     and is complete when the stream is.  Calls are capturable into a HIP
+ *     graph (no host synchronisation, no memset nodes).
+ *   - Weight format (INT4, group G = 128, symmetric, no zero point):
+ *       w13_packed int32 [E][2I][H/8]  rows 0..I-1 = gate, rows I..2I-1 = up;
+ *       w13_scales bf16  [E][2I][H/G]
+ *       w2_packed  int32 [E][H][I/8];   w2_scales bf16 [E][H][I/G]
+ *     Element k of a row is nibble k%8 (bits 4(k%8)..4(k%8)+3) of word k/8,
+ *     holding code+8 for a code in [-8, 7]; weight = code * scale[row][k/G].
+ *   - Workspace: a caller-owned device buffer of at least
+ *     moe_int4_workspace_bytes() bytes.  It must be ZERO-FILLED before its
+ *     first use; every call leaves its counters at zero again when it
+ *     completes, so a workspace can be reused without clearing.  Two calls
+ *     in flight at the same time need two workspaces.
+ *
+ * Errors: every entry point returns 0 on success or a negative code.  All
+ * checks run on the host before anything is enqueued, so a failing call has
+ * done no work.  moe_int4_last_error() returns a message for the calling
+ * thread's last failure.  No C++ exception crosses this boundary.
+ */
+#ifndef MOE_INT4_H
+#define MOE_INT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_INT4_OK 0
+#define MOE_INT4_EINVAL (-1)     /* bad dimension, null pointer, top_k mismatch */
+#define MOE_INT4_EALIGN (-2)     /* a pointer is not 16-byte aligned */
+#define MOE_INT4_EWORKSPACE (-3) /* workspace smaller than required */
+#define MOE_INT4_ELAUNCH (-4)    /* the HIP runtime refused a launch */
+#define MOE_INT4_EDEVICE (-5)    /* no usable gfx950 device */
+
+/* Layer dimensions.  Limits: tokens >= 0 (0 is a no-op); 1 <= top_k <=
+ * min(experts, 32); experts <= 1024; group == 128; hidden and inter are
+ * multiples of 128 with hidden <= 8192 and inter <= 2048. */
+typedef struct moe_int4_shape {
+    int32_t tokens;  /* T */
+    int32_t hidden;  /* H */
+    int32_t experts; /* E */
+    int32_t inter;   /* I: expert intermediate size */
+    int32_t group;   /* G: quantization group along the input dimension */
+    int32_t top_k;   /* k */
+} moe_int4_shape;
+
+/* Optional always-on shared expert with INT6 weights ("MoE block (decode-05)":
+ * it is added as sigmoid(gate logit) * shared output; model card group B:
+ * INT6, group 64).  Each run of 32 codes along the input dimension is packed
+ * into six int32 words: code i (stored code+32, code in [-32, 31]) occupies
+ * bits 6i..6i+5 of the little-endian 192-bit concatenation of the six words.
+ *   gate_w     bf16  [H]               (the extra router row)
+ *   w13_packed int32 [2*inter][H/32*6]; w13_scales bf16 [2*inter][H/group]
+ *   w2_packed  int32 [H][inter/32*6];   w2_scales  bf16 [H][inter/group]
+ * group must be 64, inter a multiple of 64 and <= 2048. */
+typedef struct moe_shared_int6 {
+    const uint16_t *gate_w;
+    const int32_t *w13_packed;
+    const uint16_t *w13_scales;
+    const int32_t *w2_packed;
+    const uint16_t *w2_scales;
+    int32_t inter;
+    int32_t group;
+} moe_shared_int6;
+
+/* Bytes of workspace needed for `shape` (and `shared`, may be NULL). */
+int32_t moe_int4_workspace_bytes(const moe_int4_shape *shape,
+                                 const moe_shared_int6 *shared,
+                                 size_t *bytes);
+
+/* Routing only: router GEMV/GEMM, fp32 softmax, top-k, and the stable
+ * expert permutation ("MoE block (decode-05)": top-k with ties to the lower
+ * id, renormalisation, and the grouping of token slots by expert).
+ *   x              bf16 [T][H]        router_w bf16 [E][H]
+ *   topk_ids       int32 [T][k]  out  expert ids, descending logit
+ *   topk_w         fp32  [T][k]  out  renormalised softmax weights
+ *   expert_counts  int32 [E]     out  slots routed to each expert
+ *   expert_offsets int32 [E+1]   out  exclusive prefix sum of the counts
+ *   sorted_slots   int32 [T*k]   out  slot s = t*k + j, grouped by expert,
+ *                                     increasing s within an expert */
+int32_t moe_int4_route(const uint16_t *x, const uint16_t *router_w,
+                       const moe_int4_shape *shape, int32_t *topk_ids,
+                       float *topk_w, int32_t *expert_counts,
+                       int32_t *expert_offsets, int32_t *sorted_slots,
+                       void *workspace, size_t workspace_bytes,
+                       void *hip_stream);
+
+/* Experts under caller-given routing (ids must lie in [0, E); weights are
+ * used as given).  `shared` may be NULL; when it is set the shared expert is
+ * added with the gate logit x . shared->gate_w.  out bf16 [T][H] is
+ * overwritten (round to nearest even once, from fp32) and must not alias x. */
+int32_t moe_int4_experts(const uint16_t *x, const int32_t *topk_ids,
+                         const float *topk_w, const int32_t *w13_packed,
+                         const uint16_t *w13_scales, const int32_t *w2_packed,
+                         const uint16_t *w2_scales, const moe_int4_shape *shape,
+                         const moe_shared_int6 *shared, uint16_t *out,
+                         void *workspace, size_t workspace_bytes,
+                         void *hip_stream);
+
+/* The whole layer: routing, routed experts and (optional) shared expert.
+ * top_k must equal shape->top_k. */
+int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w,
+                         const int32_t *w13_packed, const uint16_t *w13_scales,
+                         const int32_t *w2_packed, const uint16_t *w2_scales,
+                         int32_t top_k, uint16_t *out,
+                         const moe_int4_shape *shape,
+                         const moe_shared_int6 *shared, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
+
+/* Message for the calling thread's most recent failing call ("" if none). */
+const char *moe_int4_last_error(void);
+
+/* Library version string. */
+const char *moe_int4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_INT4_H */

@@ -21,8 +21,8 @@
  * Everything is computed straight from its definition, in double precision,
  * one output at a time.  Weights are dequantized on the fly as
  * code * scale for every multiply; nothing is blocked, fused or reordered.
- * The only concession to run time is an OpenMP loop over independent
- * (token, expert) pairs, which does not change any arithmetic.
+ * The only concession to run time is OpenMP loops over independent tokens
+ * or (token, expert) pairs, which do not change any arithmetic.
  *
  * Readings where the pages leave a step open (each listed with its reason
  * in the design notes of the repository):
@@ -130,6 +130,9 @@ void oracle_dequant_int6(const int32_t *packed, const uint16_t *scales,
 void oracle_router_logits(const uint16_t *x, const uint16_t *router_w,
                           int64_t T, int64_t H, int64_t E, float *logits)
 {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
     for (int64_t t = 0; t < T; ++t)
         for (int64_t e = 0; e < E; ++e) {
             double acc = 0.0;
@@ -160,8 +163,11 @@ static int ranks_before(float la, int a, float lb, int b)
 void oracle_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t k,
                          int32_t *ids, double *weights)
 {
-    double *p = (double *)malloc((size_t)E * sizeof(double));
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
     for (int64_t t = 0; t < T; ++t) {
+        double *p = (double *)malloc((size_t)E * sizeof(double));
         const float *l = logits + t * E;
 
         for (int64_t e = 0; e < E; ++e) {
@@ -190,8 +196,8 @@ void oracle_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t k,
             chosen += p[ids[t * k + j]];
         for (int64_t j = 0; j < k; ++j)
             weights[t * k + j] = p[ids[t * k + j]] / chosen;
+        free(p);
     }
-    free(p);
 }
 
 /* ---------------------------------------------------------------------

@@ -1,0 +1,133 @@
+"""ctypes binding of libmoe_int4.so (include/moe_int4.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors are torch tensors on the current HIP device; bf16 data may be passed
+as torch.bfloat16 or as int16/uint16 bit patterns.  Work is enqueued on
+torch's current stream unless a stream is given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_int4.so")
+
+OK, EINVAL, EALIGN, EWORKSPACE, ELAUNCH, EDEVICE = 0, -1, -2, -3, -4, -5
+
+_c_void_p = ctypes.c_void_p
+_c_i32 = ctypes.c_int32
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("tokens", _c_i32), ("hidden", _c_i32), ("experts", _c_i32),
+                ("inter", _c_i32), ("group", _c_i32), ("top_k", _c_i32)]
+
+
+class MoeSharedInt6(ctypes.Structure):
+    _fields_ = [("gate_w", _c_void_p), ("w13_packed", _c_void_p), ("w13_scales", _c_void_p),
+                ("w2_packed", _c_void_p), ("w2_scales", _c_void_p),
+                ("inter", _c_i32), ("group", _c_i32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe_int4 error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m quantized_moe_router_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = _c_void_p
+        L.moe_int4_workspace_bytes.argtypes = [P, P, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_int4_route.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_int4_experts.argtypes = [P] * 11 + [ctypes.c_size_t, P]
+        L.moe_int4_forward.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_int4_last_error.restype = ctypes.c_char_p
+        L.moe_int4_version.restype = ctypes.c_char_p
+        for f in ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts", "moe_int4_forward"):
+            getattr(L, f).restype = _c_i32
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts",
+            "moe_int4_forward", "moe_int4_last_error", "moe_int4_version")
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MoeError(rc, lib().moe_int4_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def make_shape(tokens, hidden, experts, inter, top_k, group=128) -> MoeShape:
+    return MoeShape(tokens, hidden, experts, inter, group, top_k)
+
+
+def make_shared(sh: dict | None) -> MoeSharedInt6 | None:
+    """sh: dict of device tensors gate_w, w13_packed, w13_scales, w2_packed, w2_scales."""
+    if sh is None:
+        return None
+    inter = sh["w2_packed"].shape[1] // 6 * 32
+    return MoeSharedInt6(_ptr(sh["gate_w"]), _ptr(sh["w13_packed"]), _ptr(sh["w13_scales"]),
+                         _ptr(sh["w2_packed"]), _ptr(sh["w2_scales"]), inter, int(sh.get("group", 64)))
+
+
+def workspace_bytes(shape: MoeShape, shared: MoeSharedInt6 | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_int4_workspace_bytes(ctypes.byref(shape),
+                                          ctypes.byref(shared) if shared else None, ctypes.byref(n)))
+    return n.value
+
+
+def new_workspace(shape: MoeShape, shared: MoeSharedInt6 | None = None, device="cuda"):
+    """A zero-filled workspace (the library keeps its counters at zero after each call)."""
+    import torch
+    return torch.zeros(workspace_bytes(shape, shared), dtype=torch.uint8, device=device)
+
+
+def moe_int4_route(x, router_w, shape: MoeShape, topk_ids, topk_w, expert_counts,
+                   expert_offsets, sorted_slots, workspace, stream=None):
+    _check(lib().moe_int4_route(_ptr(x), _ptr(router_w), ctypes.byref(shape), _ptr(topk_ids),
+                                _ptr(topk_w), _ptr(expert_counts), _ptr(expert_offsets),
+                                _ptr(sorted_slots), _ptr(workspace), workspace.numel(),
+                                _stream(stream)))
+
+
+def moe_int4_experts(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales,
+                     shape: MoeShape, shared: MoeSharedInt6 | None, out, workspace, stream=None):
+    _check(lib().moe_int4_experts(_ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13_packed),
+                                  _ptr(w13_scales), _ptr(w2_packed), _ptr(w2_scales),
+                                  ctypes.byref(shape), ctypes.byref(shared) if shared else None,
+                                  _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def moe_int4_forward(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k: int, out,
+                     shape: MoeShape, shared: MoeSharedInt6 | None, workspace, stream=None):
+    _check(lib().moe_int4_forward(_ptr(x), _ptr(router_w), _ptr(w13_packed), _ptr(w13_scales),
+                                  _ptr(w2_packed), _ptr(w2_scales), int(top_k), _ptr(out),
+                                  ctypes.byref(shape), ctypes.byref(shared) if shared else None,
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def version() -> str:
+    return lib().moe_int4_version().decode()

@@ -1,0 +1,305 @@
+// Host side of libmoe_int4.so: argument checks, workspace map, and the
+// extern "C" entry points declared in include/moe_int4.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "common.h"
+#include "moe_int4.h"
+
+namespace moe {
+
+hipError_t launch_experts_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                               const RouteOut &ro, hipStream_t st);
+hipError_t launch_shared(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                         hipStream_t st);
+
+namespace {
+
+thread_local std::string g_error;
+
+int32_t fail(int32_t code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t route_ticket, tile_ticket, logits, ids, weights, counts, offsets, sorted_slots,
+        slot_pos, active, chunk_hist, h, ypart, shared_gate, sh_h, total;
+};
+
+Layout layout(const Dims &d)
+{
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += round_up(bytes);
+        return o;
+    };
+    const size_t S = (size_t)d.S, T = (size_t)d.T;
+    const size_t nchunks = (S + kPermChunk - 1) / kPermChunk;
+    L.route_ticket = take(4);
+    L.tile_ticket = take(4 * (size_t)(d.H / 64));
+    L.logits = take(4 * T * d.E);
+    L.ids = take(4 * S);
+    L.weights = take(4 * S);
+    L.counts = take(4 * (size_t)d.E);
+    L.offsets = take(4 * ((size_t)d.E + 1));
+    L.sorted_slots = take(4 * S);
+    L.slot_pos = take(4 * S);
+    L.active = take(4 * ((size_t)d.E + 1));
+    L.chunk_hist = take(4 * nchunks * d.E);
+    L.h = take(2 * S * d.I);
+    L.ypart = take(4 * (S + (d.sh_I ? T : 0)) * d.H);
+    L.shared_gate = take(4 * T);
+    L.sh_h = take(2 * T * (size_t)d.sh_I);
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One-time check per device that it is a gfx950 part.
+int32_t check_device()
+{
+    static std::mutex mu;
+    static int checked[64] = {0};  // 0 unknown, 1 ok, -1 bad
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(MOE_INT4_EDEVICE, "no HIP device is current");
+    std::lock_guard<std::mutex> lock(mu);
+    if (checked[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(MOE_INT4_EDEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        checked[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (checked[dev] < 0)
+            return fail(MOE_INT4_EDEVICE, "device %d is %s; this library is built for gfx950",
+                        dev, prop.gcnArchName);
+    }
+    if (checked[dev] < 0) return fail(MOE_INT4_EDEVICE, "device %d is not gfx950", dev);
+    return MOE_INT4_OK;
+}
+
+int32_t check_shape(const moe_int4_shape *s, const moe_shared_int6 *sh, Dims *d)
+{
+    if (!s) return fail(MOE_INT4_EINVAL, "shape is NULL");
+    if (s->tokens < 0 || s->tokens > (1 << 20))
+        return fail(MOE_INT4_EINVAL, "tokens=%d outside [0, 1048576]", s->tokens);
+    if (s->group != kGroup) return fail(MOE_INT4_EINVAL, "group=%d, only 128 is supported", s->group);
+    if (s->hidden <= 0 || s->hidden % 128 || s->hidden > 4096)
+        return fail(MOE_INT4_EINVAL, "hidden=%d must be a positive multiple of 128, at most 4096",
+                    s->hidden);
+    if (s->inter <= 0 || s->inter % 128 || s->inter > 1024)
+        return fail(MOE_INT4_EINVAL, "inter=%d must be a positive multiple of 128, at most 1024",
+                    s->inter);
+    if (s->experts <= 0 || s->experts > kMaxExperts)
+        return fail(MOE_INT4_EINVAL, "experts=%d outside [1, %d]", s->experts, kMaxExperts);
+    int kmax = s->experts < kMaxTopK ? s->experts : kMaxTopK;
+    if (s->top_k < 1 || s->top_k > kmax)
+        return fail(MOE_INT4_EINVAL, "top_k=%d outside [1, %d]", s->top_k, kmax);
+    d->T = s->tokens;
+    d->H = s->hidden;
+    d->E = s->experts;
+    d->I = s->inter;
+    d->k = s->top_k;
+    d->S = s->tokens * s->top_k;
+    d->sh_I = 0;
+    if (sh) {
+        if (sh->group != kShGroup)
+            return fail(MOE_INT4_EINVAL, "shared expert group=%d, only 64 is supported", sh->group);
+        if (sh->inter <= 0 || sh->inter % 128 || sh->inter > 1024)
+            return fail(MOE_INT4_EINVAL,
+                        "shared expert inter=%d must be a positive multiple of 128, at most 1024",
+                        sh->inter);
+        if (!sh->gate_w || !sh->w13_packed || !sh->w13_scales || !sh->w2_packed || !sh->w2_scales)
+            return fail(MOE_INT4_EINVAL, "a shared-expert pointer is NULL");
+        if (!aligned16(sh->gate_w) || !aligned16(sh->w13_packed) || !aligned16(sh->w13_scales) ||
+            !aligned16(sh->w2_packed) || !aligned16(sh->w2_scales))
+            return fail(MOE_INT4_EALIGN, "a shared-expert pointer is not 16-byte aligned");
+        d->sh_I = sh->inter;
+    }
+    return MOE_INT4_OK;
+}
+
+struct PtrCheck {
+    const char *name;
+    const void *p;
+};
+
+int32_t check_ptrs(std::initializer_list<PtrCheck> ps)
+{
+    for (const PtrCheck &c : ps) {
+        if (!c.p) return fail(MOE_INT4_EINVAL, "%s is NULL", c.name);
+        if (!aligned16(c.p)) return fail(MOE_INT4_EALIGN, "%s is not 16-byte aligned", c.name);
+    }
+    return MOE_INT4_OK;
+}
+
+int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
+{
+    Layout L = layout(d);
+    if (!ws) return fail(MOE_INT4_EINVAL, "workspace is NULL");
+    if (!aligned16(ws)) return fail(MOE_INT4_EALIGN, "workspace is not 16-byte aligned");
+    if (bytes < L.total)
+        return fail(MOE_INT4_EWORKSPACE, "workspace has %zu bytes, %zu needed", bytes, L.total);
+    char *b = static_cast<char *>(ws);
+    Workspace w{};
+    w.route_ticket = reinterpret_cast<uint32_t *>(b + L.route_ticket);
+    w.tile_ticket = reinterpret_cast<uint32_t *>(b + L.tile_ticket);
+    w.logits = reinterpret_cast<float *>(b + L.logits);
+    w.ids = reinterpret_cast<int32_t *>(b + L.ids);
+    w.weights = reinterpret_cast<float *>(b + L.weights);
+    w.counts = reinterpret_cast<int32_t *>(b + L.counts);
+    w.offsets = reinterpret_cast<int32_t *>(b + L.offsets);
+    w.sorted_slots = reinterpret_cast<int32_t *>(b + L.sorted_slots);
+    w.slot_pos = reinterpret_cast<int32_t *>(b + L.slot_pos);
+    w.active = reinterpret_cast<int32_t *>(b + L.active);
+    w.chunk_hist = reinterpret_cast<int32_t *>(b + L.chunk_hist);
+    w.h = reinterpret_cast<uint16_t *>(b + L.h);
+    w.ypart = reinterpret_cast<float *>(b + L.ypart);
+    w.shared_gate = reinterpret_cast<float *>(b + L.shared_gate);
+    w.sh_h = reinterpret_cast<uint16_t *>(b + L.sh_h);
+    w.bytes = L.total;
+    *out = w;
+    return MOE_INT4_OK;
+}
+
+int32_t launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(MOE_INT4_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+    return MOE_INT4_OK;
+}
+
+}  // namespace
+
+size_t workspace_size(const Dims &d) { return layout(d).total; }
+
+hipError_t launch_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                          const RouteOut &ro, hipStream_t st)
+{
+    if (d.sh_I > 0) {
+        hipError_t e = launch_shared(a, d, ws, st);
+        if (e != hipSuccess) return e;
+    }
+    return launch_experts_gemv(a, d, ws, ro, st);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_int4_version(void) { return "moe_int4 0.1 gfx950"; }
+
+const char *moe_int4_last_error(void) { return g_error.c_str(); }
+
+int32_t moe_int4_workspace_bytes(const moe_int4_shape *shape, const moe_shared_int6 *shared,
+                                 size_t *bytes)
+{
+    Dims d;
+    int32_t rc = check_shape(shape, shared, &d);
+    if (rc) return rc;
+    if (!bytes) return fail(MOE_INT4_EINVAL, "bytes is NULL");
+    *bytes = workspace_size(d);
+    return MOE_INT4_OK;
+}
+
+int32_t moe_int4_route(const uint16_t *x, const uint16_t *router_w, const moe_int4_shape *shape,
+                       int32_t *topk_ids, float *topk_w, int32_t *expert_counts,
+                       int32_t *expert_offsets, int32_t *sorted_slots, void *workspace,
+                       size_t workspace_bytes, void *hip_stream)
+{
+    g_error.clear();
+    Dims d;
+    int32_t rc = check_shape(shape, nullptr, &d);
+    if (rc) return rc;
+    if (d.T == 0) return MOE_INT4_OK;
+    rc = check_ptrs({{"x", x}, {"router_w", router_w}, {"topk_ids", topk_ids},
+                     {"topk_w", topk_w}, {"expert_counts", expert_counts},
+                     {"expert_offsets", expert_offsets}, {"sorted_slots", sorted_slots}});
+    if (rc) return rc;
+    Workspace ws;
+    if ((rc = check_workspace(d, workspace, workspace_bytes, &ws))) return rc;
+    if ((rc = check_device())) return rc;
+    RouteOut ro{topk_ids, topk_w, expert_counts, expert_offsets, sorted_slots};
+    return launched(launch_route(x, router_w, d, ws, ro, (hipStream_t)hip_stream), "route");
+}
+
+int32_t moe_int4_experts(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                         const int32_t *w13_packed, const uint16_t *w13_scales,
+                         const int32_t *w2_packed, const uint16_t *w2_scales,
+                         const moe_int4_shape *shape, const moe_shared_int6 *shared,
+                         uint16_t *out, void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    g_error.clear();
+    Dims d;
+    int32_t rc = check_shape(shape, shared, &d);
+    if (rc) return rc;
+    if (d.T == 0) return MOE_INT4_OK;
+    rc = check_ptrs({{"x", x}, {"topk_ids", topk_ids}, {"topk_w", topk_w},
+                     {"w13_packed", w13_packed}, {"w13_scales", w13_scales},
+                     {"w2_packed", w2_packed}, {"w2_scales", w2_scales}, {"out", out}});
+    if (rc) return rc;
+    if ((const void *)out == (const void *)x) return fail(MOE_INT4_EINVAL, "out aliases x");
+    Workspace ws;
+    if ((rc = check_workspace(d, workspace, workspace_bytes, &ws))) return rc;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = (hipStream_t)hip_stream;
+    RouteOut ro{const_cast<int32_t *>(topk_ids), const_cast<float *>(topk_w), ws.counts,
+                ws.offsets, ws.sorted_slots};
+    if ((rc = launched(launch_permute(d, ws, ro, st), "permute"))) return rc;
+    ExpertArgs a{x, w13_packed, w13_scales, w2_packed, w2_scales, topk_w, out,
+                 shared ? shared->gate_w : nullptr, shared ? shared->w13_packed : nullptr,
+                 shared ? shared->w13_scales : nullptr, shared ? shared->w2_packed : nullptr,
+                 shared ? shared->w2_scales : nullptr};
+    return launched(launch_experts(a, d, ws, ro, st), "experts");
+}
+
+int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w, const int32_t *w13_packed,
+                         const uint16_t *w13_scales, const int32_t *w2_packed,
+                         const uint16_t *w2_scales, int32_t top_k, uint16_t *out,
+                         const moe_int4_shape *shape, const moe_shared_int6 *shared,
+                         void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    g_error.clear();
+    Dims d;
+    int32_t rc = check_shape(shape, shared, &d);
+    if (rc) return rc;
+    if (top_k != shape->top_k)
+        return fail(MOE_INT4_EINVAL, "top_k=%d differs from shape->top_k=%d", top_k, shape->top_k);
+    if (d.T == 0) return MOE_INT4_OK;
+    rc = check_ptrs({{"x", x}, {"router_w", router_w}, {"w13_packed", w13_packed},
+                     {"w13_scales", w13_scales}, {"w2_packed", w2_packed},
+                     {"w2_scales", w2_scales}, {"out", out}});
+    if (rc) return rc;
+    if ((const void *)out == (const void *)x) return fail(MOE_INT4_EINVAL, "out aliases x");
+    Workspace ws;
+    if ((rc = check_workspace(d, workspace, workspace_bytes, &ws))) return rc;
+    if ((rc = check_device())) return rc;
+    hipStream_t st = (hipStream_t)hip_stream;
+    RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
+    if ((rc = launched(launch_route(x, router_w, d, ws, ro, st), "route"))) return rc;
+    ExpertArgs a{x, w13_packed, w13_scales, w2_packed, w2_scales, ws.weights, out,
+                 shared ? shared->gate_w : nullptr, shared ? shared->w13_packed : nullptr,
+                 shared ? shared->w13_scales : nullptr, shared ? shared->w2_packed : nullptr,
+                 shared ? shared->w2_scales : nullptr};
+    return launched(launch_experts(a, d, ws, ro, st), "experts");
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+// Internal declarations of libmoe_int4: device helpers, the workspace map and
+// the kernel launchers.  Not part of the public ABI (see include/moe_int4.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kGroup = 128;      // INT4 group along the input dimension
+constexpr int kShGroup = 64;     // INT6 group (shared expert)
+// Decode (GEMV) path for T <= kDecodeMaxTokens, grouped-GEMM path above.
+constexpr int kDecodeMaxTokens = 16;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data read exactly once (weights): non-temporal hint.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p)
+{
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// c + a.lo*b.lo + a.hi*b.hi on bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// INT4 nibbles -> bf16 without a conversion instruction.
+//
+// bf16 0x4300 is 128.0 with a zero 7-bit mantissa, so OR-ing a nibble n into
+// the mantissa gives exactly 128 + n.  Masking a word with 0x000F000F keeps
+// nibble 0 in the low half and nibble 4 in the high half, i.e. a bf16 pair
+// (128+n0, 128+n4); shifting by 4, 8, 12 first gives (n1,n5), (n2,n6),
+// (n3,n7).  A dot product over these pairs against activations arranged the
+// same way gives sum (128 + n) x; the stored nibble is code + 8, so the true
+// sum of code * x is that minus 136 * sum x.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void nib_pairs(uint32_t w, uint32_t p[4])
+{
+    const uint32_t m = 0x000F000Fu, b = 0x43004300u;
+    p[0] = (w & m) | b;
+    p[1] = ((w >> 4) & m) | b;
+    p[2] = ((w >> 8) & m) | b;
+    p[3] = ((w >> 12) & m) | b;
+}
+
+// Natural-order bf16 octet (4 dwords: (e0,e1)(e2,e3)(e4,e5)(e6,e7)) ->
+// nibble-pair order (e0,e4)(e1,e5)(e2,e6)(e3,e7).
+__device__ __forceinline__ void octet_to_pair_order(const uint32_t in[4], uint32_t out[4])
+{
+    out[0] = __builtin_amdgcn_perm(in[2], in[0], 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(in[2], in[0], 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(in[3], in[1], 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(in[3], in[1], 0x07060302u);
+}
+
+// sum over 32 (code+8+128) * x of one 16-byte chunk of 4 INT4 words, with x
+// given as 16 dwords in nibble-pair order.
+__device__ __forceinline__ float chunk_dot(const uint4 w, const uint32_t x[16])
+{
+    uint32_t p[4];
+    float acc = 0.f;
+    nib_pairs(w.x, p);
+    acc = dot2(p[0], x[0], acc); acc = dot2(p[1], x[1], acc);
+    acc = dot2(p[2], x[2], acc); acc = dot2(p[3], x[3], acc);
+    nib_pairs(w.y, p);
+    acc = dot2(p[0], x[4], acc); acc = dot2(p[1], x[5], acc);
+    acc = dot2(p[2], x[6], acc); acc = dot2(p[3], x[7], acc);
+    nib_pairs(w.z, p);
+    acc = dot2(p[0], x[8], acc); acc = dot2(p[1], x[9], acc);
+    acc = dot2(p[2], x[10], acc); acc = dot2(p[3], x[11], acc);
+    nib_pairs(w.w, p);
+    acc = dot2(p[0], x[12], acc); acc = dot2(p[1], x[13], acc);
+    acc = dot2(p[2], x[14], acc); acc = dot2(p[3], x[15], acc);
+    return acc;
+}
+
+// Load 32 natural-order bf16 activations (64 bytes) and return them in
+// nibble-pair order, plus their sum.
+__device__ __forceinline__ float load_act_chunk(const uint16_t *p, uint32_t x[16])
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    float s = 0.f;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        uint4 v = q[o];
+        uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        octet_to_pair_order(in, x + 4 * o);
+        s = dot2(in[0], 0x3F803F80u, s);  // bf16 (1.0, 1.0)
+        s = dot2(in[1], 0x3F803F80u, s);
+        s = dot2(in[2], 0x3F803F80u, s);
+        s = dot2(in[3], 0x3F803F80u, s);
+    }
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 variant for the SwiGLU activation a = silu(g) * u, which the kernels
+// keep in fp16 (11 significant bits; bf16's 8 were too coarse for a's heavy
+// tail).  fp16 0x5800 is 128.0 with mantissa step 1/8, so (n << 3) | 0x5800 is
+// exactly 128 + n for n < 128: the same exponent trick as above.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                  false);
+}
+
+// fp32 -> fp16 bits, round to nearest even, saturating at +-65504.
+__device__ __forceinline__ uint32_t f32_to_f16_sat(float f)
+{
+    f = fminf(fmaxf(f, -65504.f), 65504.f);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// INT4 word -> fp16 pairs (128+n0,128+n4) (128+n1,128+n5) (128+n2,128+n6)
+// (128+n3,128+n7).
+__device__ __forceinline__ void nib_pairs_h(uint32_t w, uint32_t p[4])
+{
+    const uint32_t m = 0x00780078u, b = 0x58005800u;
+    p[0] = ((w << 3) & m) | b;
+    p[1] = ((w >> 1) & m) | b;
+    p[2] = ((w >> 5) & m) | b;
+    p[3] = ((w >> 9) & m) | b;
+}
+
+__device__ __forceinline__ float chunk_dot_h(const uint4 w, const uint32_t x[16])
+{
+    uint32_t p[4];
+    float acc = 0.f;
+    nib_pairs_h(w.x, p);
+    acc = dot2h(p[0], x[0], acc); acc = dot2h(p[1], x[1], acc);
+    acc = dot2h(p[2], x[2], acc); acc = dot2h(p[3], x[3], acc);
+    nib_pairs_h(w.y, p);
+    acc = dot2h(p[0], x[4], acc); acc = dot2h(p[1], x[5], acc);
+    acc = dot2h(p[2], x[6], acc); acc = dot2h(p[3], x[7], acc);
+    nib_pairs_h(w.z, p);
+    acc = dot2h(p[0], x[8], acc); acc = dot2h(p[1], x[9], acc);
+    acc = dot2h(p[2], x[10], acc); acc = dot2h(p[3], x[11], acc);
+    nib_pairs_h(w.w, p);
+    acc = dot2h(p[0], x[12], acc); acc = dot2h(p[1], x[13], acc);
+    acc = dot2h(p[2], x[14], acc); acc = dot2h(p[3], x[15], acc);
+    return acc;
+}
+
+// 32 natural-order fp16 activations -> nibble-pair order, plus their sum.
+__device__ __forceinline__ float load_act_chunk_h(const uint16_t *p, uint32_t x[16])
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    float s = 0.f;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        uint4 v = q[o];
+        uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        octet_to_pair_order(in, x + 4 * o);
+        s = dot2h(in[0], 0x3C003C00u, s);  // fp16 (1.0, 1.0)
+        s = dot2h(in[1], 0x3C003C00u, s);
+        s = dot2h(in[2], 0x3C003C00u, s);
+        s = dot2h(in[3], 0x3C003C00u, s);
+    }
+    return s;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace map.  Every region is 256-byte aligned; counters first so that
+// the zero-state contract covers a fixed prefix.
+// ---------------------------------------------------------------------------
+struct Workspace {
+    // counters (must be zero between calls)
+    uint32_t *route_ticket;  // [1]
+    uint32_t *tile_ticket;   // [H / 64] (row tiles of the decode combine)
+    // routing
+    float *logits;           // [T][E]
+    int32_t *ids;            // [T][k]   (forward: internal copy)
+    float *weights;          // [T][k]
+    int32_t *counts;         // [E]
+    int32_t *offsets;        // [E+1]
+    int32_t *sorted_slots;   // [S]
+    int32_t *slot_pos;       // [S]   inverse of sorted_slots
+    int32_t *active;         // [E+1] active[0] = n_active, then expert ids
+    int32_t *chunk_hist;     // [nchunks][E]
+    // expert intermediates
+    uint16_t *h;             // [S][I] fp16, sorted order
+    float *ypart;            // [S][H] fp32, sorted order
+    float *shared_gate;      // [T] shared-expert gate logits
+    uint16_t *sh_h;          // [T][I_sh] fp16
+    size_t bytes;
+};
+
+struct Dims {
+    int T, H, E, I, k, S;
+    int sh_I;  // 0 = no shared expert
+};
+
+constexpr int kPermChunk = 1024;  // slots per chunk of the large permutation
+
+Workspace carve_workspace(void *base, const Dims &d);
+size_t workspace_size(const Dims &d);
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+struct RouteOut {
+    int32_t *ids;
+    float *weights;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *sorted_slots;
+};
+
+hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
+                        const Workspace &ws, const RouteOut &ro, hipStream_t st);
+hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro,
+                          hipStream_t st);
+
+struct ExpertArgs {
+    const uint16_t *x;
+    const int32_t *w13p;
+    const uint16_t *w13s;
+    const int32_t *w2p;
+    const uint16_t *w2s;
+    const float *weights;  // [T][k] routing weights (slot order)
+    uint16_t *out;
+    // shared expert (nullptr when absent)
+    const uint16_t *sh_gate;
+    const int32_t *sh_w13p;
+    const uint16_t *sh_w13s;
+    const int32_t *sh_w2p;
+    const uint16_t *sh_w2s;
+};
+
+hipError_t launch_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                          const RouteOut &ro, hipStream_t st);
+
+}  // namespace moe

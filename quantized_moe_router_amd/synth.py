@@ -65,43 +65,63 @@ def _words(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.integers(0, 2**32, size=shape, dtype=np.uint32).view(np.int32)
 
 
-def make_layer(shape: LayerShape, seed: int = 0, x_seed: int | None = None,
-               zipf_s: float | None = None, shared: bool = False) -> dict:
-    """Host (numpy) layer.  Weights come from `seed`; activations from `x_seed`
-    (default: the same stream, drawn right after the router)."""
-    T, H, E, k, I, G = (shape.tokens, shape.hidden, shape.experts, shape.top_k,
-                        shape.inter, shape.group)
+def make_weights(shape: LayerShape, seed: int = 0) -> dict:
+    """Router and expert weights of one layer (independent of the token count)."""
+    H, E, I, G = shape.hidden, shape.experts, shape.inter, shape.group
     rng = np.random.Generator(np.random.PCG64(seed))
     router = rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02)
-    xrng = rng if x_seed is None else np.random.Generator(np.random.PCG64(x_seed))
+    return {
+        "router_f32": router,
+        "w13_packed": _words(rng, (E, 2 * I, H // 8)),
+        "w13_scales": bf16_bits(np.abs(rng.standard_normal((E, 2 * I, H // G), dtype=np.float32)) * np.float32(0.02)),
+        "w2_packed": _words(rng, (E, H, I // 8)),
+        "w2_scales": bf16_bits(np.abs(rng.standard_normal((E, H, I // G), dtype=np.float32)) * np.float32(0.02)),
+    }
+
+
+def make_shared(hidden: int, seed: int) -> dict:
+    """INT6 group-64 shared expert (intermediate 640) and its gate row."""
+    srng = np.random.Generator(np.random.PCG64(seed))
+    SI, SG = SHARED_INTER, SHARED_GROUP
+    H = hidden
+    return {
+        "gate_w": bf16_bits(srng.standard_normal(H, dtype=np.float32) * np.float32(0.02)),
+        "w13_packed": _words(srng, (2 * SI, H // 32 * 6)),
+        "w13_scales": bf16_bits(np.abs(srng.standard_normal((2 * SI, H // SG), dtype=np.float32)) * np.float32(0.005)),
+        "w2_packed": _words(srng, (H, SI // 32 * 6)),
+        "w2_scales": bf16_bits(np.abs(srng.standard_normal((H, SI // SG), dtype=np.float32)) * np.float32(0.005)),
+        "group": SG,
+    }
+
+
+def make_layer(shape: LayerShape, seed: int = 0, x_seed: int | None = None,
+               zipf_s: float | None = None, shared: bool = False, weights: dict | None = None) -> dict:
+    """Host (numpy) layer.  Weights come from `seed` (or are passed in, as made
+    by make_weights); activations from `x_seed` (default seed + 1)."""
+    T, H, E = shape.tokens, shape.hidden, shape.experts
+    w = make_weights(shape, seed) if weights is None else weights
+    xrng = np.random.Generator(np.random.PCG64(seed + 1 if x_seed is None else x_seed))
     x = xrng.standard_normal((T, H), dtype=np.float32)
+    router = w["router_f32"]
     if zipf_s is not None:
+        router = router.copy()
         prng = np.random.Generator(np.random.PCG64(seed + 7919))
         rank = prng.permutation(E).astype(np.float64) + 1.0
         router[:, H - 1] = (-zipf_s * np.log(rank)).astype(np.float32)
         x[:, H - 1] = 1.0
     layer = {
         "shape": shape,
-        "top_k": k,
-        "group": G,
+        "top_k": shape.top_k,
+        "group": shape.group,
         "router_w": bf16_bits(router),
         "x": bf16_bits(x),
-        "w13_packed": _words(rng, (E, 2 * I, H // 8)),
-        "w13_scales": bf16_bits(np.abs(rng.standard_normal((E, 2 * I, H // G), dtype=np.float32)) * np.float32(0.02)),
-        "w2_packed": _words(rng, (E, H, I // 8)),
-        "w2_scales": bf16_bits(np.abs(rng.standard_normal((E, H, I // G), dtype=np.float32)) * np.float32(0.02)),
+        "w13_packed": w["w13_packed"],
+        "w13_scales": w["w13_scales"],
+        "w2_packed": w["w2_packed"],
+        "w2_scales": w["w2_scales"],
     }
     if shared:
-        srng = np.random.Generator(np.random.PCG64(seed + 104729))
-        SI, SG = SHARED_INTER, SHARED_GROUP
-        layer["shared"] = {
-            "gate_w": bf16_bits(srng.standard_normal(H, dtype=np.float32) * np.float32(0.02)),
-            "w13_packed": _words(srng, (2 * SI, H // 32 * 6)),
-            "w13_scales": bf16_bits(np.abs(srng.standard_normal((2 * SI, H // SG), dtype=np.float32)) * np.float32(0.005)),
-            "w2_packed": _words(srng, (H, SI // 32 * 6)),
-            "w2_scales": bf16_bits(np.abs(srng.standard_normal((H, SI // SG), dtype=np.float32)) * np.float32(0.005)),
-            "group": SG,
-        }
+        layer["shared"] = make_shared(H, seed + 104729)
     return layer
 
 

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports what include/moe_int4.h declares, and
+rejects bad arguments on the host (no GPU needed: every check runs before
+anything touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_router_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "moe_int4.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"\b(moe_int4_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.lib()
+    names = _declared()
+    assert set(names) >= {"moe_int4_forward", "moe_int4_route", "moe_int4_experts",
+                          "moe_int4_workspace_bytes", "moe_int4_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTED) <= set(names)
+    assert B.version().startswith("moe_int4")
+
+
+def _shape(**kw):
+    d = dict(tokens=4, hidden=2560, experts=512, inter=640, top_k=10, group=128)
+    d.update(kw)
+    return B.make_shape(d["tokens"], d["hidden"], d["experts"], d["inter"], d["top_k"], d["group"])
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(group=64), "group"),
+    (dict(hidden=2500), "hidden"),
+    (dict(hidden=8192), "hidden"),
+    (dict(inter=100), "inter"),
+    (dict(experts=0), "experts"),
+    (dict(experts=2048), "experts"),
+    (dict(top_k=0), "top_k"),
+    (dict(top_k=33), "top_k"),
+    (dict(experts=8, top_k=9), "top_k"),
+    (dict(tokens=-1), "tokens"),
+])
+def test_bad_shapes_rejected(kw, msg):
+    n = ctypes.c_size_t(0)
+    rc = B.lib().moe_int4_workspace_bytes(ctypes.byref(_shape(**kw)), None, ctypes.byref(n))
+    assert rc == B.EINVAL
+    assert msg in B.lib().moe_int4_last_error().decode()
+
+
+def test_workspace_size_grows_with_tokens():
+    a = B.workspace_bytes(_shape(tokens=1))
+    b = B.workspace_bytes(_shape(tokens=4))
+    c = B.workspace_bytes(_shape(tokens=8192))
+    assert 0 < a < b < c
+    assert B.workspace_bytes(_shape(tokens=0)) > 0
+
+
+FAKE = 0x10000  # never dereferenced: validation fails before any device access
+
+
+def _forward(shape, ptrs=None, top_k=10, ws_bytes=1 << 40):
+    p = dict(x=FAKE, router=FAKE, w13p=FAKE, w13s=FAKE, w2p=FAKE, w2s=FAKE, out=FAKE * 2, ws=FAKE)
+    p.update(ptrs or {})
+    return B.lib().moe_int4_forward(p["x"], p["router"], p["w13p"], p["w13s"], p["w2p"], p["w2s"],
+                                    top_k, p["out"], ctypes.byref(shape), None, p["ws"], ws_bytes, None)
+
+
+def test_forward_argument_errors():
+    s = _shape()
+    assert _forward(s, {"x": None}) == B.EINVAL
+    assert "x is NULL" in B.lib().moe_int4_last_error().decode()
+    assert _forward(s, {"w13p": FAKE + 4}) == B.EALIGN
+    assert _forward(s, top_k=8) == B.EINVAL
+    assert "top_k" in B.lib().moe_int4_last_error().decode()
+    assert _forward(s, {"out": FAKE}) == B.EINVAL          # out aliases x
+    assert _forward(s, ws_bytes=16) == B.EWORKSPACE
+    assert _forward(s, {"ws": None}) == B.EINVAL
+
+
+def test_route_and_experts_argument_errors():
+    s = _shape()
+    L = B.lib()
+    rc = L.moe_int4_route(FAKE, FAKE, ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert rc == B.EINVAL and "sorted_slots" in L.moe_int4_last_error().decode()
+    rc = L.moe_int4_experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), None, FAKE * 2,
+                            FAKE, 8, None)
+    assert rc == B.EWORKSPACE
+    bad = B.MoeSharedInt6(FAKE, FAKE, FAKE, FAKE, FAKE, 640, 128)
+    rc = L.moe_int4_experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(bad),
+                            FAKE * 2, FAKE, 1 << 40, None)
+    assert rc == B.EINVAL and "group" in L.moe_int4_last_error().decode()
+
+
+def test_no_device_is_reported_not_crashed():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = _forward(_shape())
+    assert rc == B.EDEVICE
