@@ -133,6 +133,21 @@ int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w,
                          const moe_shared_int6 *shared, void *workspace,
                          size_t workspace_bytes, void *hip_stream);
 
+/* moe_int4_forward with stage markers, for measurement: `events` points to
+ * four hipEvent_t (created by the caller) that are recorded on hip_stream
+ * before routing, after routing, after the gate/up projection (and the shared
+ * expert, if any), and after the down projection + combine.  Elapsed times
+ * between them give each stage's device time.  Otherwise identical to
+ * moe_int4_forward. */
+int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
+                                const int32_t *w13_packed, const uint16_t *w13_scales,
+                                const int32_t *w2_packed, const uint16_t *w2_scales,
+                                int32_t top_k, uint16_t *out,
+                                const moe_int4_shape *shape,
+                                const moe_shared_int6 *shared, void *workspace,
+                                size_t workspace_bytes, void *hip_stream,
+                                void *const *events);
+
 /* Message for the calling thread's most recent failing call ("" if none). */
 const char *moe_int4_last_error(void);
 

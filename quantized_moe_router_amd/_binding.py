@@ -51,16 +51,18 @@ def lib() -> ctypes.CDLL:
         L.moe_int4_route.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_int4_experts.argtypes = [P] * 11 + [ctypes.c_size_t, P]
         L.moe_int4_forward.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_int4_forward_traced.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P, P]
         L.moe_int4_last_error.restype = ctypes.c_char_p
         L.moe_int4_version.restype = ctypes.c_char_p
-        for f in ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts", "moe_int4_forward"):
+        for f in ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts", "moe_int4_forward",
+                  "moe_int4_forward_traced"):
             getattr(L, f).restype = _c_i32
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts",
-            "moe_int4_forward", "moe_int4_last_error", "moe_int4_version")
+            "moe_int4_forward", "moe_int4_forward_traced", "moe_int4_last_error", "moe_int4_version")
 
 
 def _check(rc: int):
@@ -127,6 +129,20 @@ def moe_int4_forward(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, 
                                   _ptr(w2_packed), _ptr(w2_scales), int(top_k), _ptr(out),
                                   ctypes.byref(shape), ctypes.byref(shared) if shared else None,
                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def moe_int4_forward_traced(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k: int,
+                            out, shape: MoeShape, shared: MoeSharedInt6 | None, workspace, events,
+                            stream=None):
+    """events: four torch.cuda.Event(enable_timing=True), already recorded once
+    (torch creates the underlying event lazily), re-recorded between the stages."""
+    arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    if not all(arr):
+        raise ValueError("record each torch.cuda.Event once before passing it (lazy creation)")
+    _check(lib().moe_int4_forward_traced(_ptr(x), _ptr(router_w), _ptr(w13_packed), _ptr(w13_scales),
+                                         _ptr(w2_packed), _ptr(w2_scales), int(top_k), _ptr(out),
+                                         ctypes.byref(shape), ctypes.byref(shared) if shared else None,
+                                         _ptr(workspace), workspace.numel(), _stream(stream), arr))
 
 
 def version() -> str:

@@ -12,10 +12,17 @@
 
 namespace moe {
 
-hipError_t launch_experts_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                               const RouteOut &ro, hipStream_t st);
+hipError_t launch_w13_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                           const RouteOut &ro, hipStream_t st);
+hipError_t launch_w2_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                          const RouteOut &ro, hipStream_t st);
 hipError_t launch_shared(const ExpertArgs &a, const Dims &d, const Workspace &ws,
                          hipStream_t st);
+hipError_t launch_decode_forward(const uint16_t *x, const uint16_t *router_w, const ExpertArgs &a,
+                                 const Dims &d, const Workspace &ws, hipEvent_t ev_route,
+                                 hipEvent_t ev_mid, hipStream_t st);
+hipError_t launch_decode_experts(const ExpertArgs &a, const int32_t *ids, const float *wts,
+                                 const Dims &d, const Workspace &ws, hipStream_t st);
 
 namespace {
 
@@ -190,13 +197,13 @@ int32_t launched(hipError_t e, const char *what)
 size_t workspace_size(const Dims &d) { return layout(d).total; }
 
 hipError_t launch_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                          const RouteOut &ro, hipStream_t st)
+                          const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid)
 {
-    if (d.sh_I > 0) {
-        hipError_t e = launch_shared(a, d, ws, st);
-        if (e != hipSuccess) return e;
-    }
-    return launch_experts_gemv(a, d, ws, ro, st);
+    hipError_t e;
+    if (d.sh_I > 0 && (e = launch_shared(a, d, ws, st)) != hipSuccess) return e;
+    if ((e = launch_w13_gemv(a, d, ws, ro, st)) != hipSuccess) return e;
+    if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
+    return launch_w2_gemv(a, d, ws, ro, st);
 }
 
 }  // namespace moe
@@ -261,21 +268,24 @@ int32_t moe_int4_experts(const uint16_t *x, const int32_t *topk_ids, const float
     if ((rc = check_workspace(d, workspace, workspace_bytes, &ws))) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t st = (hipStream_t)hip_stream;
-    RouteOut ro{const_cast<int32_t *>(topk_ids), const_cast<float *>(topk_w), ws.counts,
-                ws.offsets, ws.sorted_slots};
-    if ((rc = launched(launch_permute(d, ws, ro, st), "permute"))) return rc;
     ExpertArgs a{x, w13_packed, w13_scales, w2_packed, w2_scales, topk_w, out,
                  shared ? shared->gate_w : nullptr, shared ? shared->w13_packed : nullptr,
                  shared ? shared->w13_scales : nullptr, shared ? shared->w2_packed : nullptr,
                  shared ? shared->w2_scales : nullptr};
+    if (d.T <= kDecodeMaxTokens)
+        return launched(launch_decode_experts(a, topk_ids, topk_w, d, ws, st), "experts");
+    RouteOut ro{const_cast<int32_t *>(topk_ids), const_cast<float *>(topk_w), ws.counts,
+                ws.offsets, ws.sorted_slots};
+    if ((rc = launched(launch_permute(d, ws, ro, st), "permute"))) return rc;
     return launched(launch_experts(a, d, ws, ro, st), "experts");
 }
 
-int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w, const int32_t *w13_packed,
-                         const uint16_t *w13_scales, const int32_t *w2_packed,
-                         const uint16_t *w2_scales, int32_t top_k, uint16_t *out,
-                         const moe_int4_shape *shape, const moe_shared_int6 *shared,
-                         void *workspace, size_t workspace_bytes, void *hip_stream)
+static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
+                           const int32_t *w13_packed, const uint16_t *w13_scales,
+                           const int32_t *w2_packed, const uint16_t *w2_scales, int32_t top_k,
+                           uint16_t *out, const moe_int4_shape *shape,
+                           const moe_shared_int6 *shared, void *workspace,
+                           size_t workspace_bytes, void *hip_stream, void *const *events)
 {
     g_error.clear();
     Dims d;
@@ -293,13 +303,50 @@ int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w, const int3
     if ((rc = check_workspace(d, workspace, workspace_bytes, &ws))) return rc;
     if ((rc = check_device())) return rc;
     hipStream_t st = (hipStream_t)hip_stream;
-    RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
-    if ((rc = launched(launch_route(x, router_w, d, ws, ro, st), "route"))) return rc;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (events)
+        for (int i = 0; i < 4; ++i) {
+            if (!events[i]) return fail(MOE_INT4_EINVAL, "events[%d] is NULL", i);
+            ev[i] = (hipEvent_t)events[i];
+        }
+    if (ev[0] && (rc = launched(hipEventRecord(ev[0], st), "event"))) return rc;
     ExpertArgs a{x, w13_packed, w13_scales, w2_packed, w2_scales, ws.weights, out,
                  shared ? shared->gate_w : nullptr, shared ? shared->w13_packed : nullptr,
                  shared ? shared->w13_scales : nullptr, shared ? shared->w2_packed : nullptr,
                  shared ? shared->w2_scales : nullptr};
-    return launched(launch_experts(a, d, ws, ro, st), "experts");
+    if (d.T <= kDecodeMaxTokens) {
+        if ((rc = launched(launch_decode_forward(x, router_w, a, d, ws, ev[1], ev[2], st), "decode")))
+            return rc;
+    } else {
+        RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
+        if ((rc = launched(launch_route(x, router_w, d, ws, ro, st), "route"))) return rc;
+        if (ev[1] && (rc = launched(hipEventRecord(ev[1], st), "event"))) return rc;
+        if ((rc = launched(launch_experts(a, d, ws, ro, st, ev[2]), "experts"))) return rc;
+    }
+    if (ev[3] && (rc = launched(hipEventRecord(ev[3], st), "event"))) return rc;
+    return MOE_INT4_OK;
+}
+
+int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w, const int32_t *w13_packed,
+                         const uint16_t *w13_scales, const int32_t *w2_packed,
+                         const uint16_t *w2_scales, int32_t top_k, uint16_t *out,
+                         const moe_int4_shape *shape, const moe_shared_int6 *shared,
+                         void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    return forward_impl(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out,
+                        shape, shared, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
+                                const int32_t *w13_packed, const uint16_t *w13_scales,
+                                const int32_t *w2_packed, const uint16_t *w2_scales,
+                                int32_t top_k, uint16_t *out, const moe_int4_shape *shape,
+                                const moe_shared_int6 *shared, void *workspace,
+                                size_t workspace_bytes, void *hip_stream, void *const *events)
+{
+    if (!events) return fail(MOE_INT4_EINVAL, "events is NULL");
+    return forward_impl(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out,
+                        shape, shared, workspace, workspace_bytes, hip_stream, events);
 }
 
 }  // extern "C"

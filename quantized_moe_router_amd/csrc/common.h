@@ -99,16 +99,25 @@ __device__ __forceinline__ float chunk_dot(const uint4 w, const uint32_t x[16])
     return acc;
 }
 
-// Load 32 natural-order bf16 activations (64 bytes) and return them in
-// nibble-pair order, plus their sum.
-__device__ __forceinline__ float load_act_chunk(const uint16_t *p, uint32_t x[16])
+// 32 activations (64 bytes) as four 16-byte loads.  Loading every chunk
+// first and transforming afterwards keeps all loads in flight together.
+struct ActRaw {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ ActRaw load_act_raw(const uint16_t *p)
 {
     const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    return ActRaw{{q[0], q[1], q[2], q[3]}};
+}
+
+// Natural-order bf16 activations -> nibble-pair order, plus their sum.
+__device__ __forceinline__ float act_pairs(const ActRaw &r, uint32_t x[16])
+{
     float s = 0.f;
 #pragma unroll
     for (int o = 0; o < 4; ++o) {
-        uint4 v = q[o];
-        uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        uint32_t in[4] = {r.v[o].x, r.v[o].y, r.v[o].z, r.v[o].w};
         octet_to_pair_order(in, x + 4 * o);
         s = dot2(in[0], 0x3F803F80u, s);  // bf16 (1.0, 1.0)
         s = dot2(in[1], 0x3F803F80u, s);
@@ -169,15 +178,13 @@ __device__ __forceinline__ float chunk_dot_h(const uint4 w, const uint32_t x[16]
     return acc;
 }
 
-// 32 natural-order fp16 activations -> nibble-pair order, plus their sum.
-__device__ __forceinline__ float load_act_chunk_h(const uint16_t *p, uint32_t x[16])
+// Natural-order fp16 activations -> nibble-pair order, plus their sum.
+__device__ __forceinline__ float act_pairs_h(const ActRaw &r, uint32_t x[16])
 {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
     float s = 0.f;
 #pragma unroll
     for (int o = 0; o < 4; ++o) {
-        uint4 v = q[o];
-        uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        uint32_t in[4] = {r.v[o].x, r.v[o].y, r.v[o].z, r.v[o].w};
         octet_to_pair_order(in, x + 4 * o);
         s = dot2h(in[0], 0x3C003C00u, s);  // fp16 (1.0, 1.0)
         s = dot2h(in[1], 0x3C003C00u, s);
@@ -266,7 +273,9 @@ struct ExpertArgs {
     const uint16_t *sh_w2s;
 };
 
+// Expert phases: gate/up projection (+ the whole shared expert), then down
+// projection + combine.  `ev` (may be null) is recorded between the phases.
 hipError_t launch_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                          const RouteOut &ro, hipStream_t st);
+                          const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid = nullptr);
 
 }  // namespace moe

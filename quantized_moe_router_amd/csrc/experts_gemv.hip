@@ -54,32 +54,34 @@ __global__ __launch_bounds__(kW13Waves *kWave) void w13_gemv_kernel(ExpertArgs a
         const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w13p + r * words);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            int kc = q + 16 * c;
-            if (kc < nck) {
-                w[qd][c] = load_stream(wrow + kc);
-                sc[qd][c] = bf16_to_f32(a.w13s[r * nsc + kc / 4]);
-            }
+            // unconditional loads (a guard here makes the compiler wait on each
+            // load in turn); chunks past the row end read chunk 0 with scale 0
+            const int kc = q + 16 * c, ok = kc < nck, kcl = ok ? kc : 0;
+            w[qd][c] = load_stream(wrow + kcl);
+            const float s = bf16_to_f32(a.w13s[r * nsc + kcl / 4]);
+            sc[qd][c] = ok ? s : 0.f;
         }
     }
 
     for (int tok = 0; tok < ne; ++tok) {
         const int p = beg + tok;
         const int t = ro.sorted_slots[p] / d.k;
+        ActRaw raw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int kc = q + 16 * c, kcl = kc < nck ? kc : 0;
+            raw[c] = load_act_raw(a.x + (size_t)t * d.H + kcl * 32);
+        }
         uint32_t xv[CPL][16];
         float xs[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            int kc = q + 16 * c;
-            if (kc < nck) xs[c] = load_act_chunk(a.x + (size_t)t * d.H + kc * 32, xv[c]);
-        }
+        for (int c = 0; c < CPL; ++c) xs[c] = act_pairs(raw[c], xv[c]);
 #pragma unroll
         for (int qd = 0; qd < kW13QuadsPerWave; ++qd) {
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                int kc = q + 16 * c;
-                if (kc < nck) acc = fmaf(sc[qd][c], chunk_dot(w[qd][c], xv[c]) - 136.f * xs[c], acc);
-            }
+            for (int c = 0; c < CPL; ++c)
+                acc = fmaf(sc[qd][c], chunk_dot(w[qd][c], xv[c]) - 136.f * xs[c], acc);
             acc += __shfl_xor(acc, 8, kWave);
             acc += __shfl_xor(acc, 4, kWave);
             acc += __shfl_xor(acc, 2, kWave);
@@ -117,25 +119,28 @@ __global__ __launch_bounds__(kW2Waves *kWave) void w2_gemv_kernel(ExpertArgs a, 
         const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w2p + r * words);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            int kc = q + 4 * c;
-            if (kc < nck) {
-                w[c] = load_stream(wrow + kc);
-                sc[c] = bf16_to_f32(a.w2s[r * nsc + kc / 4]);
-            }
+            const int kc = q + 4 * c, ok = kc < nck, kcl = ok ? kc : 0;
+            w[c] = load_stream(wrow + kcl);
+            const float s = bf16_to_f32(a.w2s[r * nsc + kcl / 4]);
+            sc[c] = ok ? s : 0.f;
         }
     }
     for (int tok = 0; tok < ne; ++tok) {
         const int p = beg + tok;
-        float acc = 0.f;
+        ActRaw raw[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            int kc = q + 4 * c;
-            if (kc < nck) {
-                uint32_t hv[16];
-                float hs = load_act_chunk_h(ws.h + (size_t)p * d.I + kc * 32, hv);
-                acc = fmaf(sc[c], chunk_dot_h(w[c], hv) - 136.f * hs, acc);
-            }
+            const int kc = q + 4 * c, kcl = kc < nck ? kc : 0;
+            raw[c] = load_act_raw(ws.h + (size_t)p * d.I + kcl * 32);
         }
+        uint32_t hv[CPL][16];
+        float hs[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) hs[c] = act_pairs_h(raw[c], hv[c]);
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            acc = fmaf(sc[c], chunk_dot_h(w[c], hv[c]) - 136.f * hs[c], acc);
         acc += __shfl_xor(acc, 2, kWave);
         acc += __shfl_xor(acc, 1, kWave);
         if (q == 0) ws.ypart[(size_t)p * d.H + row] = acc;
@@ -168,8 +173,8 @@ __global__ __launch_bounds__(kW2Waves *kWave) void w2_gemv_kernel(ExpertArgs a, 
     if (threadIdx.x == 0) ws.tile_ticket[blockIdx.x] = 0;
 }
 
-hipError_t launch_experts_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                               const RouteOut &ro, hipStream_t st)
+hipError_t launch_w13_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                           const RouteOut &ro, hipStream_t st)
 {
     const int max_active = d.E < d.S ? d.E : d.S;
     {
@@ -184,8 +189,13 @@ hipError_t launch_experts_gemv(const ExpertArgs &a, const Dims &d, const Workspa
         }
 #undef MOE_W13_CASE
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+hipError_t launch_w2_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                          const RouteOut &ro, hipStream_t st)
+{
+    const int max_active = d.E < d.S ? d.E : d.S;
     {
         dim3 grid(d.H / kW2RowsPerBlock, max_active);
         int cpl = (d.I / 32 + 3) / 4;

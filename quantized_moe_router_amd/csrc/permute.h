@@ -1,0 +1,125 @@
+// Stable grouping of token slots by expert, computed by one wave with
+// ballots ("Running 125B MoE on Three 3090s - vLLM Optimization Edition",
+// section 3.3, "MoE block (decode-05)": the block-alignment step groups the
+// token slots by expert).  slot s = t*k + j; within an expert, slots keep
+// increasing order, so the result is unique and integer-exact.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Lanes holding the same (valid) id as this lane, as a 64-bit mask.
+__device__ __forceinline__ uint64_t match_id(int id, bool valid, int nbits)
+{
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (id >> b) & 1;
+        uint64_t bal = __ballot(valid && bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+// Caller-given ids outside [0, E) are clamped so that no access leaves its
+// buffer (the results for such input are unspecified).
+__device__ __forceinline__ int clamp_id(int id, int E) { return id < 0 ? 0 : (id >= E ? E - 1 : id); }
+
+__device__ __forceinline__ int id_bits(int E)
+{
+    int b = 1;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+// Count slots per expert over slots [beg, end) into run[] (LDS, E ints, must
+// be zero on entry).  One wave.
+__device__ inline void wave_count(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run)
+{
+    const int nbits = id_bits(E);
+    for (int base = beg; base < end; base += kWave) {
+        int s = base + lane;
+        bool valid = s < end;
+        int id = valid ? clamp_id(ids[s], E) : 0;
+        uint64_t m = match_id(id, valid, nbits);
+        bool leader = valid && ((m & ((1ull << lane) - 1)) == 0);
+        if (leader) run[id] += __popcll(m);
+    }
+}
+
+// Place slots [beg, end) at run[id] + (rank among equal ids), advancing run[].
+__device__ inline void wave_scatter(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run,
+                             int32_t *sorted_slots, int32_t *slot_pos)
+{
+    const int nbits = id_bits(E);
+    for (int base = beg; base < end; base += kWave) {
+        int s = base + lane;
+        bool valid = s < end;
+        int id = valid ? clamp_id(ids[s], E) : 0;
+        uint64_t m = match_id(id, valid, nbits);
+        uint64_t below = m & ((1ull << lane) - 1);
+        int pos = valid ? run[id] + __popcll(below) : 0;
+        if (valid) {
+            sorted_slots[pos] = s;
+            slot_pos[s] = pos;
+        }
+        if (valid && below == 0) run[id] += __popcll(m);
+    }
+}
+
+// counts -> offsets (exclusive) and the active-expert list; turns run[] into
+// the per-expert write cursor.  One wave; run[] holds the counts on entry.
+__device__ inline void wave_offsets(int E, int S, int lane, int32_t *run, int32_t *counts,
+                             int32_t *offsets, int32_t *active)
+{
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = lane * per;
+    int local = 0, nz = 0;
+    for (int i = 0; i < per; ++i) {
+        int e = e0 + i;
+        if (e < E) {
+            local += run[e];
+            nz += run[e] > 0;
+        }
+    }
+    int excl = wave_incl_scan(local, lane) - local;
+    int nz_excl = wave_incl_scan(nz, lane) - nz;
+    for (int i = 0; i < per; ++i) {
+        int e = e0 + i;
+        if (e < E) {
+            int c = run[e];
+            counts[e] = c;
+            offsets[e] = excl;
+            run[e] = excl;
+            if (c > 0) active[1 + nz_excl++] = e;
+            excl += c;
+        }
+    }
+    if (lane == kWave - 1) {
+        offsets[E] = S;
+        active[0] = nz_excl;
+    }
+}
+
+// The whole permutation by one wave (small S).  run: LDS, E ints.
+__device__ inline void wave_permute(const int32_t *ids, int S, int E, int lane, int32_t *run,
+                             int32_t *counts, int32_t *offsets, int32_t *sorted_slots,
+                             int32_t *slot_pos, int32_t *active)
+{
+    for (int e = lane; e < E; e += kWave) run[e] = 0;
+    wave_count(ids, 0, S, E, lane, run);
+    wave_offsets(E, S, lane, run, counts, offsets, active);
+    wave_scatter(ids, 0, S, E, lane, run, sorted_slots, slot_pos);
+}
+
+}  // namespace moe

@@ -14,267 +14,10 @@
 //     weights are a softmax over the k selected logits.
 // Logits stay fp32 (the page keys on bf16 logits; fp32 avoids manufacturing
 // ties).  Everything here is integer-exact except the fp32 sums and exp.
-#include "common.h"
+#include "permute.h"
+#include "topk.h"
 
 namespace moe {
-
-// ---------------------------------------------------------------------------
-// wave-level helpers
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, kWave);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane)
-{
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(v, off, kWave);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
-
-// Order-preserving map of a finite float onto uint32 (-0 and +0 coincide).
-__device__ __forceinline__ uint32_t float_order(float l)
-{
-    uint32_t u = __float_as_uint(l == 0.f ? 0.f : l);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float order_float(uint32_t o)
-{
-    uint32_t u = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
-    return __uint_as_float(u);
-}
-
-// Top-k of one token's logits by one wave.  KPL = ceil(E/64) keys per lane.
-// Writes ids/weights (global) and, if lds_ids != nullptr, the ids to LDS.
-template <int KPL>
-__device__ void wave_topk(const float *lrow, int E, int k, int lane, int32_t *ids,
-                          float *weights, int32_t *lds_ids)
-{
-    uint64_t key[KPL];
-    uint64_t lmax = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        int e = lane + kWave * i;
-        key[i] = 0;
-        if (e < E) {
-            uint64_t o = float_order(lrow[e]);
-            key[i] = (o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-        }
-        lmax = key[i] > lmax ? key[i] : lmax;
-    }
-    int my_e = 0;
-    float my_l = 0.f, first_l = 0.f;
-    for (int r = 0; r < k; ++r) {
-        uint64_t m = wave_max_u64(lmax);
-        int e = (int)(0xFFFFFFFFu - (uint32_t)m);
-        float l = order_float((uint32_t)(m >> 32));
-        if (r == 0) first_l = l;
-        if (lane == r) { my_e = e; my_l = l; }
-        if ((e & (kWave - 1)) == lane) {
-            lmax = 0;
-#pragma unroll
-            for (int i = 0; i < KPL; ++i) {
-                if (i == (e >> 6)) key[i] = 0;
-                lmax = key[i] > lmax ? key[i] : lmax;
-            }
-        }
-    }
-    float ex = lane < k ? expf(my_l - first_l) : 0.f;
-    float sum = wave_sum(ex);
-    if (lane < k) {
-        ids[lane] = my_e;
-        weights[lane] = ex / sum;
-        if (lds_ids) lds_ids[lane] = my_e;
-    }
-}
-
-__device__ void topk_any(const float *lrow, int E, int k, int lane, int32_t *ids, float *w,
-                         int32_t *lds_ids)
-{
-    if (E <= 64) wave_topk<1>(lrow, E, k, lane, ids, w, lds_ids);
-    else if (E <= 128) wave_topk<2>(lrow, E, k, lane, ids, w, lds_ids);
-    else if (E <= 256) wave_topk<4>(lrow, E, k, lane, ids, w, lds_ids);
-    else if (E <= 512) wave_topk<8>(lrow, E, k, lane, ids, w, lds_ids);
-    else wave_topk<16>(lrow, E, k, lane, ids, w, lds_ids);
-}
-
-// Lanes holding the same (valid) id as this lane, as a 64-bit mask.
-__device__ __forceinline__ uint64_t match_id(int id, bool valid, int nbits)
-{
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        bool bit = (id >> b) & 1;
-        uint64_t bal = __ballot(valid && bit);
-        m &= bit ? bal : ~bal;
-    }
-    return m;
-}
-
-// Caller-given ids outside [0, E) are clamped so that no access leaves its
-// buffer (the results for such input are unspecified).
-__device__ __forceinline__ int clamp_id(int id, int E) { return id < 0 ? 0 : (id >= E ? E - 1 : id); }
-
-__device__ __forceinline__ int id_bits(int E)
-{
-    int b = 1;
-    while ((1 << b) < E) ++b;
-    return b;
-}
-
-// Count slots per expert over slots [beg, end) into run[] (LDS, E ints, must
-// be zero on entry).  One wave.
-__device__ void wave_count(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run)
-{
-    const int nbits = id_bits(E);
-    for (int base = beg; base < end; base += kWave) {
-        int s = base + lane;
-        bool valid = s < end;
-        int id = valid ? clamp_id(ids[s], E) : 0;
-        uint64_t m = match_id(id, valid, nbits);
-        bool leader = valid && ((m & ((1ull << lane) - 1)) == 0);
-        if (leader) run[id] += __popcll(m);
-    }
-}
-
-// Place slots [beg, end) at run[id] + (rank among equal ids), advancing run[].
-__device__ void wave_scatter(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run,
-                             int32_t *sorted_slots, int32_t *slot_pos)
-{
-    const int nbits = id_bits(E);
-    for (int base = beg; base < end; base += kWave) {
-        int s = base + lane;
-        bool valid = s < end;
-        int id = valid ? clamp_id(ids[s], E) : 0;
-        uint64_t m = match_id(id, valid, nbits);
-        uint64_t below = m & ((1ull << lane) - 1);
-        int pos = valid ? run[id] + __popcll(below) : 0;
-        if (valid) {
-            sorted_slots[pos] = s;
-            slot_pos[s] = pos;
-        }
-        if (valid && below == 0) run[id] += __popcll(m);
-    }
-}
-
-// counts -> offsets (exclusive) and the active-expert list; turns run[] into
-// the per-expert write cursor.  One wave; run[] holds the counts on entry.
-__device__ void wave_offsets(int E, int S, int lane, int32_t *run, int32_t *counts,
-                             int32_t *offsets, int32_t *active)
-{
-    const int per = (E + kWave - 1) / kWave;
-    const int e0 = lane * per;
-    int local = 0, nz = 0;
-    for (int i = 0; i < per; ++i) {
-        int e = e0 + i;
-        if (e < E) {
-            local += run[e];
-            nz += run[e] > 0;
-        }
-    }
-    int excl = wave_incl_scan(local, lane) - local;
-    int nz_excl = wave_incl_scan(nz, lane) - nz;
-    for (int i = 0; i < per; ++i) {
-        int e = e0 + i;
-        if (e < E) {
-            int c = run[e];
-            counts[e] = c;
-            offsets[e] = excl;
-            run[e] = excl;
-            if (c > 0) active[1 + nz_excl++] = e;
-            excl += c;
-        }
-    }
-    if (lane == kWave - 1) {
-        offsets[E] = S;
-        active[0] = nz_excl;
-    }
-}
-
-// The whole permutation by one wave (small S).  run: LDS, E ints.
-__device__ void wave_permute(const int32_t *ids, int S, int E, int lane, int32_t *run,
-                             int32_t *counts, int32_t *offsets, int32_t *sorted_slots,
-                             int32_t *slot_pos, int32_t *active)
-{
-    for (int e = lane; e < E; e += kWave) run[e] = 0;
-    wave_count(ids, 0, S, E, lane, run);
-    wave_offsets(E, S, lane, run, counts, offsets, active);
-    wave_scatter(ids, 0, S, E, lane, run, sorted_slots, slot_pos);
-}
-
-// ---------------------------------------------------------------------------
-// Decode routing: one kernel.  Each wave computes one expert's logits for all
-// T tokens; the last workgroup to finish selects and permutes.
-// ---------------------------------------------------------------------------
-constexpr int kRouterWaves = 2;
-
-template <int CPL>
-__global__ __launch_bounds__(kRouterWaves * kWave) void router_decode_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ router_w, Dims d, Workspace ws,
-    RouteOut ro)
-{
-    __shared__ int32_t s_ids[kDecodeMaxTokens * kMaxTopK];
-    __shared__ int32_t s_run[kMaxExperts];
-    __shared__ int s_last;
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * kRouterWaves + wave;
-    const int nck = d.H / 8;  // 16-byte chunks per row
-
-    if (e < d.E) {
-        uint4 wr[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            int idx = lane + kWave * c;
-            if (idx < nck)
-                wr[c] = reinterpret_cast<const uint4 *>(router_w + (size_t)e * d.H)[idx];
-        }
-        for (int t = 0; t < d.T; ++t) {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                int idx = lane + kWave * c;
-                if (idx < nck) {
-                    uint4 xv = reinterpret_cast<const uint4 *>(x + (size_t)t * d.H)[idx];
-                    acc = dot2(wr[c].x, xv.x, acc);
-                    acc = dot2(wr[c].y, xv.y, acc);
-                    acc = dot2(wr[c].z, xv.z, acc);
-                    acc = dot2(wr[c].w, xv.w, acc);
-                }
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) ws.logits[(size_t)t * d.E + e] = acc;
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t ticket = atomicAdd(ws.route_ticket, 1u);
-        s_last = (ticket == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    for (int t = wave; t < d.T; t += kRouterWaves)
-        topk_any(ws.logits + (size_t)t * d.E, d.E, d.k, lane, ro.ids + (size_t)t * d.k,
-                 ro.weights + (size_t)t * d.k, s_ids + t * d.k);
-    __syncthreads();
-    if (wave == 0)
-        wave_permute(s_ids, d.S, d.E, lane, s_run, ro.counts, ro.offsets, ro.sorted_slots,
-                     ws.slot_pos, ws.active);
-    if (threadIdx.x == 0) *ws.route_ticket = 0;
-}
 
 // ---------------------------------------------------------------------------
 // Prefill routing
@@ -332,11 +75,15 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, Dims d,
                                                    int32_t *ids, float *weights)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ uint32_t s_topk[4][128];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
     if (t >= d.T) return;
-    topk_any(logits + (size_t)t * d.E, d.E, d.k, lane, ids + (size_t)t * d.k,
-             weights + (size_t)t * d.k, nullptr);
+    const TopkLane r = topk_any(logits + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave]);
+    if (lane < d.k) {
+        ids[(size_t)t * d.k + lane] = r.id;
+        weights[(size_t)t * d.k + lane] = r.w;
+    }
 }
 
 // Small permutation (one wave): used when routing is given by the caller.
@@ -422,22 +169,13 @@ hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro
     return hipGetLastError();
 }
 
+hipError_t launch_decode_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
+                               const Workspace &ws, const RouteOut &ro, hipStream_t st);
+
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                         const Workspace &ws, const RouteOut &ro, hipStream_t st)
 {
-    if (d.T <= kDecodeMaxTokens) {
-        int grid = (d.E + kRouterWaves - 1) / kRouterWaves;
-        int cpl = (d.H / 8 + kWave - 1) / kWave;
-#define MOE_ROUTER_CASE(N) \
-    case N: router_decode_kernel<N><<<grid, kRouterWaves * kWave, 0, st>>>(x, router_w, d, ws, ro); break;
-        switch (cpl) {
-            MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4)
-            MOE_ROUTER_CASE(5) MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8)
-            default: return hipErrorInvalidValue;
-        }
-#undef MOE_ROUTER_CASE
-        return hipGetLastError();
-    }
+    if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
     dim3 grid((d.T + kRG_T - 1) / kRG_T, (d.E + kRG_E - 1) / kRG_E);
     router_gemm_kernel<<<grid, 256, 0, st>>>(x, router_w, d, ws.logits);
     topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, d, ro.ids, ro.weights);

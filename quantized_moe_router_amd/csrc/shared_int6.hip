@@ -11,79 +11,9 @@
 // funnel shift (v_alignbit) and the same exponent trick as the INT4 path:
 // bf16 0x4300 | v (against bf16 x) and fp16 (v << 3) | 0x5800 (against the
 // fp16 activation) are exactly 128 + v for v < 128.
-#include "common.h"
+#include "int6.h"
 
 namespace moe {
-
-// 6-bit field i (0..31) of a 192-bit block held in w[0..5] (w[6] == 0).
-template <int I>
-__device__ __forceinline__ uint32_t field6(const uint32_t w[7])
-{
-    constexpr int lo = (6 * I) / 32, sh = (6 * I) % 32;
-    if constexpr (sh <= 26)
-        return (w[lo] >> sh) & 63u;
-    else
-        return __builtin_amdgcn_alignbit(w[lo + 1], w[lo], sh) & 63u;
-}
-
-// One pair (fields 2J, 2J+1) as 128 + v: bf16 (0x4300 | v) when F16 is
-// false, fp16 ((v << 3) | 0x5800) when true.
-template <int J, bool F16>
-__device__ __forceinline__ float pair6_dot(const uint32_t w[7], const uint32_t x[16], float acc)
-{
-    if constexpr (F16) {
-        uint32_t p = (field6<2 * J>(w) << 3) | (field6<2 * J + 1>(w) << 19) | 0x58005800u;
-        return dot2h(p, x[J], acc);
-    } else {
-        uint32_t p = field6<2 * J>(w) | (field6<2 * J + 1>(w) << 16) | 0x43004300u;
-        return dot2(p, x[J], acc);
-    }
-}
-
-// sum over 32 (code + 32 + 128) * x for one block; x in natural pairs
-// (bf16 when F16 is false, fp16 when true).
-template <bool F16>
-__device__ __forceinline__ float chunk_dot6(const uint32_t w[7], const uint32_t x[16])
-{
-    float acc = 0.f;
-    acc = pair6_dot<0, F16>(w, x, acc);  acc = pair6_dot<1, F16>(w, x, acc);
-    acc = pair6_dot<2, F16>(w, x, acc);  acc = pair6_dot<3, F16>(w, x, acc);
-    acc = pair6_dot<4, F16>(w, x, acc);  acc = pair6_dot<5, F16>(w, x, acc);
-    acc = pair6_dot<6, F16>(w, x, acc);  acc = pair6_dot<7, F16>(w, x, acc);
-    acc = pair6_dot<8, F16>(w, x, acc);  acc = pair6_dot<9, F16>(w, x, acc);
-    acc = pair6_dot<10, F16>(w, x, acc); acc = pair6_dot<11, F16>(w, x, acc);
-    acc = pair6_dot<12, F16>(w, x, acc); acc = pair6_dot<13, F16>(w, x, acc);
-    acc = pair6_dot<14, F16>(w, x, acc); acc = pair6_dot<15, F16>(w, x, acc);
-    return acc;
-}
-
-__device__ __forceinline__ void load_block6(const int32_t *p, uint32_t w[7])
-{
-    const uint2 *q = reinterpret_cast<const uint2 *>(p);
-    uint2 a = q[0], b = q[1], c = q[2];
-    w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y; w[4] = c.x; w[5] = c.y; w[6] = 0;
-}
-
-// 32 natural-order activations (bf16, or fp16 when F16) and their sum.
-template <bool F16>
-__device__ __forceinline__ float load_act_natural(const uint16_t *p, uint32_t x[16])
-{
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    float s = 0.f;
-#pragma unroll
-    for (int o = 0; o < 4; ++o) {
-        uint4 v = q[o];
-        x[4 * o] = v.x; x[4 * o + 1] = v.y; x[4 * o + 2] = v.z; x[4 * o + 3] = v.w;
-        if constexpr (F16) {
-            s = dot2h(v.x, 0x3C003C00u, s); s = dot2h(v.y, 0x3C003C00u, s);
-            s = dot2h(v.z, 0x3C003C00u, s); s = dot2h(v.w, 0x3C003C00u, s);
-        } else {
-            s = dot2(v.x, 0x3F803F80u, s); s = dot2(v.y, 0x3F803F80u, s);
-            s = dot2(v.z, 0x3F803F80u, s); s = dot2(v.w, 0x3F803F80u, s);
-        }
-    }
-    return s;
-}
 
 constexpr int kShTok = 8;  // tokens per workgroup
 
@@ -126,11 +56,10 @@ __global__ __launch_bounds__(256) void sh_w13_kernel(ExpertArgs a, Dims d, Works
         int row = (grp < 2) ? ii + grp : SI + ii + (grp - 2);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            int kc = q + 16 * c;
-            if (kc < nck) {
-                load_block6(a.sh_w13p + (size_t)row * words + kc * 6, w[qd][c]);
-                sc[qd][c] = bf16_to_f32(a.sh_w13s[(size_t)row * nsc + kc / 2]);
-            }
+            const int kc = q + 16 * c, ok = kc < nck, kcl = ok ? kc : 0;
+            load_block6(a.sh_w13p + (size_t)row * words + kcl * 6, w[qd][c]);
+            const float s = bf16_to_f32(a.sh_w13s[(size_t)row * nsc + kcl / 2]);
+            sc[qd][c] = ok ? s : 0.f;
         }
     }
     const int t_end = min(d.T, (int)(blockIdx.y + 1) * kShTok);
@@ -139,17 +68,15 @@ __global__ __launch_bounds__(256) void sh_w13_kernel(ExpertArgs a, Dims d, Works
         float xs[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            int kc = q + 16 * c;
-            if (kc < nck) xs[c] = load_act_natural<false>(a.x + (size_t)t * d.H + kc * 32, xv[c]);
+            const int kc = q + 16 * c, kcl = kc < nck ? kc : 0;
+            xs[c] = load_act_natural<false>(a.x + (size_t)t * d.H + kcl * 32, xv[c]);
         }
 #pragma unroll
         for (int qd = 0; qd < 2; ++qd) {
             float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                int kc = q + 16 * c;
-                if (kc < nck) acc = fmaf(sc[qd][c], chunk_dot6<false>(w[qd][c], xv[c]) - 160.f * xs[c], acc);
-            }
+            for (int c = 0; c < CPL; ++c)
+                acc = fmaf(sc[qd][c], chunk_dot6<false>(w[qd][c], xv[c]) - 160.f * xs[c], acc);
             acc += __shfl_xor(acc, 8, kWave);
             acc += __shfl_xor(acc, 4, kWave);
             acc += __shfl_xor(acc, 2, kWave);
@@ -174,24 +101,24 @@ __global__ __launch_bounds__(256) void sh_w2_kernel(ExpertArgs a, Dims d, Worksp
     float sc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        int kc = q + 4 * c;
-        if (kc < nck) {
-            load_block6(a.sh_w2p + (size_t)row * words + kc * 6, w[c]);
-            sc[c] = bf16_to_f32(a.sh_w2s[(size_t)row * nsc + kc / 2]);
-        }
+        const int kc = q + 4 * c, ok = kc < nck, kcl = ok ? kc : 0;
+        load_block6(a.sh_w2p + (size_t)row * words + kcl * 6, w[c]);
+        const float s = bf16_to_f32(a.sh_w2s[(size_t)row * nsc + kcl / 2]);
+        sc[c] = ok ? s : 0.f;
     }
     const int t_end = min(d.T, (int)(blockIdx.y + 1) * kShTok);
     for (int t = blockIdx.y * kShTok; t < t_end; ++t) {
-        float acc = 0.f;
+        uint32_t hv[CPL][16];
+        float hs[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            int kc = q + 4 * c;
-            if (kc < nck) {
-                uint32_t hv[16];
-                float hs = load_act_natural<true>(ws.sh_h + (size_t)t * SI + kc * 32, hv);
-                acc = fmaf(sc[c], chunk_dot6<true>(w[c], hv) - 160.f * hs, acc);
-            }
+            const int kc = q + 4 * c, kcl = kc < nck ? kc : 0;
+            hs[c] = load_act_natural<true>(ws.sh_h + (size_t)t * SI + kcl * 32, hv[c]);
         }
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            acc = fmaf(sc[c], chunk_dot6<true>(w[c], hv[c]) - 160.f * hs[c], acc);
         acc += __shfl_xor(acc, 2, kWave);
         acc += __shfl_xor(acc, 1, kWave);
         if (q == 0) ws.ypart[((size_t)d.S + t) * d.H + row] = acc;
