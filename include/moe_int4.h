@@ -59,8 +59,8 @@ extern "C" {
 #define MOE_INT4_EDEVICE (-5)    /* no usable gfx950 device */
 
 /* Layer dimensions.  Limits: tokens >= 0 (0 is a no-op); 1 <= top_k <=
- * min(experts, 32); experts <= 1024; group == 128; hidden and inter are
- * multiples of 128 with hidden <= 8192 and inter <= 2048. */
+ * min(experts, 32); experts <= 1024; group == 128; hidden a multiple of 256,
+ * at most 4096; inter a multiple of 128, at most 1024. */
 typedef struct moe_int4_shape {
     int32_t tokens;  /* T */
     int32_t hidden;  /* H */
@@ -78,7 +78,7 @@ typedef struct moe_int4_shape {
  *   gate_w     bf16  [H]               (the extra router row)
  *   w13_packed int32 [2*inter][H/32*6]; w13_scales bf16 [2*inter][H/group]
  *   w2_packed  int32 [H][inter/32*6];   w2_scales  bf16 [H][inter/group]
- * group must be 64, inter a multiple of 64 and <= 2048. */
+ * group must be 64, inter a multiple of 128 and <= 1024. */
 typedef struct moe_shared_int6 {
     const uint16_t *gate_w;
     const int32_t *w13_packed;

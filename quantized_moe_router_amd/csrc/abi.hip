@@ -12,12 +12,6 @@
 
 namespace moe {
 
-hipError_t launch_w13_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                           const RouteOut &ro, hipStream_t st);
-hipError_t launch_w2_gemv(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                          const RouteOut &ro, hipStream_t st);
-hipError_t launch_shared(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                         hipStream_t st);
 hipError_t launch_decode_forward(const uint16_t *x, const uint16_t *router_w, const ExpertArgs &a,
                                  const Dims &d, const Workspace &ws, hipEvent_t ev_route,
                                  hipEvent_t ev_mid, hipStream_t st);
@@ -44,7 +38,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t route_ticket, tile_ticket, logits, ids, weights, counts, offsets, sorted_slots,
-        slot_pos, active, chunk_hist, h, ypart, shared_gate, sh_h, total;
+        slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, total;
 };
 
 Layout layout(const Dims &d)
@@ -69,8 +63,10 @@ Layout layout(const Dims &d)
     L.slot_pos = take(4 * S);
     L.active = take(4 * ((size_t)d.E + 1));
     L.chunk_hist = take(4 * nchunks * d.E);
+    L.tiles = take(4 * ((S + 127) / 128 + (size_t)d.E));
+    L.n_tiles = take(4);
     L.h = take(2 * S * d.I);
-    L.ypart = take(4 * (S + (d.sh_I ? T : 0)) * d.H);
+    L.y = take(2 * T * ((size_t)d.k + 1) * d.H);
     L.shared_gate = take(4 * T);
     L.sh_h = take(2 * T * (size_t)d.sh_I);
     L.total = off;
@@ -107,8 +103,8 @@ int32_t check_shape(const moe_int4_shape *s, const moe_shared_int6 *sh, Dims *d)
     if (s->tokens < 0 || s->tokens > (1 << 20))
         return fail(MOE_INT4_EINVAL, "tokens=%d outside [0, 1048576]", s->tokens);
     if (s->group != kGroup) return fail(MOE_INT4_EINVAL, "group=%d, only 128 is supported", s->group);
-    if (s->hidden <= 0 || s->hidden % 128 || s->hidden > 4096)
-        return fail(MOE_INT4_EINVAL, "hidden=%d must be a positive multiple of 128, at most 4096",
+    if (s->hidden <= 0 || s->hidden % 256 || s->hidden > 4096)
+        return fail(MOE_INT4_EINVAL, "hidden=%d must be a positive multiple of 256, at most 4096",
                     s->hidden);
     if (s->inter <= 0 || s->inter % 128 || s->inter > 1024)
         return fail(MOE_INT4_EINVAL, "inter=%d must be a positive multiple of 128, at most 1024",
@@ -176,8 +172,10 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
     w.slot_pos = reinterpret_cast<int32_t *>(b + L.slot_pos);
     w.active = reinterpret_cast<int32_t *>(b + L.active);
     w.chunk_hist = reinterpret_cast<int32_t *>(b + L.chunk_hist);
+    w.tiles = reinterpret_cast<int32_t *>(b + L.tiles);
+    w.n_tiles = reinterpret_cast<int32_t *>(b + L.n_tiles);
     w.h = reinterpret_cast<uint16_t *>(b + L.h);
-    w.ypart = reinterpret_cast<float *>(b + L.ypart);
+    w.y = reinterpret_cast<uint16_t *>(b + L.y);
     w.shared_gate = reinterpret_cast<float *>(b + L.shared_gate);
     w.sh_h = reinterpret_cast<uint16_t *>(b + L.sh_h);
     w.bytes = L.total;
@@ -195,16 +193,6 @@ int32_t launched(hipError_t e, const char *what)
 }  // namespace
 
 size_t workspace_size(const Dims &d) { return layout(d).total; }
-
-hipError_t launch_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                          const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid)
-{
-    hipError_t e;
-    if (d.sh_I > 0 && (e = launch_shared(a, d, ws, st)) != hipSuccess) return e;
-    if ((e = launch_w13_gemv(a, d, ws, ro, st)) != hipSuccess) return e;
-    if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
-    return launch_w2_gemv(a, d, ws, ro, st);
-}
 
 }  // namespace moe
 
@@ -277,7 +265,7 @@ int32_t moe_int4_experts(const uint16_t *x, const int32_t *topk_ids, const float
     RouteOut ro{const_cast<int32_t *>(topk_ids), const_cast<float *>(topk_w), ws.counts,
                 ws.offsets, ws.sorted_slots};
     if ((rc = launched(launch_permute(d, ws, ro, st), "permute"))) return rc;
-    return launched(launch_experts(a, d, ws, ro, st), "experts");
+    return launched(launch_prefill_experts(a, d, ws, ro, st, nullptr), "experts");
 }
 
 static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
@@ -321,7 +309,7 @@ static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
         RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
         if ((rc = launched(launch_route(x, router_w, d, ws, ro, st), "route"))) return rc;
         if (ev[1] && (rc = launched(hipEventRecord(ev[1], st), "event"))) return rc;
-        if ((rc = launched(launch_experts(a, d, ws, ro, st, ev[2]), "experts"))) return rc;
+        if ((rc = launched(launch_prefill_experts(a, d, ws, ro, st, ev[2]), "experts"))) return rc;
     }
     if (ev[3] && (rc = launched(hipEventRecord(ev[3], st), "event"))) return rc;
     return MOE_INT4_OK;

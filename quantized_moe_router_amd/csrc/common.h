@@ -223,9 +223,11 @@ struct Workspace {
     int32_t *slot_pos;       // [S]   inverse of sorted_slots
     int32_t *active;         // [E+1] active[0] = n_active, then expert ids
     int32_t *chunk_hist;     // [nchunks][E]
+    int32_t *tiles;          // [ceil(S/128) + E] grouped-GEMM tiles
+    int32_t *n_tiles;        // [1]
     // expert intermediates
     uint16_t *h;             // [S][I] fp16, sorted order
-    float *ypart;            // [S][H] fp32, sorted order
+    uint16_t *y;             // [T][k+1][H] fp16 weighted slot outputs (many-token path)
     float *shared_gate;      // [T] shared-expert gate logits
     uint16_t *sh_h;          // [T][I_sh] fp16
     size_t bytes;
@@ -273,9 +275,10 @@ struct ExpertArgs {
     const uint16_t *sh_w2s;
 };
 
-// Expert phases: gate/up projection (+ the whole shared expert), then down
-// projection + combine.  `ev` (may be null) is recorded between the phases.
-hipError_t launch_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                          const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid = nullptr);
+// Many-token experts: grouped GEMMs (gate/up, then down + combine), with the
+// shared expert when present.  `ev_mid` (may be null) is recorded between the
+// gate/up and down projections.
+hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid);
 
 }  // namespace moe

@@ -1,0 +1,559 @@
+// Many-token path: matrix-core (MFMA) kernels for the router GEMM and the
+// expert grouped GEMMs.
+//
+// Method ("Running 125B MoE on Three 3090s - vLLM Optimization Edition",
+// section 3.3: the routed experts are a W4A16 grouped GEMM over the token
+// slots grouped by expert, gate_up followed by SiLU-and-multiply, then down
+// and the weighted sum of the k expert outputs per token; the INT6 shared
+// expert is added as sigmoid(gate) x shared).  The page's lesson that decode
+// and prefill need different kernels holds here too: this path is a dense
+// contraction, so it runs on matrix cores.
+//
+// gfx950 design
+//   * tile 128 rows x 256 weight rows per workgroup, 4 waves each owning all
+//     128 rows x 64 weight rows (v_mfma_f32_32x32x16_f16), K stages of 64;
+//     activations through double-buffered LDS, weights straight into
+//     registers (no LDS, no redundant conversion);
+//   * weights are dequantized once per workgroup, in registers, as
+//     fp16 values (code * scale * 2^10): a 4-bit code times a bf16 scale has
+//     at most 11 significant bits, so the value is exact in fp16 (the 2^10
+//     keeps small scales out of the subnormal range and is removed from the
+//     fp32 accumulator);
+//   * activations are fp16 (bf16 inputs converted exactly in the normal
+//     range; the SwiGLU activation is produced in fp16);
+//   * nibble pairs (n_j, n_j+4) are formed with one mask, so the 8 K values a
+//     lane holds are in the order 0,4,1,5,2,6,3,7 on both operands (the dot
+//     product does not care);
+//   * gate and up rows of the same outputs sit in the same wave, so
+//     silu(gate) * up is formed in registers;
+//   * the down projection writes each slot's weighted output (fp16) and a
+//     combine kernel sums a token's slots in a fixed order (deterministic; the
+//     fp32-atomic alternative measured about 2x slower on this layer);
+//   * workgroup -> tile order is XCD-aware: the weight-row blocks of one token
+//     tile go to the same XCD back to back, so the gathered activations are
+//     re-read from that XCD's L2.
+#include "int6.h"
+
+namespace moe {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMT = 128;          // tokens (sorted rows) per tile
+constexpr int kNT = 256;          // weight rows per tile (4 waves x 64)
+constexpr int kKS = 64;           // K per stage
+constexpr int kLdsRow = kKS + 8;  // padded LDS row (fp16 elements)
+constexpr int kGemmThreads = 256;
+constexpr int kRouterThreads = 512;
+constexpr float kScaleUp = 1024.f;
+constexpr float kScaleDown = 1.f / 1024.f;
+
+enum GemmMode { kRoutedW13 = 0, kRoutedW2 = 1, kSharedW13 = 2, kSharedW2 = 3 };
+
+struct GemmArgs {
+    const uint16_t *x;         // bf16 [T][H]
+    const uint16_t *a16;       // fp16 activation rows (down modes), pair order
+    const int32_t *bp;         // packed weights (expert 0)
+    const uint16_t *bs;        // bf16 scales (expert 0)
+    const int32_t *tiles;      // routed: (mblock << 16) | expert
+    const int32_t *n_tiles;    // routed: number of tiles (device)
+    const int32_t *offsets;
+    const int32_t *counts;
+    const int32_t *sorted_slots;
+    const float *weights;      // routing weights per slot
+    const float *gate;         // shared-expert gate logits [T]
+    uint16_t *h_out;           // fp16 activation out (gate/up modes)
+    uint16_t *y_out;           // fp16 weighted down-projection rows [T][k+1][H]
+    int T, H, I, k;            // I: intermediate of this expert kind
+    int K;                     // reduction length
+    size_t b_words;            // words of packed weights per expert
+    size_t b_scales;           // scales per expert
+};
+
+// Position of element i (0..7) of an 8-block in nibble-pair order.
+__device__ __forceinline__ int pair_pos(int i) { return (i < 4) ? 2 * i : 2 * (i - 4) + 1; }
+
+// INT4 word -> one MFMA operand: 8 fp16 values code * s in pair order
+// (0,4)(1,5)(2,6)(3,7); s2 = fp16 pair (s, s).
+__device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, h2_t s2)
+{
+    const h2_t bias = {(_Float16)-136.f, (_Float16)-136.f};
+    f16x8_t out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p = (((w >> (4 * j)) << 3) & 0x00780078u) | 0x58005800u;  // 128 + n
+        h2_t v = __builtin_bit_cast(h2_t, p);
+        v = (v + bias) * s2;  // (n - 8) * s, exact
+        out[2 * j] = v[0];
+        out[2 * j + 1] = v[1];
+    }
+    return out;
+}
+
+// 8 INT6 codes (octet o of a 32-code block) -> one MFMA operand in pair order.
+template <int O>
+__device__ __forceinline__ f16x8_t dequant_int6_octet(const uint32_t w[7], h2_t s2)
+{
+    const h2_t bias = {(_Float16)-160.f, (_Float16)-160.f};
+    f16x8_t out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t a, b;
+        switch (j) {  // fields 8O + j and 8O + j + 4 (compile-time)
+        case 0: a = field6<8 * O + 0>(w); b = field6<8 * O + 4>(w); break;
+        case 1: a = field6<8 * O + 1>(w); b = field6<8 * O + 5>(w); break;
+        case 2: a = field6<8 * O + 2>(w); b = field6<8 * O + 6>(w); break;
+        default: a = field6<8 * O + 3>(w); b = field6<8 * O + 7>(w); break;
+        }
+        const uint32_t p = (a << 3) | (b << 19) | 0x58005800u;  // 128 + v
+        h2_t v = __builtin_bit_cast(h2_t, p);
+        v = (v + bias) * s2;  // (v - 32) * s
+        out[2 * j] = v[0];
+        out[2 * j + 1] = v[1];
+    }
+    return out;
+}
+
+// bf16 octet (natural order) -> fp16 octet in pair order.
+__device__ __forceinline__ uint4 bf16_octet_to_f16_pairs(uint4 v)
+{
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // element j is in dword j/2, element j+4 in dword 2 + j/2
+        const uint32_t a = in[j >> 1], b = in[2 + (j >> 1)];
+        const float fa = __uint_as_float((j & 1) ? (a & 0xFFFF0000u) : (a << 16));
+        const float fb = __uint_as_float((j & 1) ? (b & 0xFFFF0000u) : (b << 16));
+        out[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+__device__ __forceinline__ h2_t scale_pair(uint16_t bf)
+{
+    const _Float16 s = (_Float16)(bf16_to_f32(bf) * kScaleUp);
+    return h2_t{s, s};
+}
+
+// Grouped / dense GEMM.  Workgroup tile: 128 rows (tokens or sorted slots) x
+// 256 weight rows; wave w owns all 128 rows and weight rows [64 w, +64) as two
+// 32-wide MFMA tiles.  Activations go through double-buffered LDS; each lane
+// loads its weight fragments straight from global memory (16 bytes = 32 codes
+// of one row per K stage) and dequantizes them in registers, so every weight
+// byte is read and converted once per workgroup.  Within a 64-wide K stage,
+// MFMA step j uses, on lanes 0-31, octet j and, on lanes 32-63, octet 4 + j:
+// that makes each lane's weight bytes for the stage contiguous.
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, int nblocks)
+{
+    constexpr bool kW13 = (MODE == kRoutedW13 || MODE == kSharedW13);
+    constexpr bool kRouted = (MODE == kRoutedW13 || MODE == kRoutedW2);
+    constexpr bool kInt6 = !kRouted;
+    __shared__ __align__(16) _Float16 s_a[2][kMT * kLdsRow];
+    __shared__ int s_tok[kMT];     // token of each tile row (-1: none)
+    __shared__ int s_slot[kMT];    // routed: slot of each tile row
+
+    // ---- tile assignment (XCD-aware: the n-blocks of one tile share an XCD) ----
+    const int wid = blockIdx.x;
+    const int xcd = wid & 7, r = wid >> 3;
+    const int nb = r % nblocks, tile = (r / nblocks) * 8 + xcd;
+    int e = 0, m0 = 0, rows = 0, pbase = 0;
+    if constexpr (kRouted) {
+        if (tile >= *g.n_tiles) return;
+        const int tv = g.tiles[tile];
+        e = tv & 0xFFFF;
+        const int mb = tv >> 16;
+        pbase = g.offsets[e] + mb * kMT;
+        rows = min(kMT, g.counts[e] - mb * kMT);
+    } else {
+        m0 = tile * kMT;
+        if (m0 >= g.T) return;
+        rows = min(kMT, g.T - m0);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < kMT) {
+        int tok = -1, slot = -1;
+        if (tid < rows) {
+            if constexpr (kRouted) {
+                slot = g.sorted_slots[pbase + tid];
+                tok = slot / g.k;
+            } else {
+                tok = m0 + tid;
+            }
+        }
+        s_tok[tid] = tok;
+        s_slot[tid] = slot;
+    }
+    __syncthreads();
+
+    const int K = g.K, nsteps = K / kKS;
+    // ---- activation staging: thread -> (row ar, 32 values at 32 * ahalf) ----
+    const int ar = tid >> 1, ahalf = tid & 1;
+    // rows past the tile read a valid row (row 0) and are stored as zeros, so
+    // no load sits behind a branch (a guarded load makes the compiler wait for
+    // every outstanding load at the next use)
+    const bool avalid = s_tok[ar] >= 0;
+    const int arow = avalid ? ar : 0;
+    const uint16_t *asrc;
+    if constexpr (kW13) asrc = g.x + (size_t)s_tok[arow] * g.H + 32 * ahalf;
+    else asrc = g.a16 + (size_t)(kRouted ? pbase + arow : s_tok[arow]) * K + 32 * ahalf;
+    uint4 ra[4];
+    auto load_a = [&](int s) {
+#pragma unroll
+        for (int o = 0; o < 4; ++o) ra[o] = reinterpret_cast<const uint4 *>(asrc + s * kKS)[o];
+    };
+    auto store_a = [&](int buf) {
+        uint4 *dst = reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 32 * ahalf);
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            const uint4 v = kW13 ? bf16_octet_to_f16_pairs(ra[o]) : ra[o];
+            dst[o] = avalid ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // ---- weight fragments: lane -> (row n = base + lane % 32, octets 4 * half ..) ----
+    const int half = lane >> 5;
+    int brow[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int c = 64 * wave + 32 * nt + (lane & 31);  // weight row within the tile
+        if constexpr (kW13) brow[nt] = nt == 0 ? 128 * nb + 32 * wave + (lane & 31)
+                                               : g.I + 128 * nb + 32 * wave + (lane & 31);
+        else brow[nt] = kNT * nb + c;
+    }
+    const int32_t *bp = g.bp + (size_t)e * g.b_words;
+    const uint16_t *bs = g.bs + (size_t)e * g.b_scales;
+    const size_t bstride = kInt6 ? (size_t)K / 32 * 6 : (size_t)K / 8;
+    const int sgroup = kInt6 ? kShGroup : kGroup;
+    // weights for two stages in flight: set q holds stage s with s % 2 == q
+    uint4 rb4[2][2];
+    uint32_t rb6[2][2][7];
+    uint16_t rsc[2][2];
+    auto load_b = [&](int s, int q) {
+        const int k0 = s * kKS + 32 * half;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            if constexpr (!kInt6)
+                rb4[q][nt] = load_stream(reinterpret_cast<const uint4 *>(bp + brow[nt] * bstride + k0 / 8));
+            else
+                load_block6(bp + brow[nt] * bstride + k0 / 32 * 6, rb6[q][nt]);
+            rsc[q][nt] = bs[(size_t)brow[nt] * (K / sgroup) + k0 / sgroup];
+        }
+    };
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    const int mtiles = (rows + 31) / 32;
+
+    // one K stage: stage s's weights (set q) against LDS buffer s % 2, while
+    // stage s+1's activations are stored and stages s+1/s+2's loads are in flight
+    auto stage = [&](int s, int q) {
+        if (s + 1 < nsteps) store_a((s + 1) & 1);   // loaded one stage ago
+        // keep this stage's raw weights and scales; the set is reloaded below
+        uint4 w4[2];
+        uint32_t w6[2][7];
+        h2_t s2[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            s2[nt] = scale_pair(rsc[q][nt]);
+            if constexpr (!kInt6) w4[nt] = rb4[q][nt];
+            else
+#pragma unroll
+                for (int u = 0; u < 7; ++u) w6[nt][u] = rb6[q][nt][u];
+        }
+        {   // the last stages re-load the last one (no branch around loads)
+            const int sn = min(s + 2, nsteps - 1);
+            load_a(sn);
+            load_b(sn, q);
+        }
+        // activation fragments of all four row tiles are read one MFMA step
+        // ahead (rows past the tile hold zeros); weight operands are converted
+        // per step, between the matrix instructions
+        const _Float16 *A = s_a[s & 1] + (lane & 31) * kLdsRow + 32 * half;
+        f16x8_t af[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            af[0][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kLdsRow);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < 3) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kLdsRow + 8 * (j + 1));
+            }
+            f16x8_t bf[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                if constexpr (!kInt6) {
+                    const uint32_t wj = j == 0 ? w4[nt].x : j == 1 ? w4[nt].y : j == 2 ? w4[nt].z : w4[nt].w;
+                    bf[nt] = dequant_int4_f16(wj, s2[nt]);
+                } else {
+                    bf[nt] = j == 0 ? dequant_int6_octet<0>(w6[nt], s2[nt])
+                           : j == 1 ? dequant_int6_octet<1>(w6[nt], s2[nt])
+                           : j == 2 ? dequant_int6_octet<2>(w6[nt], s2[nt])
+                                    : dequant_int6_octet<3>(w6[nt], s2[nt]);
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (mt < mtiles) {
+                    acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bf[0], acc[mt][0], 0, 0, 0);
+                    acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bf[1], acc[mt][1], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    // prologue: stage 0 in LDS, stage 1 activations in registers, weights of
+    // stages 0 and 1 in flight
+    load_a(0);
+    load_b(0, 0);
+    store_a(0);
+    load_a(min(1, nsteps - 1));
+    load_b(min(1, nsteps - 1), 1);
+    __syncthreads();
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        stage(s, 0);
+        stage(s + 1, 1);
+    }
+    if (s < nsteps) stage(s, 0);
+
+    // ---- epilogue ----
+    const int col = lane & 31;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= mtiles) continue;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int m = 32 * mt + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            if (m >= rows) continue;
+            if constexpr (kW13) {
+                const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
+                const int i = 128 * nb + 32 * wave + col;
+                const int ip = (i & ~7) | pair_pos(i & 7);
+                const size_t row_out = kRouted ? (size_t)(pbase + m) : (size_t)s_tok[m];
+                g.h_out[row_out * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
+            } else {
+                // weighted row of slot (t, j) -> y[t][j][:]; the shared expert is slot k
+                float wgt;
+                size_t yrow;
+                const int t = s_tok[m];
+                if constexpr (kRouted) {
+                    const int slot = s_slot[m];
+                    wgt = g.weights[slot];
+                    yrow = (size_t)t * (g.k + 1) + (slot - t * g.k);
+                } else {
+                    wgt = 1.f / (1.f + expf(-g.gate[t]));
+                    yrow = (size_t)t * (g.k + 1) + g.k;
+                }
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int n = kNT * nb + 64 * wave + 32 * nt + col;
+                    g.y_out[yrow * g.H + n] = (uint16_t)f32_to_f16_sat(wgt * acc[mt][nt][j] * kScaleDown);
+                }
+            }
+        }
+    }
+}
+
+// out[t][n] = bf16( sum_j y[t][j][n] (+ y[t][k][n] for the shared expert) ),
+// fixed order; one thread per 8 outputs.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ y, int T, int H,
+                                                      int k, int nslots, uint16_t *__restrict__ out)
+{
+    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    const size_t n8 = (size_t)T * H / 8;
+    if (i >= n8) return;
+    const size_t t = i / (H / 8), c = i % (H / 8);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < nslots; ++j) {
+        const uint4 v = reinterpret_cast<const uint4 *>(y + (t * (k + 1) + j) * H)[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const h2_t hv = __builtin_bit_cast(h2_t, w[q]);
+            acc[2 * q] += (float)hv[0];
+            acc[2 * q + 1] += (float)hv[1];
+        }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
+    reinterpret_cast<uint4 *>(out + t * H)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Router GEMM on matrix cores: logits[t][e] = x_t . router_w[e] with bf16
+// operands (exact products) and fp32 accumulation.  Tile 128 tokens x 128
+// experts, 8 waves (2 x 4), each 64 x 32.
+// ---------------------------------------------------------------------------
+constexpr int kRT_N = 128;
+
+__global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint16_t *__restrict__ x,
+                                                                   const uint16_t *__restrict__ rw,
+                                                                   int T, int H, int E,
+                                                                   float *__restrict__ logits)
+{
+    __shared__ __align__(16) uint16_t s_a[2][kMT * kLdsRow];
+    __shared__ __align__(16) uint16_t s_b[2][kRT_N * kLdsRow];
+    const int m0 = blockIdx.x * kMT, e0 = blockIdx.y * kRT_N;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int mh = wave & 1, nq = wave >> 1;
+    // staging: A 128 x 64 bf16 (2 octets per thread), B 128 x 64 (2 octets per
+    // thread: rows br and br + 64)
+    const int ar = tid >> 2, apart = tid & 3;
+    const int br = tid >> 3, bpart = tid & 7;
+    const bool aok = m0 + ar < T, bok0 = e0 + br < E, bok1 = e0 + br + 64 < E;
+    uint4 ra[2], rb[2];
+    auto load_stage = [&](int s) {
+        const int k0 = s * kKS;
+        if (aok) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(m0 + ar) * H + k0 + 16 * apart);
+            ra[0] = src[0];
+            ra[1] = src[1];
+        } else {
+            ra[0] = ra[1] = make_uint4(0, 0, 0, 0);
+        }
+        rb[0] = bok0 ? reinterpret_cast<const uint4 *>(rw + (size_t)(e0 + br) * H + k0)[bpart] : make_uint4(0, 0, 0, 0);
+        rb[1] = bok1 ? reinterpret_cast<const uint4 *>(rw + (size_t)(e0 + br + 64) * H + k0)[bpart] : make_uint4(0, 0, 0, 0);
+    };
+    auto store_stage = [&](int buf) {
+        *reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 16 * apart) = ra[0];
+        *reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 16 * apart + 8) = ra[1];
+        *reinterpret_cast<uint4 *>(s_b[buf] + br * kLdsRow + 8 * bpart) = rb[0];
+        *reinterpret_cast<uint4 *>(s_b[buf] + (br + 64) * kLdsRow + 8 * bpart) = rb[1];
+    };
+    f32x16_t acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+    const int nsteps = H / kKS;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nsteps) load_stage(s + 1);
+#pragma unroll
+        for (int ks = 0; ks < kKS / 16; ++ks) {
+            const int kk = 16 * ks + 8 * (lane >> 5);
+            bf16x8_t af[2], bfr;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                af[mt] = *reinterpret_cast<const bf16x8_t *>(s_a[buf] + (64 * mh + 32 * mt + (lane & 31)) * kLdsRow + kk);
+            bfr = *reinterpret_cast<const bf16x8_t *>(s_b[buf] + (32 * nq + (lane & 31)) * kLdsRow + kk);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr, acc[mt], 0, 0, 0);
+        }
+        if (s + 1 < nsteps) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int m = m0 + 64 * mh + 32 * mt + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            const int n = e0 + 32 * nq + (lane & 31);
+            if (m < T && n < E) logits[(size_t)m * E + n] = acc[mt][j];
+        }
+}
+
+// Tile list of the grouped GEMMs: expert e contributes ceil(count_e / 128)
+// tiles (e | mblock << 16), experts in id order.  One workgroup of 1024.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts, int E,
+                                                           int32_t *__restrict__ tiles,
+                                                           int32_t *__restrict__ n_tiles)
+{
+    __shared__ int s_sum[16];
+    const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+    const int nt = e < E ? (counts[e] + kMT - 1) / kMT : 0;
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_sum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_sum[w];
+    const int start = base + incl - nt;
+    for (int i = 0; i < nt; ++i) tiles[start + i] = e | (i << 16);
+    if (e == 1023) *n_tiles = start + nt;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, const Dims &d, float *out,
+                              hipStream_t st);
+
+hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const Dims &d,
+                              float *logits, hipStream_t st)
+{
+    dim3 grid((d.T + kMT - 1) / kMT, (d.E + kRT_N - 1) / kRT_N);
+    router_mfma_kernel<<<grid, kRouterThreads, 0, st>>>(x, router_w, d.T, d.H, d.E, logits);
+    return hipGetLastError();
+}
+
+static int max_routed_tiles(const Dims &d) { return (d.S + kMT - 1) / kMT + d.E; }
+
+template <int MODE>
+static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st)
+{
+    const int groups = (ntiles_max + 7) / 8;
+    moe_gemm_kernel<MODE><<<groups * 8 * nblocks, kGemmThreads, 0, st>>>(g, nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid)
+{
+    hipError_t e;
+    build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, d.E, ws.tiles, ws.n_tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint16_t *y = ws.y;
+    if (d.sh_I > 0) {
+        // gate logits, shared gate/up -> sh_h, shared down -> y[t][k] = sigmoid(g) * ys
+        if ((e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;
+        GemmArgs g{};
+        g.x = a.x; g.bp = a.sh_w13p; g.bs = a.sh_w13s; g.h_out = ws.sh_h;
+        g.T = d.T; g.H = d.H; g.I = d.sh_I; g.k = d.k; g.K = d.H;
+        if ((e = launch_gemm<kSharedW13>(g, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) return e;
+        GemmArgs g2{};
+        g2.a16 = ws.sh_h; g2.bp = a.sh_w2p; g2.bs = a.sh_w2s; g2.gate = ws.shared_gate; g2.y_out = y;
+        g2.T = d.T; g2.H = d.H; g2.I = d.sh_I; g2.k = d.k; g2.K = d.sh_I;
+        if ((e = launch_gemm<kSharedW2>(g2, (d.T + kMT - 1) / kMT, d.H / kNT, st)) != hipSuccess) return e;
+    }
+    const int tmax = max_routed_tiles(d);
+    GemmArgs g{};
+    g.x = a.x; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
+    g.offsets = ro.offsets; g.counts = ro.counts; g.sorted_slots = ro.sorted_slots;
+    g.h_out = ws.h; g.T = d.T; g.H = d.H; g.I = d.I; g.k = d.k; g.K = d.H;
+    g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H / kGroup);
+    if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st)) != hipSuccess) return e;
+    if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
+    GemmArgs g2 = g;
+    g2.a16 = ws.h; g2.bp = a.w2p; g2.bs = a.w2s; g2.weights = a.weights; g2.y_out = y;
+    g2.K = d.I;
+    g2.b_words = (size_t)d.H * d.I / 8; g2.b_scales = (size_t)d.H * (d.I / kGroup);
+    if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st)) != hipSuccess) return e;
+    const size_t n8 = (size_t)d.T * d.H / 8;
+    combine_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(y, d.T, d.H, d.k,
+                                                                 d.k + (d.sh_I > 0 ? 1 : 0), a.out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

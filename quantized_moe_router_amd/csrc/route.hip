@@ -23,54 +23,6 @@ namespace moe {
 // Prefill routing
 // ---------------------------------------------------------------------------
 
-// Router GEMM for many tokens: 64 tokens x 64 experts per workgroup, fp32
-// FMA over LDS-staged tiles.
-constexpr int kRG_T = 64, kRG_E = 64, kRG_K = 32;
-
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ router_w,
-                                                          Dims d, float *__restrict__ logits)
-{
-    __shared__ float sa[kRG_K][kRG_T + 1];
-    __shared__ float sb[kRG_K][kRG_E + 1];
-    const int t0 = blockIdx.x * kRG_T, e0 = blockIdx.y * kRG_E;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < d.H; k0 += kRG_K) {
-        for (int i = threadIdx.x; i < kRG_T * kRG_K; i += 256) {
-            int r = i / kRG_K, c = i % kRG_K;
-            int t = t0 + r, e = e0 + r;
-            sa[c][r] = t < d.T ? bf16_to_f32(x[(size_t)t * d.H + k0 + c]) : 0.f;
-            sb[c][r] = e < d.E ? bf16_to_f32(router_w[(size_t)e * d.H + k0 + c]) : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < kRG_K; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = sa[kk][ty * 4 + i];
-                b[i] = sb[kk][tx * 4 + i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int t = t0 + ty * 4 + i;
-        if (t >= d.T) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int e = e0 + tx * 4 + j;
-            if (e < d.E) logits[(size_t)t * d.E + e] = acc[i][j];
-        }
-    }
-}
-
 // One wave per token.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, Dims d,
                                                    int32_t *ids, float *weights)
@@ -171,13 +123,15 @@ hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro
 
 hipError_t launch_decode_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                                const Workspace &ws, const RouteOut &ro, hipStream_t st);
+hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const Dims &d,
+                              float *logits, hipStream_t st);
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                         const Workspace &ws, const RouteOut &ro, hipStream_t st)
 {
     if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
-    dim3 grid((d.T + kRG_T - 1) / kRG_T, (d.E + kRG_E - 1) / kRG_E);
-    router_gemm_kernel<<<grid, 256, 0, st>>>(x, router_w, d, ws.logits);
+    hipError_t e = launch_router_mfma(x, router_w, d, ws.logits, st);
+    if (e != hipSuccess) return e;
     topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, d, ro.ids, ro.weights);
     return launch_permute(d, ws, ro, st);
 }
