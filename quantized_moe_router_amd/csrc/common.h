@@ -196,6 +196,47 @@ __device__ __forceinline__ float act_pairs_h(const ActRaw &r, uint32_t x[16])
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// ---------------------------------------------------------------------------
+// Hand-over between workgroups of one launch.  Agent-scope relaxed atomic
+// loads and stores are coherent across the XCDs' separate L2 caches (they
+// compile to sc1 accesses), so data written this way and read this way needs
+// no cache write-back or invalidate: the writer only waits until its stores
+// have completed (vmcnt counts stores on this architecture) before it
+// publishes a counter, and the reader reads the data after it has seen the
+// counter.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_coherent(uint16_t *p, uint16_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave has issued has completed.
+__device__ __forceinline__ void wait_memory()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v)
 {

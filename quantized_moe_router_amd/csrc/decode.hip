@@ -1,101 +1,144 @@
-// Decode path (few tokens): three kernels, no cross-workgroup synchronisation
-// inside any of them.
+// Decode path (few tokens): three kernels.
 //
-//   1. router_gemv_kernel   logits[t][e] = x_t . router_w[e]  (bf16, fp32 sum),
-//                           plus the shared-expert gate logit as one more row
-//   2. w13_slot_kernel      per (slot, 16-output tile): the top-k of the slot's
-//                           token (recomputed by one wave of every workgroup,
-//                           cheaper than a grid-wide handshake), then the INT4
-//                           gate/up GEMV and a = silu(g) * u -> fp16;
-//                           extra slots run the INT6 shared expert's gate/up
+//   1. router_kernel        logits[t][e] = x_t . router_w[e]  (bf16, fp32 sum),
+//                           plus the shared-expert gate logit as one more row;
+//                           its last workgroup selects every token's experts
+//                           (and builds the permutation for the routing-only
+//                           entry point)
+//   2. w13_slot_kernel      per (slot, 16-output tile): the INT4 gate/up GEMV
+//                           and a = silu(g) * u -> fp16; extra slots run the
+//                           INT6 shared expert's gate/up
 //   3. w2_rows_kernel       each workgroup owns 16 output rows and sums, in a
 //                           fixed order, every slot's down projection weighted
 //                           by its routing weight (plus sigmoid(gate) times the
 //                           shared expert), then rounds once to bf16
 //
 // Method ("Running 125B MoE on Three 3090s - vLLM Optimization Edition",
-// section 3.3, "MoE block (decode-05)"): router and shared gate as one GEMV;
-// top-k with renormalisation; routed experts; shared expert added as
-// sigmoid(gate) x shared; down projection fused with the final combine.
-// On MI355X a kernel boundary costs about 2 us and a device-scope release/
-// acquire handshake several us once many workgroups take part, so the
-// dependencies (routing -> experts -> combine) are carried by the two kernel
-// boundaries only, and the small top-k is recomputed where it is needed.
+// section 3.3, "MoE block (decode-05)"): router and shared gate as one GEMV
+// whose last CTA does the top-k and renormalisation; routed experts; shared
+// expert added as sigmoid(gate) x shared; down projection fused with the
+// final combine.
 #include "int6.h"
 #include "permute.h"
 #include "topk.h"
 
 namespace moe {
 
-// ---------------------------------------------------------------------------
-// 1. router GEMV: one wave per row; rows [0, nrouted) are router rows, row
-//    nrouted (if gate_w) is the shared-expert gate.
-// ---------------------------------------------------------------------------
-template <int CPL>
-__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__restrict__ x,
-                                                          const uint16_t *__restrict__ router_w,
-                                                          const uint16_t *__restrict__ gate_w,
-                                                          int nrouted, Dims d, Workspace ws)
+__device__ __forceinline__ int clamp_expert(int id, int E)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const bool gate = gate_w != nullptr && row == nrouted;
-    if (row >= nrouted && !gate) return;
-    const uint16_t *wrow = gate ? gate_w : router_w + (size_t)row * d.H;
-    const int nck = d.H / 8;
-    uint4 wr[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        // unconditional loads; a chunk past the row end re-reads chunk 0, zeroed
-        const int idx = lane + kWave * c, ok = idx < nck;
-        const uint4 v = reinterpret_cast<const uint4 *>(wrow)[ok ? idx : 0];
-        wr[c] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-    for (int t = 0; t < d.T; ++t) {
-        uint4 xv[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int idx = lane + kWave * c;
-            xv[c] = reinterpret_cast<const uint4 *>(x + (size_t)t * d.H)[idx < nck ? idx : 0];
-        }
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            acc = dot2(wr[c].x, xv[c].x, acc);
-            acc = dot2(wr[c].y, xv[c].y, acc);
-            acc = dot2(wr[c].z, xv[c].z, acc);
-            acc = dot2(wr[c].w, xv[c].w, acc);
-        }
-        acc = wave_sum(acc);
-        if (lane == 0) {
-            if (gate) ws.shared_gate[t] = acc;
-            else ws.logits[(size_t)t * d.E + row] = acc;
-        }
-    }
+    return id < 0 ? 0 : (id >= E ? E - 1 : id);
 }
 
 // ---------------------------------------------------------------------------
-// 1b. routing only (moe_int4_route for few tokens): one workgroup selects every
-//     token's experts (one wave per token) and builds the permutation.
+// 1. Router GEMV with the routing tail in its last workgroup.
+//    One router row per wave (8 per workgroup; row E is the shared-expert gate
+//    when present), activations of four tokens in flight at a time.  Each
+//    workgroup stores its 8 logits of a token with one 32-byte coherent store,
+//    waits for its stores and takes a ticket; the workgroup that takes the
+//    last ticket selects every token's experts (one wave per token) and, for
+//    the routing-only entry point, builds the expert permutation.  ("MoE block
+//    (decode-05)": the CTA that finishes last does the top-k, the
+//    renormalisation and the block alignment, with no separate kernel.)
+//    The ticket needs no cache write-back: the logits are written and read
+//    with agent-scope coherent accesses.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_tail_kernel(Dims d, Workspace ws, RouteOut ro)
+constexpr int kRtWaves = 8;
+enum RouteTail { kTailNone = 0, kTailTopk = 1, kTailPermute = 2 };
+
+struct RouterArgs {
+    const uint16_t *x, *router_w, *gate_w;
+    int nrouted;     // router rows: E, or 0 when only the gate logit is wanted
+    Dims d;
+    Workspace ws;
+    RouteOut ro;     // tail outputs: ids, weights (+ counts, offsets, sorted_slots)
+    int tail;        // RouteTail
+};
+
+template <int CPL>
+__global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
 {
+    __shared__ float s_lg[kDecodeMaxTokens][kRtWaves];
+    __shared__ uint32_t s_topk[kRtWaves][kTopkLds];
     __shared__ int32_t s_ids[kDecodeMaxTokens * kMaxTopK];
     __shared__ int32_t s_run[kMaxExperts];
-    __shared__ uint32_t s_topk[4][128];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-    for (int t = wave; t < d.T; t += 4) {
-        TopkLane r = topk_any(ws.logits + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave]);
-        if (lane < d.k) {
-            ro.ids[t * d.k + lane] = r.id;
-            ro.weights[t * d.k + lane] = r.w;
-            s_ids[t * d.k + lane] = r.id;
+    __shared__ uint32_t s_last;
+    const Dims &d = r.d;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int row = blockIdx.x * kRtWaves + wave;
+    const bool gate = r.gate_w != nullptr && row == r.nrouted;
+    if (row < r.nrouted || gate) {
+        const uint16_t *wrow = gate ? r.gate_w : r.router_w + (size_t)row * d.H;
+        const int nck = d.H / 8;
+        uint4 wr[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            // unconditional loads; a chunk past the row end re-reads chunk 0, zeroed
+            const int idx = lane + kWave * c, ok = idx < nck;
+            const uint4 v = reinterpret_cast<const uint4 *>(wrow)[ok ? idx : 0];
+            wr[c] = ok ? v : make_uint4(0, 0, 0, 0);
+        }
+        for (int t0 = 0; t0 < d.T; t0 += 4) {
+            uint4 xv[4][CPL];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = min(t0 + u, d.T - 1);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const int idx = lane + kWave * c;
+                    xv[u][c] = reinterpret_cast<const uint4 *>(r.x + (size_t)t * d.H)[idx < nck ? idx : 0];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    acc = dot2(wr[c].x, xv[u][c].x, acc);
+                    acc = dot2(wr[c].y, xv[u][c].y, acc);
+                    acc = dot2(wr[c].z, xv[u][c].z, acc);
+                    acc = dot2(wr[c].w, xv[u][c].w, acc);
+                }
+                acc = wave_sum(acc);
+                if (lane == 0 && t0 + u < d.T) {
+                    if (gate) r.ws.shared_gate[t0 + u] = acc;
+                    else s_lg[t0 + u][wave] = acc;
+                }
+            }
         }
     }
+    if (r.tail == kTailNone) return;
+
     __syncthreads();
-    if (wave == 0)
-        wave_permute(s_ids, d.S, d.E, lane, s_run, ro.counts, ro.offsets, ro.sorted_slots,
-                     ws.slot_pos, ws.active);
+    // the workgroup's logits of token t are 8 consecutive words: one 32-byte store
+    if (tid < kRtWaves * d.T) {
+        const int t = tid / kRtWaves, j = tid % kRtWaves, rr = blockIdx.x * kRtWaves + j;
+        if (rr < r.nrouted)
+            store_coherent(reinterpret_cast<uint32_t *>(r.ws.logits) + (size_t)t * d.E + rr,
+                           __float_as_uint(s_lg[t][j]));
+    }
+    wait_memory();
+    __syncthreads();
+    if (tid == 0) s_last = atomic_add_agent(r.ws.route_ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
+    __syncthreads();
+    if (!s_last) return;
+
+    // last workgroup: routing of every token
+    if (tid == 0) *r.ws.route_ticket = 0;   // ready for the next call
+    for (int t = wave; t < d.T; t += kRtWaves) {
+        const TopkLane tk = topk_any<true>(r.ws.logits + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave]);
+        if (lane < d.k) {
+            const int id = clamp_expert(tk.id, d.E);
+            r.ro.ids[t * d.k + lane] = id;
+            r.ro.weights[t * d.k + lane] = tk.w;
+            s_ids[t * d.k + lane] = id;
+        }
+    }
+    if (r.tail == kTailPermute) {
+        __syncthreads();
+        if (wave == 0)
+            wave_permute(s_ids, d.S, d.E, lane, s_run, r.ro.counts, r.ro.offsets, r.ro.sorted_slots,
+                         r.ws.slot_pos, r.ws.active);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -106,14 +149,11 @@ __global__ __launch_bounds__(256) void route_tail_kernel(Dims d, Workspace ws, R
 // ---------------------------------------------------------------------------
 constexpr int kTileOut = 16;  // outputs of a per workgroup (4 waves x 2 quads x 2)
 
-__device__ __forceinline__ int clamp_expert(int id, int E)
-{
-    return id < 0 ? 0 : (id >= E ? E - 1 : id);
-}
 
+// Writes h[i] for i in [i0, i0 + 4) to hrow[i - hbase] (hrow may be in LDS).
 template <int CPL>
 __device__ __forceinline__ void w13_int4_tile(const ExpertArgs &a, const Dims &d, int e, int t,
-                                              uint16_t *hrow, int i0, int lane)
+                                              uint16_t *hrow, int i0, int lane, int hbase = 0)
 {
     const int grp = lane >> 4, q = lane & 15;
     const int nck = d.H / 32, words = d.H / 8, nsc = d.H / kGroup;
@@ -155,7 +195,7 @@ __device__ __forceinline__ void w13_int4_tile(const ExpertArgs &a, const Dims &d
         acc += __shfl_xor(acc, 1, kWave);
         const float up = __shfl(acc, (lane + 32) & (kWave - 1), kWave);
         if (lane == 0 || lane == 16)
-            hrow[i0 + 2 * qd + grp] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
+            hrow[i0 + 2 * qd + grp - hbase] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
     }
 }
 
@@ -213,14 +253,12 @@ __device__ __forceinline__ void w13_int6_tile(const ExpertArgs &a, const Dims &d
     }
 }
 
-// grid (max(I, sh_I) / 16, S + (shared ? T : 0)).  TOPK: routing from the
-// logits (forward); otherwise from ids_in / w_in (caller routing).
-template <int CPL, bool TOPK>
+// grid (max(I, sh_I) / 16, S + (shared ? T : 0)); expert ids of the slots
+// from `ids` (written by the router's tail, or given by the caller).
+template <int CPL>
 __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Workspace ws,
-                                                       const int32_t *__restrict__ ids_in)
+                                                       const int32_t *__restrict__ ids)
 {
-    __shared__ int s_e;
-    __shared__ uint32_t s_topk[128];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     const int s = blockIdx.y;
     const int i0 = blockIdx.x * kTileOut + wave * 4;
@@ -231,23 +269,8 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
         return;
     }
     if (blockIdx.x * kTileOut >= d.I) return;
-    const int t = s / d.k, j = s - t * d.k;
-    int e;
-    if constexpr (TOPK) {
-        if (wave == 0) {
-            const TopkLane r = topk_any(ws.logits + (size_t)t * d.E, d.E, d.k, lane, s_topk);
-            if (lane == j) s_e = r.id;
-            if (blockIdx.x == 0 && j == 0 && lane < d.k) {
-                ws.ids[t * d.k + lane] = r.id;
-                ws.weights[t * d.k + lane] = r.w;
-            }
-        }
-        __syncthreads();
-        e = s_e;
-    } else {
-        e = clamp_expert(ids_in[s], d.E);
-    }
-    w13_int4_tile<CPL>(a, d, e, t, ws.h + (size_t)s * d.I, i0, lane);
+    const int t = s / d.k;
+    w13_int4_tile<CPL>(a, d, clamp_expert(ids[s], d.E), t, ws.h + (size_t)s * d.I, i0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,14 +392,13 @@ __global__ __launch_bounds__(kDnWaves *kWave) void w2_rows_kernel(ExpertArgs a, 
 // ---------------------------------------------------------------------------
 static int cpl_of(int chunks, int lanes) { return (chunks + lanes - 1) / lanes; }
 
-hipError_t launch_router_gemv(const uint16_t *x, const uint16_t *router_w, const uint16_t *gate_w,
-                              int nrouted, const Dims &d, const Workspace &ws, hipStream_t st)
+static hipError_t launch_router(const RouterArgs &r, hipStream_t st)
 {
-    const int rows = nrouted + (gate_w ? 1 : 0);
-    const int grid = (rows + 3) / 4;
-    switch (cpl_of(d.H / 8, kWave)) {
+    const int rows = r.nrouted + (r.gate_w ? 1 : 0);
+    const int grid = (rows + kRtWaves - 1) / kRtWaves;
+    switch (cpl_of(r.d.H / 8, kWave)) {
 #define MOE_CASE(N) \
-    case N: router_gemv_kernel<N><<<grid, 256, 0, st>>>(x, router_w, gate_w, nrouted, d, ws); break;
+    case N: router_kernel<N><<<grid, kRtWaves * kWave, 0, st>>>(r); break;
         MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
     default: return hipErrorInvalidValue;
@@ -387,13 +409,9 @@ hipError_t launch_router_gemv(const uint16_t *x, const uint16_t *router_w, const
 hipError_t launch_decode_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                                const Workspace &ws, const RouteOut &ro, hipStream_t st)
 {
-    hipError_t e = launch_router_gemv(x, router_w, nullptr, d.E, d, ws, st);
-    if (e != hipSuccess) return e;
-    route_tail_kernel<<<1, 256, 0, st>>>(d, ws, ro);
-    return hipGetLastError();
+    return launch_router(RouterArgs{x, router_w, nullptr, d.E, d, ws, ro, kTailPermute}, st);
 }
 
-template <bool TOPK>
 static hipError_t launch_w13_slots(const ExpertArgs &a, const Dims &d, const Workspace &ws,
                                    const int32_t *ids, hipStream_t st)
 {
@@ -401,7 +419,7 @@ static hipError_t launch_w13_slots(const ExpertArgs &a, const Dims &d, const Wor
     dim3 grid(outs / kTileOut, d.S + (d.sh_I ? d.T : 0));
     switch (cpl_of(d.H / 32, 16)) {
 #define MOE_CASE(N) \
-    case N: w13_slot_kernel<N, TOPK><<<grid, 256, 0, st>>>(a, d, ws, ids); break;
+    case N: w13_slot_kernel<N><<<grid, 256, 0, st>>>(a, d, ws, ids); break;
         MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
     default: return hipErrorInvalidValue;
@@ -428,10 +446,11 @@ hipError_t launch_decode_forward(const uint16_t *x, const uint16_t *router_w, co
                                  const Dims &d, const Workspace &ws, hipEvent_t ev_route,
                                  hipEvent_t ev_mid, hipStream_t st)
 {
-    hipError_t e = launch_router_gemv(x, router_w, a.sh_gate, d.E, d, ws, st);
+    RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
+    hipError_t e = launch_router(RouterArgs{x, router_w, a.sh_gate, d.E, d, ws, ro, kTailTopk}, st);
     if (e != hipSuccess) return e;
     if (ev_route && (e = hipEventRecord(ev_route, st)) != hipSuccess) return e;
-    if ((e = launch_w13_slots<true>(a, d, ws, nullptr, st)) != hipSuccess) return e;
+    if ((e = launch_w13_slots(a, d, ws, ws.ids, st)) != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
     return launch_w2_rows(a, d, ws, ws.ids, ws.weights, st);
 }
@@ -440,9 +459,12 @@ hipError_t launch_decode_experts(const ExpertArgs &a, const int32_t *ids, const 
                                  const Dims &d, const Workspace &ws, hipStream_t st)
 {
     hipError_t e;
-    if (d.sh_I > 0 && (e = launch_router_gemv(a.x, nullptr, a.sh_gate, 0, d, ws, st)) != hipSuccess)
-        return e;
-    if ((e = launch_w13_slots<false>(a, d, ws, ids, st)) != hipSuccess) return e;
+    if (d.sh_I > 0) {
+        RouteOut none{};
+        e = launch_router(RouterArgs{a.x, nullptr, a.sh_gate, 0, d, ws, none, kTailNone}, st);
+        if (e != hipSuccess) return e;
+    }
+    if ((e = launch_w13_slots(a, d, ws, ids, st)) != hipSuccess) return e;
     return launch_w2_rows(a, d, ws, ids, wts, st);
 }
 

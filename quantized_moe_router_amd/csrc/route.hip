@@ -27,7 +27,7 @@ namespace moe {
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, Dims d,
                                                    int32_t *ids, float *weights)
 {
-    __shared__ uint32_t s_topk[4][128];
+    __shared__ uint32_t s_topk[4][kTopkLds];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= d.T) return;

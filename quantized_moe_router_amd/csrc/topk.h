@@ -2,21 +2,32 @@
 //
 // Method ("Running 125B MoE on Three 3090s - vLLM Optimization Edition",
 // section 3.3, "MoE block (decode-05)"): each logit becomes an
-// order-preserving integer with the inverted expert id packed below it, so a
-// single max yields value and id and equal logits resolve to the lower id;
-// with renormalisation the full softmax denominator cancels, so the weights
-// are a softmax over the k selected logits.  Logits stay fp32 here (the page
-// keys bf16 logits), packed into 64-bit keys.
+// order-preserving integer, the k largest are taken with equal logits
+// resolving to the lower expert id, and with renormalisation the full softmax
+// denominator cancels, so the weights are a softmax over the k selected
+// logits.  Logits stay fp32 here (the page keys bf16 logits).
 //
-// The selection is latency-bound (one wave, a few microseconds if done as k
-// dependent wave-wide max reductions), so it is done with ballots instead.
+// The selection is latency-bound (one wave, E = 512 logits, k = 10), so it
+// avoids k dependent wave-wide reductions:
+//   1. P = the k-th largest of the 64 per-lane maxima (a 32-step binary search
+//      on one value per lane, counting with ballots).  At least k logits are
+//      >= P, so every selected logit is >= P.
+//   2. The candidates (logits >= P; about k to 2k of them for continuous
+//      logits) are compacted into LDS, and each is ranked against all others
+//      by (value descending, id ascending).  Rank < k is selected, at that
+//      position.
+//   3. If more than 64 logits are >= P (heavy ties), an exact fallback finds
+//      the k-th value itself by a binary search over all logits.
 #pragma once
 
 #include "common.h"
 
 namespace moe {
 
+constexpr int kTopkLds = 192;  // words of wave-private LDS scratch per call
+
 // Order-preserving map of a finite float onto uint32 (-0 and +0 coincide).
+// Finite floats map above 0, so 0 can mark "no logit".
 __device__ __forceinline__ uint32_t float_order(float l)
 {
     uint32_t u = __float_as_uint(l == 0.f ? 0.f : l);
@@ -36,27 +47,10 @@ struct TopkLane {
 
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
-// Top-k of one token's E logits (lrow) by one wave; KPL = ceil(E / 64).
-// `lds` is 128 words of wave-private LDS scratch.
-//
-// Selection without a chain of k wave reductions:
-//   1. V = the k-th largest order-preserving logit image, by a 32-step binary
-//      search whose counts are popcounts of v_cmp masks (no lane shuffles);
-//   2. chosen = every key above V, plus the (k - #above) lowest ids equal to V
-//      (equal logits resolve to the lower id);
-//   3. the k chosen (id, value) pairs are compacted into LDS, ranked by
-//      (value descending, id ascending) against each other, and re-read in
-//      rank order, so lane j holds the j-th selection.
+// Largest V with #{keys >= V} >= k, by a binary search over the 32 key bits.
 template <int KPL>
-__device__ TopkLane wave_topk(const float *lrow, int E, int k, int lane, uint32_t *lds)
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&val)[KPL], int k)
 {
-    uint32_t val[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int e = lane + kWave * i;
-        const float l = lrow[e < E ? e : 0];
-        val[i] = e < E ? float_order(l) : 0u;  // finite logits map above 0
-    }
     uint32_t V = 0;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = V | (1u << b);
@@ -65,64 +59,123 @@ __device__ TopkLane wave_topk(const float *lrow, int E, int k, int lane, uint32_
         for (int i = 0; i < KPL; ++i) cnt += popc(__ballot(val[i] >= cand));
         if (cnt >= k) V = cand;
     }
-    int gt = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) gt += popc(__ballot(val[i] > V));
-    const int need = k - gt;
+    return V;
+}
+
+// Writes the keys with val >= thr (val > thr, plus the lowest-id `eq_take`
+// keys equal to thr if eq_take >= 0) as (key, id) pairs to lds[0..2n), in
+// ascending id order; returns n.
+template <int KPL>
+__device__ __forceinline__ int compact_keys(const uint32_t (&val)[KPL], uint32_t thr, int eq_take,
+                                            int lane, uint32_t *lds)
+{
     const uint64_t lt = (1ull << lane) - 1;
-    int eq_before = 0, sel_before = 0;
+    int eq_before = 0, n = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
-        const uint64_t eqm = __ballot(val[i] == V);
-        const bool sel = val[i] > V || (val[i] == V && eq_before + popc(eqm & lt) < need);
+        bool sel;
+        if (eq_take < 0) {
+            sel = val[i] >= thr && val[i] != 0u;
+        } else {
+            const uint64_t eqm = __ballot(val[i] == thr);
+            sel = val[i] > thr || (val[i] == thr && eq_before + popc(eqm & lt) < eq_take);
+            eq_before += popc(eqm);
+        }
         const uint64_t selm = __ballot(sel);
         if (sel) {
-            const int pos = sel_before + popc(selm & lt);
+            const int pos = n + popc(selm & lt);
             lds[2 * pos] = val[i];
             lds[2 * pos + 1] = (uint32_t)(lane + kWave * i);
         }
-        eq_before += popc(eqm);
-        sel_before += popc(selm);
+        n += popc(selm);
+    }
+    return n;
+}
+
+// Top-k of one token from its order-preserving keys val[i] = key of expert
+// lane + 64 i (0 where the expert does not exist).  Requires 1 <= k <= 32 and
+// at least k existing experts.  Lane j < k returns the j-th selection.
+template <int KPL>
+__device__ TopkLane wave_topk_keys(const uint32_t (&val)[KPL], int k, int lane, uint32_t *lds)
+{
+    uint32_t m = val[0];
+#pragma unroll
+    for (int i = 1; i < KPL; ++i) m = max(m, val[i]);
+    uint32_t lm[1] = {m};
+    const uint32_t P = kth_key<1>(lm, k);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) n += popc(__ballot(val[i] >= P));
+
+    uint32_t my_v = 0, my_e = 0xFFFFFFFFu;
+    int ncand;
+    if (n <= kWave) {
+        ncand = compact_keys<KPL>(val, P, -1, lane, lds);
+    } else {
+        // heavy ties: the exact k-th key, then exactly k candidates
+        const uint32_t V = kth_key<KPL>(val, k);
+        int gt = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) gt += popc(__ballot(val[i] > V));
+        ncand = compact_keys<KPL>(val, V, k - gt, lane, lds);
     }
     __builtin_amdgcn_wave_barrier();
-    uint32_t my_v = 0, my_e = 0;
-    if (lane < k) {
+    if (lane < ncand) {
         my_v = lds[2 * lane];
         my_e = lds[2 * lane + 1];
     }
-    // rank among the chosen: larger value first, then lower id
+    // rank among the candidates: larger key first, then lower id
     int rank = 0;
-    for (int j = 0; j < k; ++j) {
+    for (int j = 0; j < ncand; ++j) {
         const uint32_t vj = (uint32_t)__builtin_amdgcn_readlane((int)my_v, j);
         const uint32_t ej = (uint32_t)__builtin_amdgcn_readlane((int)my_e, j);
         rank += (vj > my_v || (vj == my_v && ej < my_e)) ? 1 : 0;
     }
     __builtin_amdgcn_wave_barrier();
-    if (lane < k) {
-        lds[64 + 2 * rank] = my_v;
-        lds[64 + 2 * rank + 1] = my_e;
+    if (lane < ncand && rank < k) {
+        lds[128 + 2 * rank] = my_v;
+        lds[128 + 2 * rank + 1] = my_e;
     }
     __builtin_amdgcn_wave_barrier();
     TopkLane out{0, 0.f};
     float l = 0.f;
     if (lane < k) {
-        l = order_float(lds[64 + 2 * lane]);
-        out.id = (int)lds[64 + 2 * lane + 1];
+        l = order_float(lds[128 + 2 * lane]);
+        out.id = (int)lds[128 + 2 * lane + 1];
     }
-    const float first = order_float(lds[64]);
+    const float first = order_float(lds[128]);
     const float ex = lane < k ? expf(l - first) : 0.f;
     out.w = ex / wave_sum(ex);
+    __builtin_amdgcn_wave_barrier();
     return out;
 }
 
+// Top-k of one token's E fp32 logits (lrow); KPL = ceil(E / 64).  COHERENT
+// reads the logits with agent-scope loads (written by other workgroups of the
+// same launch).
+template <int KPL, bool COHERENT>
+__device__ TopkLane wave_topk(const float *lrow, int E, int k, int lane, uint32_t *lds)
+{
+    uint32_t val[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + kWave * i, ec = e < E ? e : 0;
+        const float l = COHERENT ? __uint_as_float(load_coherent(reinterpret_cast<const uint32_t *>(lrow) + ec))
+                                 : lrow[ec];
+        val[i] = e < E ? float_order(l) : 0u;
+    }
+    return wave_topk_keys<KPL>(val, k, lane, lds);
+}
+
+template <bool COHERENT = false>
 __device__ __forceinline__ TopkLane topk_any(const float *lrow, int E, int k, int lane,
                                              uint32_t *lds)
 {
-    if (E <= 64) return wave_topk<1>(lrow, E, k, lane, lds);
-    if (E <= 128) return wave_topk<2>(lrow, E, k, lane, lds);
-    if (E <= 256) return wave_topk<4>(lrow, E, k, lane, lds);
-    if (E <= 512) return wave_topk<8>(lrow, E, k, lane, lds);
-    return wave_topk<16>(lrow, E, k, lane, lds);
+    if (E <= 64) return wave_topk<1, COHERENT>(lrow, E, k, lane, lds);
+    if (E <= 128) return wave_topk<2, COHERENT>(lrow, E, k, lane, lds);
+    if (E <= 256) return wave_topk<4, COHERENT>(lrow, E, k, lane, lds);
+    if (E <= 512) return wave_topk<8, COHERENT>(lrow, E, k, lane, lds);
+    return wave_topk<16, COHERENT>(lrow, E, k, lane, lds);
 }
 
 }  // namespace moe

@@ -172,6 +172,28 @@ def test_deterministic(T):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_decode_repeated_calls_share_workspace(T):
+    """Consecutive decode forwards on one workspace, alternating inputs: each
+    call sees only its own routing and activations, and the counters at the
+    head of the workspace are back at zero after each call."""
+    shape = synth.LayerShape(tokens=T, hidden=512, experts=64, top_k=4, inter=256)
+    host = synth.make_layer(shape, seed=21)
+    dev = synth.to_device(host)
+    x2 = synth.to_device(synth.make_layer(shape, seed=21, x_seed=77))["x"]
+    L = MoeInt4Layer(dev, shape.top_k)
+    first = [L.forward(dev["x"]).clone(), L.forward(x2).clone()]
+    torch.cuda.synchronize()
+    for i in range(6):
+        got = L.forward(dev["x"] if i % 2 == 0 else x2)
+        torch.cuda.synchronize()
+        assert torch.equal(got, first[i % 2]), f"call {i}"
+    assert not L.workspace(T)[:512].any(), "workspace counters were not returned to zero"
+    fresh = MoeInt4Layer(dev, shape.top_k).forward(dev["x"])   # a new zeroed workspace
+    torch.cuda.synchronize()
+    assert torch.equal(fresh, first[0])
+
+
 def test_tiny_shared_expert():
     for T in (3, 40):
         shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=2, inter=128)
