@@ -10,6 +10,11 @@ each with its own seeded weights and activations, so every step streams its
 weights from HBM rather than from the 256 MB last-level cache.  Inputs are
 resident in HBM before timing starts.
 
+Timed region: exactly K steps replayed from captured HIP graphs, bracketed by
+events.  Per-stage times come from a second pass over the same K steps, run
+eagerly behind a short spin kernel (so the host's enqueue never starves the
+GPU) with timing-only events between the stages on the launch stream.
+
 Prints one JSON line (rank 0).  `roofline` describes the dominant kernel,
 timed live with HIP events recorded around it on the stream it runs on;
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
@@ -50,7 +55,43 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="resident layers (0: config default)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="also run 4 plain device copies of MIB MiB (reference for memory counters)")
     return p.parse_args()
+
+
+class TimingEvents:
+    """hipEvents created with hipEventDisableSystemFence, on the HIP runtime this
+    process already uses (torch's).  A default event performs a system-scope
+    fence when it is recorded, which costs microseconds per record on this
+    part; a timing-only event does not."""
+
+    FLAG = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        self.hip = ctypes.CDLL(path)
+
+    def create(self) -> int:
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.FLAG)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return ev.value
+
+    def record(self, ev: int, stream: int) -> None:
+        rc = self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a: int, b: int) -> float:
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return out.value
 
 
 def kernel_source_hash() -> str:
@@ -123,6 +164,16 @@ def main():
                                       w["w2_packed"], w["w2_scales"], k, out, lay.shape(T), lay._shared_c,
                                       ws, events)
 
+    if args.copy_calibration:
+        # a plain copy of known size: each launch reads and writes exactly n bytes
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- exact algorithmic work: distinct experts touched per layer ----
     distinct = []
     for l in range(L):
@@ -130,11 +181,13 @@ def main():
         distinct.append(int((r["counts"] > 0).sum().item()))
     torch.cuda.synchronize()
 
-    # ---- warmup (eager), then the timed region: replays of captured HIP graphs ----
+    # ---- warmup (eager) ----
     K, W = args.steps, args.warmup
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps replayed from captured HIP graphs ----
     G = min(L, K)
     graphs = []
     for start, n in [(W, G), (W + (K // G) * G, K % G)]:
@@ -149,63 +202,94 @@ def main():
     # the full graph holds G consecutive steps (all L layers once when K >= L); the
     # optional second graph holds the K mod G remaining steps
     plan = [graphs[0]] * (K // G) + ([graphs[1]] if K % G else [])
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    assert sum(n for _, n in plan) == K
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
+    ga.record()
     for g, _ in plan:
         g.replay()
-    ev1.record()
+    gb.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    assert sum(n for _, n in plan) == K
-    ms_per_step = wall / K * 1e3
-    tokens_per_s = T * K / wall
+    gpu_ms = ga.elapsed_time(gb)
+    ms_per_step = gpu_ms / K
+    tokens_per_s = T * K / (gpu_ms * 1e-3)
 
-    # ---- stage breakdown: eager traced forwards (events around each stage) ----
-    NS = max(L, 2 * L if T <= 64 else L)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(NS)]
-    for e4 in evs:                  # torch creates the underlying hipEvent on first record
-        for e in e4:
-            e.record()
+    # ---- stage timing: K traced forwards queued behind a spin kernel ----
+    # The spin keeps the GPU busy while the host enqueues all K steps, so they
+    # run back to back; timing-only events on the launch stream mark every
+    # stage of every step (each event adds a little time between stages, not
+    # inside them).
+    TE = TimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [[TE.create() for _ in range(4)] for _ in range(K)]
+    ev0, ev1 = TE.create(), TE.create()
     torch.cuda.synchronize()
-    for i in range(NS):
+    t_enq = time.perf_counter()
+    for i in range(min(W, 8)):
         step(i, evs[i])
+    t_enq = (time.perf_counter() - t_enq) / max(1, min(W, 8))
     torch.cuda.synchronize()
-    st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(NS)]) * 1e3
+    sa, sb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sa.record(); torch.cuda._sleep(1_000_000); sb.record(); torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(sa.elapsed_time(sb), 1e-3)
+    spin = int(cycles_per_ms * (K * t_enq * 1e3 * 1.5 + 2.0))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin)
+    TE.record(ev0, stream)
+    for i in range(K):
+        step(W + i, evs[i])
+    TE.record(ev1, stream)
+    torch.cuda.synchronize()
+    traced_us = TE.ms(ev0, ev1) * 1e3 / K
+    st = np.array([[TE.ms(evs[i][j], evs[i][j + 1]) for j in range(3)] for i in range(K)]) * 1e3
     route_us, w13_us, w2_us = st.mean(axis=0)
-    layer_us = gpu_ms * 1e3 / K      # device time per step inside the graph replays
 
     # bytes / flops per step (averaged over the layers the timed steps visited)
-    visited = [(W + i % G) % L for i in range(K)]
+    visited = [(W + i) % L for i in range(K)]
     dist = np.array([distinct[l] for l in visited], dtype=np.float64)
+    d_mean = float(np.mean(dist))
     sh_bytes = acc.shared_int6_bytes() if cfg["shared"] else 0
     layer_bytes = np.mean([acc.layer_bytes(T, d, shared_bytes=sh_bytes) for d in dist])
+    S = T * k
     expert_w13 = 2 * I * H // 2 + 2 * I * (H // 128) * 2
-    w13_bytes = float(np.mean(dist)) * expert_w13 + T * H * 2 + T * k * I * 2
+    expert_w2 = H * I // 2 + H * (I // 128) * 2
+    stage_bytes = {"route": acc.router_bytes() + T * H * 2,
+                   "gate_up": d_mean * expert_w13 + T * H * 2 + S * I * 2,
+                   "down_combine": d_mean * expert_w2 + S * I * 2 + T * H * 2 + sh_bytes}
     flops = acc.layer_flops(T, shared_inter=640 if cfg["shared"] else 0)
-    w13_flops = 2 * T * k * 2 * I * H
+    w13_flops = 2 * S * 2 * I * H
+    stage_us = {"route": route_us, "gate_up": w13_us, "down_combine": w2_us}
+    layer_us = ms_per_step * 1e3
 
-    decode = T <= 64
+    decode = T <= 16
+    kernels = {"route": "router_kernel (router GEMV; top-k in its last workgroup)",
+               "gate_up": "w13_slot_kernel (INT4 gate/up dequant GEMV + SiLU-gate)",
+               "down_combine": "w2_rows_kernel (INT4 down dequant GEMV + weighted combine)"}
     if decode:
-        achieved = w13_bytes / (w13_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": "w13_slot_kernel (top-k + gate/up INT4 dequant GEMV + SiLU-gate)",
+        dom = max(stage_us, key=stage_us.get)
+        achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": kernels[dom],
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes_per_launch": round(w13_bytes)}
+                "algorithmic_bytes_per_launch": round(stage_bytes[dom]),
+                "launch_us": round(stage_us[dom], 3)}
+        trf_key = dom
     else:
         achieved = w13_flops / (w13_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": "gate/up projection stage",
+        roof = {"bound": "mfma", "kernel": "moe_gemm_kernel<kRoutedW13> (routed gate/up grouped GEMM, "
+                                           "fp16 MFMA on INT4 dequantised in registers) + tile list",
                 "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "algorithmic_flops_per_launch": w13_flops}
+                "algorithmic_flops_per_launch": w13_flops, "launch_us": round(w13_us, 3)}
+        trf_key = "gate_up"
     trf = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
     if os.path.exists(trf):
         with open(trf) as f:
             tr = json.load(f)
-        if tr.get("source_hash") == kernel_source_hash():
-            roof["traffic"] = tr.get("bytes_per_launch")
+        if tr.get("source_hash") == kernel_source_hash() and trf_key in tr.get("stages", {}):
+            roof["traffic"] = tr["stages"][trf_key]
 
     result = {
         "metric": METRIC,
@@ -226,13 +310,18 @@ def main():
                                + (", INT6 shared expert" if cfg["shared"] else "")
                                + f"; {L} resident layers rotated",
                    "tokens": T, "layers_resident": L},
-        "layer": {"device_us": round(layer_us, 3), "timing": "HIP-graph replay, events around the replays",
-                  "stages_us_eager": {"route": round(route_us, 2),
-                  "gate_up": round(w13_us, 2), "down_combine": round(w2_us, 2)},
-                  "distinct_experts": round(float(dist.mean()), 2),
+        "layer": {"device_us": round(layer_us, 3),
+                  "timing": "HIP-graph replay of the K steps, events around the replays",
+                  "stage_timing": "K traced forwards queued behind a spin kernel, timing-only events "
+                                  "between the stages on the launch stream",
+                  "traced_us_per_step": round(traced_us, 3),
+                  "stages_us": {kk: round(v, 2) for kk, v in stage_us.items()},
+                  "stages_gbs": {kk: round(stage_bytes[kk] / (stage_us[kk] * 1e-6) / 1e9, 1) for kk in stage_us},
+                  "distinct_experts": round(d_mean, 2),
                   "algorithmic_bytes": round(layer_bytes), "hbm_gbs": round(layer_bytes / (layer_us * 1e-6) / 1e9, 1),
                   "hbm_frac": round(layer_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                  "flops": flops, "tflops": round(flops / (layer_us * 1e-6) / 1e12, 3)},
+                  "flops": flops, "tflops": round(flops / (layer_us * 1e-6) / 1e12, 3),
+                  "wall_s": round(wall, 4)},
         "roofline": roof,
         "cpu_baseline": None,
     }

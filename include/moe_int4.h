@@ -135,9 +135,10 @@ int32_t moe_int4_forward(const uint16_t *x, const uint16_t *router_w,
 
 /* moe_int4_forward with stage markers, for measurement: `events` points to
  * four hipEvent_t (created by the caller) that are recorded on hip_stream
- * before routing, after routing, after the gate/up projection (and the shared
- * expert, if any), and after the down projection + combine.  Elapsed times
- * between them give each stage's device time.  Otherwise identical to
+ * before routing, after routing, after the routed gate/up projection (for
+ * at most 16 tokens this stage also holds the shared expert's gate/up), and
+ * after the rest (down projection, shared expert, combine).  Elapsed
+ * times between them give each stage's device time.  Otherwise identical to
  * moe_int4_forward. */
 int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
                                 const int32_t *w13_packed, const uint16_t *w13_scales,

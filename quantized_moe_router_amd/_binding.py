@@ -134,9 +134,10 @@ def moe_int4_forward(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, 
 def moe_int4_forward_traced(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k: int,
                             out, shape: MoeShape, shared: MoeSharedInt6 | None, workspace, events,
                             stream=None):
-    """events: four torch.cuda.Event(enable_timing=True), already recorded once
-    (torch creates the underlying event lazily), re-recorded between the stages."""
-    arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    """events: four hipEvent_t handles (ints), or four torch.cuda.Event(enable_timing=True)
+    already recorded once (torch creates the underlying event lazily); they are
+    re-recorded between the stages."""
+    arr = (ctypes.c_void_p * 4)(*[e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events])
     if not all(arr):
         raise ValueError("record each torch.cuda.Event once before passing it (lazy creation)")
     _check(lib().moe_int4_forward_traced(_ptr(x), _ptr(router_w), _ptr(w13_packed), _ptr(w13_scales),

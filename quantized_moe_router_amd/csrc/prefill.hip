@@ -525,18 +525,7 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, d.E, ws.tiles, ws.n_tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint16_t *y = ws.y;
-    if (d.sh_I > 0) {
-        // gate logits, shared gate/up -> sh_h, shared down -> y[t][k] = sigmoid(g) * ys
-        if ((e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;
-        GemmArgs g{};
-        g.x = a.x; g.bp = a.sh_w13p; g.bs = a.sh_w13s; g.h_out = ws.sh_h;
-        g.T = d.T; g.H = d.H; g.I = d.sh_I; g.k = d.k; g.K = d.H;
-        if ((e = launch_gemm<kSharedW13>(g, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) return e;
-        GemmArgs g2{};
-        g2.a16 = ws.sh_h; g2.bp = a.sh_w2p; g2.bs = a.sh_w2s; g2.gate = ws.shared_gate; g2.y_out = y;
-        g2.T = d.T; g2.H = d.H; g2.I = d.sh_I; g2.k = d.k; g2.K = d.sh_I;
-        if ((e = launch_gemm<kSharedW2>(g2, (d.T + kMT - 1) / kMT, d.H / kNT, st)) != hipSuccess) return e;
-    }
+    // routed gate/up -> h (sorted slot order)
     const int tmax = max_routed_tiles(d);
     GemmArgs g{};
     g.x = a.x; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
@@ -545,11 +534,24 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H / kGroup);
     if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st)) != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
+    // routed down -> y[t][j] = w * (W2 h)
     GemmArgs g2 = g;
     g2.a16 = ws.h; g2.bp = a.w2p; g2.bs = a.w2s; g2.weights = a.weights; g2.y_out = y;
     g2.K = d.I;
     g2.b_words = (size_t)d.H * d.I / 8; g2.b_scales = (size_t)d.H * (d.I / kGroup);
     if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st)) != hipSuccess) return e;
+    if (d.sh_I > 0) {
+        // shared expert: gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
+        if ((e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;
+        GemmArgs gs{};
+        gs.x = a.x; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
+        gs.T = d.T; gs.H = d.H; gs.I = d.sh_I; gs.k = d.k; gs.K = d.H;
+        if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) return e;
+        GemmArgs gs2{};
+        gs2.a16 = ws.sh_h; gs2.bp = a.sh_w2p; gs2.bs = a.sh_w2s; gs2.gate = ws.shared_gate; gs2.y_out = y;
+        gs2.T = d.T; gs2.H = d.H; gs2.I = d.sh_I; gs2.k = d.k; gs2.K = d.sh_I;
+        if ((e = launch_gemm<kSharedW2>(gs2, (d.T + kMT - 1) / kMT, d.H / kNT, st)) != hipSuccess) return e;
+    }
     const size_t n8 = (size_t)d.T * d.H / 8;
     combine_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(y, d.T, d.H, d.k,
                                                                  d.k + (d.sh_I > 0 ? 1 : 0), a.out);
