@@ -237,7 +237,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             if constexpr (!kInt6)
-                rb4[q][nt] = load_stream(reinterpret_cast<const uint4 *>(bp + brow[nt] * bstride + k0 / 8));
+                // plain load: the rest of this 128-byte line is used by the next
+                // three stages, so it must not be marked for early eviction
+                rb4[q][nt] = *reinterpret_cast<const uint4 *>(bp + brow[nt] * bstride + k0 / 8);
             else
                 load_block6(bp + brow[nt] * bstride + k0 / 32 * 6, rb6[q][nt]);
             rsc[q][nt] = bs[(size_t)brow[nt] * (K / sgroup) + k0 / sgroup];
