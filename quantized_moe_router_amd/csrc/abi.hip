@@ -38,7 +38,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t route_ticket, tile_ticket, logits, ids, weights, counts, offsets, sorted_slots,
-        slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, total;
+        slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, xh, total;
 };
 
 Layout layout(const Dims &d)
@@ -69,6 +69,7 @@ Layout layout(const Dims &d)
     L.y = take(2 * T * ((size_t)d.k + 1) * d.H);
     L.shared_gate = take(4 * T);
     L.sh_h = take(2 * T * (size_t)d.sh_I);
+    L.xh = take(d.T > kDecodeMaxTokens ? 2 * T * (size_t)d.H : 0);
     L.total = off;
     return L;
 }
@@ -178,6 +179,7 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
     w.y = reinterpret_cast<uint16_t *>(b + L.y);
     w.shared_gate = reinterpret_cast<float *>(b + L.shared_gate);
     w.sh_h = reinterpret_cast<uint16_t *>(b + L.sh_h);
+    w.xh = reinterpret_cast<uint16_t *>(b + L.xh);
     w.bytes = L.total;
     *out = w;
     return MOE_INT4_OK;

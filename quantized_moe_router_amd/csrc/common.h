@@ -271,6 +271,7 @@ struct Workspace {
     uint16_t *y;             // [T][k+1][H] fp16 weighted slot outputs (many-token path)
     float *shared_gate;      // [T] shared-expert gate logits
     uint16_t *sh_h;          // [T][I_sh] fp16
+    uint16_t *xh;            // [T][H] fp16 copy of x in nibble-pair order (many-token path)
     size_t bytes;
 };
 

@@ -19,8 +19,9 @@
 //     at most 11 significant bits, so the value is exact in fp16 (the 2^10
 //     keeps small scales out of the subnormal range and is removed from the
 //     fp32 accumulator);
-//   * activations are fp16 (bf16 inputs converted exactly in the normal
-//     range; the SwiGLU activation is produced in fp16);
+//   * activations are fp16: bf16 inputs are converted once per forward
+//     (exact in fp16's normal range) into nibble-pair order, and the SwiGLU
+//     activation is produced in fp16;
 //   * nibble pairs (n_j, n_j+4) are formed with one mask, so the 8 K values a
 //     lane holds are in the order 0,4,1,5,2,6,3,7 on both operands (the dot
 //     product does not care);
@@ -53,7 +54,7 @@ constexpr float kScaleDown = 1.f / 1024.f;
 enum GemmMode { kRoutedW13 = 0, kRoutedW2 = 1, kSharedW13 = 2, kSharedW2 = 3 };
 
 struct GemmArgs {
-    const uint16_t *x;         // bf16 [T][H]
+    const uint16_t *x;         // fp16 [T][H] in nibble-pair order (gate/up modes)
     const uint16_t *a16;       // fp16 activation rows (down modes), pair order
     const int32_t *bp;         // packed weights (expert 0)
     const uint16_t *bs;        // bf16 scales (expert 0)
@@ -132,6 +133,17 @@ __device__ __forceinline__ uint4 bf16_octet_to_f16_pairs(uint4 v)
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// xh[t][:] = x[t][:] as fp16 in nibble-pair order, once per forward: the
+// gate/up GEMMs read each token row once per weight block, so converting here
+// saves that many conversions.
+__global__ __launch_bounds__(256) void convert_x_kernel(const uint16_t *__restrict__ x,
+                                                        uint16_t *__restrict__ xh, size_t n8)
+{
+    const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    reinterpret_cast<uint4 *>(xh)[i] = bf16_octet_to_f16_pairs(reinterpret_cast<const uint4 *>(x)[i]);
+}
+
 __device__ __forceinline__ h2_t scale_pair(uint16_t bf)
 {
     const _Float16 s = (_Float16)(bf16_to_f32(bf) * kScaleUp);
@@ -208,10 +220,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     auto store_a = [&](int buf) {
         uint4 *dst = reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 32 * ahalf);
 #pragma unroll
-        for (int o = 0; o < 4; ++o) {
-            const uint4 v = kW13 ? bf16_octet_to_f16_pairs(ra[o]) : ra[o];
-            dst[o] = avalid ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int o = 0; o < 4; ++o) dst[o] = avalid ? ra[o] : make_uint4(0, 0, 0, 0);
     };
 
     // ---- weight fragments: lane -> (row n = base + lane % 32, octets 4 * half ..) ----
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     const int mtiles = (rows + 31) / 32;
 
     // one K stage: stage s's weights (set q) against LDS buffer s % 2, while
-    // stage s+1's activations are stored and stages s+1/s+2's loads are in flight
+    // stage s+1's activations are stored and the next stages' loads are in flight
     auto stage = [&](int s, int q) {
         if (s + 1 < nsteps) store_a((s + 1) & 1);   // loaded one stage ago
         // keep this stage's raw weights and scales; the set is reloaded below
@@ -272,9 +281,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
                 for (int u = 0; u < 7; ++u) w6[nt][u] = rb6[q][nt][u];
         }
         {   // the last stages re-load the last one (no branch around loads)
-            const int sn = min(s + 2, nsteps - 1);
-            load_a(sn);
-            load_b(sn, q);
+            load_a(min(s + 2, nsteps - 1));
+            load_b(min(s + 2, nsteps - 1), q);
         }
         // activation fragments of all four row tiles are read one MFMA step
         // ahead (rows past the tile hold zeros); weight operands are converted
@@ -524,13 +532,15 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
                                   const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid)
 {
     hipError_t e;
+    const size_t xn8 = (size_t)d.T * d.H / 8;
+    convert_x_kernel<<<(unsigned)((xn8 + 255) / 256), 256, 0, st>>>(a.x, ws.xh, xn8);
     build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, d.E, ws.tiles, ws.n_tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint16_t *y = ws.y;
     // routed gate/up -> h (sorted slot order)
     const int tmax = max_routed_tiles(d);
     GemmArgs g{};
-    g.x = a.x; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
+    g.x = ws.xh; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
     g.offsets = ro.offsets; g.counts = ro.counts; g.sorted_slots = ro.sorted_slots;
     g.h_out = ws.h; g.T = d.T; g.H = d.H; g.I = d.I; g.k = d.k; g.K = d.H;
     g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H / kGroup);
@@ -546,7 +556,7 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
         // shared expert: gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
         if ((e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;
         GemmArgs gs{};
-        gs.x = a.x; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
+        gs.x = ws.xh; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
         gs.T = d.T; gs.H = d.H; gs.I = d.sh_I; gs.k = d.k; gs.K = d.H;
         if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) return e;
         GemmArgs gs2{};
