@@ -78,6 +78,9 @@ __device__ __forceinline__ void octet_to_pair_order(const uint32_t in[4], uint32
     out[3] = __builtin_amdgcn_perm(in[3], in[1], 0x07060302u);
 }
 
+// Position of element i (0..7) of an 8-block in nibble-pair order.
+__device__ __forceinline__ int pair_pos(int i) { return (i < 4) ? 2 * i : 2 * (i - 4) + 1; }
+
 // sum over 32 (code+8+128) * x of one 16-byte chunk of 4 INT4 words, with x
 // given as 16 dwords in nibble-pair order.
 __device__ __forceinline__ float chunk_dot(const uint4 w, const uint32_t x[16])

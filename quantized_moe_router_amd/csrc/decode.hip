@@ -150,7 +150,10 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
 constexpr int kTileOut = 16;  // outputs of a per workgroup (4 waves x 2 quads x 2)
 
 
-// Writes h[i] for i in [i0, i0 + 4) to hrow[i - hbase] (hrow may be in LDS).
+// Writes h[i] for i in [i0, i0 + 4) to hrow[pair(i) - hbase] (hrow may be in
+// LDS), where pair(i) places each 8-block in nibble-pair order
+// (0,4)(1,5)(2,6)(3,7): the order in which the down projection's weight
+// nibbles come out of a word, so h needs no reordering there.
 template <int CPL>
 __device__ __forceinline__ void w13_int4_tile(const ExpertArgs &a, const Dims &d, int e, int t,
                                               uint16_t *hrow, int i0, int lane, int hbase = 0)
@@ -194,8 +197,10 @@ __device__ __forceinline__ void w13_int4_tile(const ExpertArgs &a, const Dims &d
         acc += __shfl_xor(acc, 2, kWave);
         acc += __shfl_xor(acc, 1, kWave);
         const float up = __shfl(acc, (lane + 32) & (kWave - 1), kWave);
-        if (lane == 0 || lane == 16)
-            hrow[i0 + 2 * qd + grp - hbase] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
+        if (lane == 0 || lane == 16) {
+            const int i = i0 + 2 * qd + grp;
+            hrow[((i & ~7) | pair_pos(i & 7)) - hbase] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
+        }
     }
 }
 
@@ -274,26 +279,35 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
 }
 
 // ---------------------------------------------------------------------------
-// 3. down projection + combine: each workgroup owns 16 output rows (4 lanes
-//    per row, lane q reads chunks q + 4c) and all slots; waves take slots
-//    round-robin and their partial sums are added in wave order.
+// 3. down projection + combine.  Each workgroup owns kDnRows output rows and
+//    every slot.  A lane group of 32 lanes takes one slot at a time (4 lanes
+//    per row; lane q reads chunks q + 4c of the row), 2 groups per wave, so a
+//    workgroup has 16 groups; group g takes the slots g, g + 16, ...  Each
+//    group keeps its own partial sum per (token, row), and the partials are
+//    added in group order at the end (a fixed order: deterministic).  The
+//    weights of a batch of slots are requested before the activations are
+//    staged in LDS, so the two latencies overlap.  h arrives in nibble-pair
+//    order; each 32-value chunk's sum (for the +8 code bias) is formed once
+//    while staging, not once per output row.
 // ---------------------------------------------------------------------------
 constexpr int kDnWaves = 8;
-constexpr int kDnRows = 16;
-constexpr int kDnBatch = 4;               // slots whose weights are in flight together
-constexpr int kDnHBytes = 64 * 1024;      // LDS for staged activations
+constexpr int kDnRows = 8;
+constexpr int kDnGroups = kDnWaves * 2;    // 32-lane slot groups per workgroup
+constexpr int kDnBatch = 1;               // slots per group with weights in flight
+constexpr int kDnHBytes = 64 * 1024;      // LDS for staged activations (holds k * I fp16 for k <= 32, I <= 1024)
 constexpr int kDnMaxGroup = 16;           // tokens per LDS group
 
 template <int CPL, int SHCPL>
-__global__ __launch_bounds__(kDnWaves *kWave) void w2_rows_kernel(ExpertArgs a, Dims d,
+__global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) void w2_rows_kernel(ExpertArgs a, Dims d,
                                                                  Workspace ws,
                                                                  const int32_t *__restrict__ ids,
                                                                  const float *__restrict__ wts)
 {
     __shared__ __align__(16) uint16_t s_h[kDnHBytes / 2];
-    __shared__ float s_part[kDnWaves][kDnMaxGroup][kDnRows];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-    const int q = lane & 3, rl = lane >> 2;
+    __shared__ float s_hs[kDnHBytes / 64];                  // chunk sums (32 values each)
+    __shared__ float s_part[kDnGroups][kDnMaxGroup][kDnRows];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int grp = wave * 2 + (lane >> 5), rl = (lane >> 2) & 7, q = lane & 3;
     const int row = blockIdx.x * kDnRows + rl;
     const int nck = d.I / 32, words = d.I / 8, nsc = d.I / kGroup;
     const int slots_per_group = kDnHBytes / (2 * d.I);
@@ -303,25 +317,18 @@ __global__ __launch_bounds__(kDnWaves *kWave) void w2_rows_kernel(ExpertArgs a, 
     for (int t0 = 0; t0 < d.T; t0 += tg) {
         const int nt = min(tg, d.T - t0);
         const int s0 = t0 * d.k, ns = nt * d.k;
-        // stage the group's activations (ns x I fp16) into LDS
-        {
-            const uint4 *src = reinterpret_cast<const uint4 *>(ws.h + (size_t)s0 * d.I);
-            uint4 *dst = reinterpret_cast<uint4 *>(s_h);
-            const int n16 = ns * d.I / 8;
-            for (int i = threadIdx.x; i < n16; i += kDnWaves * kWave) dst[i] = src[i];
-        }
-        for (int i = threadIdx.x; i < kDnWaves * kDnMaxGroup * kDnRows; i += kDnWaves * kWave)
+        for (int i = tid; i < kDnGroups * kDnMaxGroup * kDnRows; i += kDnWaves * kWave)
             (&s_part[0][0][0])[i] = 0.f;
-        __syncthreads();
-
-        for (int b0 = wave; b0 < ns; b0 += kDnWaves * kDnBatch) {
+        bool staged = false;
+        for (int b0 = grp; b0 < ns || !staged; b0 += kDnGroups * kDnBatch) {
+            // this group's next batch of slots: weights first
             uint4 w[kDnBatch][CPL];
             float sc[kDnBatch][CPL];
             int sl[kDnBatch];
             float rw[kDnBatch];
 #pragma unroll
             for (int u = 0; u < kDnBatch; ++u) {
-                const int sr = b0 + u * kDnWaves;  // slot relative to the group
+                const int sr = b0 + u * kDnGroups;  // slot relative to the token group
                 sl[u] = sr;
                 const int sg = s0 + (sr < ns ? sr : 0);
                 const int e = clamp_expert(ids[sg], d.E);
@@ -336,6 +343,27 @@ __global__ __launch_bounds__(kDnWaves *kWave) void w2_rows_kernel(ExpertArgs a, 
                     sc[u][c] = ok ? s : 0.f;
                 }
             }
+            if (!staged) {
+                // the group's activations (ns x I fp16, nibble-pair order) into LDS, once
+                const uint4 *src = reinterpret_cast<const uint4 *>(ws.h + (size_t)s0 * d.I);
+                uint4 *dst = reinterpret_cast<uint4 *>(s_h);
+                const int n16 = ns * d.I / 8;
+                for (int i = tid; i < n16; i += kDnWaves * kWave) dst[i] = src[i];
+                __syncthreads();
+                for (int i = tid; i < ns * nck; i += kDnWaves * kWave) {
+                    const uint4 *cp = reinterpret_cast<const uint4 *>(s_h + (size_t)i * 32);
+                    float hs = 0.f;
+#pragma unroll
+                    for (int o = 0; o < 4; ++o) {
+                        const uint4 v = cp[o];
+                        hs = dot2h(v.x, 0x3C003C00u, hs); hs = dot2h(v.y, 0x3C003C00u, hs);
+                        hs = dot2h(v.z, 0x3C003C00u, hs); hs = dot2h(v.w, 0x3C003C00u, hs);
+                    }
+                    s_hs[i] = hs;
+                }
+                __syncthreads();
+                staged = true;
+            }
 #pragma unroll
             for (int u = 0; u < kDnBatch; ++u) {
                 if (sl[u] >= ns) break;
@@ -343,20 +371,26 @@ __global__ __launch_bounds__(kDnWaves *kWave) void w2_rows_kernel(ExpertArgs a, 
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     const int kc = q + 4 * c, kcl = kc < nck ? kc : 0;
-                    const ActRaw raw = *reinterpret_cast<const ActRaw *>(s_h + (size_t)sl[u] * d.I + kcl * 32);
+                    const uint4 *hp = reinterpret_cast<const uint4 *>(s_h + (size_t)sl[u] * d.I + kcl * 32);
                     uint32_t hv[16];
-                    const float hs = act_pairs_h(raw, hv);
+#pragma unroll
+                    for (int o = 0; o < 4; ++o) {
+                        const uint4 v = hp[o];
+                        hv[4 * o] = v.x; hv[4 * o + 1] = v.y; hv[4 * o + 2] = v.z; hv[4 * o + 3] = v.w;
+                    }
+                    const float hs = s_hs[sl[u] * nck + kcl];
                     acc = fmaf(sc[u][c], chunk_dot_h(w[u][c], hv) - 136.f * hs, acc);
                 }
                 acc += __shfl_xor(acc, 2, kWave);
                 acc += __shfl_xor(acc, 1, kWave);
-                if (q == 0) s_part[wave][sl[u] / d.k][rl] += rw[u] * acc;
+                if (q == 0) s_part[grp][sl[u] / d.k][rl] += rw[u] * acc;
             }
+            if (b0 >= ns) break;   // a group with no slots only helped to stage
         }
-        // shared expert: one extra slot per token, INT6 rows of the same 16 outputs
+        // shared expert: one extra slot per token, INT6 rows of the same outputs
         if (d.sh_I > 0) {
             const int snck = d.sh_I / 32, swords = d.sh_I / 32 * 6, snsc = d.sh_I / kShGroup;
-            for (int tl = wave; tl < nt; tl += kDnWaves) {
+            for (int tl = grp; tl < nt; tl += kDnGroups) {
                 const int t = t0 + tl;
                 float acc = 0.f;
 #pragma unroll
@@ -372,15 +406,14 @@ __global__ __launch_bounds__(kDnWaves *kWave) void w2_rows_kernel(ExpertArgs a, 
                 acc += __shfl_xor(acc, 2, kWave);
                 acc += __shfl_xor(acc, 1, kWave);
                 const float g = 1.f / (1.f + expf(-ws.shared_gate[t]));
-                if (q == 0) s_part[wave][tl][rl] += g * acc;
+                if (q == 0) s_part[grp][tl][rl] += g * acc;
             }
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < nt * kDnRows; i += kDnWaves * kWave) {
+        for (int i = tid; i < nt * kDnRows; i += kDnWaves * kWave) {
             const int tl = i / kDnRows, r = i % kDnRows;
             float acc = 0.f;
-#pragma unroll
-            for (int w = 0; w < kDnWaves; ++w) acc += s_part[w][tl][r];
+            for (int g2 = 0; g2 < kDnGroups; ++g2) acc += s_part[g2][tl][r];
             a.out[(size_t)(t0 + tl) * d.H + blockIdx.x * kDnRows + r] = (uint16_t)f32_to_bf16(acc);
         }
         __syncthreads();

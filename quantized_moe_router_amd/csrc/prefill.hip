@@ -73,9 +73,6 @@ struct GemmArgs {
     size_t b_scales;           // scales per expert
 };
 
-// Position of element i (0..7) of an 8-block in nibble-pair order.
-__device__ __forceinline__ int pair_pos(int i) { return (i < 4) ? 2 * i : 2 * (i - 4) + 1; }
-
 // INT4 word -> one MFMA operand: 8 fp16 values code * s in pair order
 // (0,4)(1,5)(2,6)(3,7); s2 = fp16 pair (s, s).
 __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, h2_t s2)

@@ -45,19 +45,30 @@ struct TopkLane {
     float w;
 };
 
-__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+// Population count of a ballot as a 32-bit value (two 32-bit counts: a 64-bit
+// count would be compared on the vector unit, the scalar unit has no 64-bit
+// ordered compare).
+__device__ __forceinline__ int popc(uint64_t m)
+{
+    return __builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32));
+}
 
 // Largest V with #{keys >= V} >= k, by a binary search over the 32 key bits.
+// k must be wave-uniform; it is read into a scalar register so that the count
+// and the choice of each bit stay on the scalar unit (a vector compare there
+// would bounce every step between the vector and scalar units).
 template <int KPL>
 __device__ __forceinline__ uint32_t kth_key(const uint32_t (&val)[KPL], int k)
 {
+    const uint32_t ku = (uint32_t)__builtin_amdgcn_readfirstlane(k);
     uint32_t V = 0;
+#pragma unroll
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = V | (1u << b);
-        int cnt = 0;
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) cnt += popc(__ballot(val[i] >= cand));
-        if (cnt >= k) V = cand;
+        for (int i = 0; i < KPL; ++i) cnt += (uint32_t)popc(__ballot(val[i] >= cand));
+        V = cnt >= ku ? cand : V;
     }
     return V;
 }
@@ -96,8 +107,9 @@ __device__ __forceinline__ int compact_keys(const uint32_t (&val)[KPL], uint32_t
 // lane + 64 i (0 where the expert does not exist).  Requires 1 <= k <= 32 and
 // at least k existing experts.  Lane j < k returns the j-th selection.
 template <int KPL>
-__device__ TopkLane wave_topk_keys(const uint32_t (&val)[KPL], int k, int lane, uint32_t *lds)
+__device__ TopkLane wave_topk_keys(const uint32_t (&val)[KPL], int k_in, int lane, uint32_t *lds)
 {
+    const int k = __builtin_amdgcn_readfirstlane(k_in);   // uniform: scalar compares
     uint32_t m = val[0];
 #pragma unroll
     for (int i = 1; i < KPL; ++i) m = max(m, val[i]);
