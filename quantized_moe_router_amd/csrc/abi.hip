@@ -38,7 +38,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t route_ticket, tile_ticket, logits, ids, weights, counts, offsets, sorted_slots,
-        slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, xh, total;
+        slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, xh, xp, xs, total;
 };
 
 Layout layout(const Dims &d)
@@ -70,6 +70,8 @@ Layout layout(const Dims &d)
     L.shared_gate = take(4 * T);
     L.sh_h = take(2 * T * (size_t)d.sh_I);
     L.xh = take(d.T > kDecodeMaxTokens ? 2 * T * (size_t)d.H : 0);
+    L.xp = take(d.T <= kDecodeMaxTokens ? 2 * T * (size_t)d.H : 0);
+    L.xs = take(d.T <= kDecodeMaxTokens ? 4 * T * (size_t)(d.H / 32) : 0);
     L.total = off;
     return L;
 }
@@ -180,6 +182,8 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
     w.shared_gate = reinterpret_cast<float *>(b + L.shared_gate);
     w.sh_h = reinterpret_cast<uint16_t *>(b + L.sh_h);
     w.xh = reinterpret_cast<uint16_t *>(b + L.xh);
+    w.xp = reinterpret_cast<uint16_t *>(b + L.xp);
+    w.xs = reinterpret_cast<float *>(b + L.xs);
     w.bytes = L.total;
     *out = w;
     return MOE_INT4_OK;

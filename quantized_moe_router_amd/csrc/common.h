@@ -11,6 +11,7 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
+constexpr int kMaxHidden = 4096;
 constexpr int kGroup = 128;      // INT4 group along the input dimension
 constexpr int kShGroup = 64;     // INT6 group (shared expert)
 // Decode (GEMV) path for T <= kDecodeMaxTokens, grouped-GEMM path above.
@@ -275,6 +276,8 @@ struct Workspace {
     float *shared_gate;      // [T] shared-expert gate logits
     uint16_t *sh_h;          // [T][I_sh] fp16
     uint16_t *xh;            // [T][H] fp16 copy of x in nibble-pair order (many-token path)
+    uint16_t *xp;            // [T][H] bf16 copy of x in nibble-pair order (decode path)
+    float *xs;               // [T][H/32] sums of 32-value chunks of x (decode path)
     size_t bytes;
 };
 

@@ -6,8 +6,8 @@
 //                           (and builds the permutation for the routing-only
 //                           entry point)
 //   2. w13_slot_kernel      per (slot, 16-output tile): the INT4 gate/up GEMV
-//                           and a = silu(g) * u -> fp16; extra slots run the
-//                           INT6 shared expert's gate/up
+//                           and a = silu(g) * u -> fp16 (w13_shared_kernel:
+//                           the INT6 shared expert's gate/up per token)
 //   3. w2_rows_kernel       each workgroup owns 16 output rows and sums, in a
 //                           fixed order, every slot's down projection weighted
 //                           by its routing weight (plus sigmoid(gate) times the
@@ -106,6 +106,28 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
             }
         }
     }
+    // x in nibble-pair order with its 32-value chunk sums, for the gate/up kernel
+    {
+        const int nchunk = d.T * (d.H / 32);
+        for (int ci = blockIdx.x * blockDim.x + tid; ci < nchunk; ci += gridDim.x * blockDim.x) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(r.x) + (size_t)ci * 4;
+            uint4 *dst = reinterpret_cast<uint4 *>(r.ws.xp) + (size_t)ci * 4;
+            float sum = 0.f;
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const uint4 v = src[o];
+                const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+                uint32_t pr[4];
+                octet_to_pair_order(in, pr);
+                sum = dot2(in[0], 0x3F803F80u, sum);  // bf16 (1.0, 1.0)
+                sum = dot2(in[1], 0x3F803F80u, sum);
+                sum = dot2(in[2], 0x3F803F80u, sum);
+                sum = dot2(in[3], 0x3F803F80u, sum);
+                dst[o] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+            }
+            r.ws.xs[ci] = sum;
+        }
+    }
     if (r.tail == kTailNone) return;
 
     __syncthreads();
@@ -149,60 +171,6 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
 // ---------------------------------------------------------------------------
 constexpr int kTileOut = 16;  // outputs of a per workgroup (4 waves x 2 quads x 2)
 
-
-// Writes h[i] for i in [i0, i0 + 4) to hrow[pair(i) - hbase] (hrow may be in
-// LDS), where pair(i) places each 8-block in nibble-pair order
-// (0,4)(1,5)(2,6)(3,7): the order in which the down projection's weight
-// nibbles come out of a word, so h needs no reordering there.
-template <int CPL>
-__device__ __forceinline__ void w13_int4_tile(const ExpertArgs &a, const Dims &d, int e, int t,
-                                              uint16_t *hrow, int i0, int lane, int hbase = 0)
-{
-    const int grp = lane >> 4, q = lane & 15;
-    const int nck = d.H / 32, words = d.H / 8, nsc = d.H / kGroup;
-    ActRaw raw[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int kc = q + 16 * c, kcl = kc < nck ? kc : 0;
-        raw[c] = load_act_raw(a.x + (size_t)t * d.H + kcl * 32);
-    }
-    uint4 w[2][CPL];
-    float sc[2][CPL];
-#pragma unroll
-    for (int qd = 0; qd < 2; ++qd) {
-        const int i = i0 + 2 * qd;
-        const int row = (grp < 2) ? i + grp : d.I + i + (grp - 2);
-        const size_t r = (size_t)e * 2 * d.I + row;
-        const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w13p + r * words);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int kc = q + 16 * c, ok = kc < nck, kcl = ok ? kc : 0;
-            w[qd][c] = load_stream(wrow + kcl);
-            const float s = bf16_to_f32(a.w13s[r * nsc + kcl / 4]);
-            sc[qd][c] = ok ? s : 0.f;
-        }
-    }
-    uint32_t xv[CPL][16];
-    float xs[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) xs[c] = act_pairs(raw[c], xv[c]);
-#pragma unroll
-    for (int qd = 0; qd < 2; ++qd) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-            acc = fmaf(sc[qd][c], chunk_dot(w[qd][c], xv[c]) - 136.f * xs[c], acc);
-        acc += __shfl_xor(acc, 8, kWave);
-        acc += __shfl_xor(acc, 4, kWave);
-        acc += __shfl_xor(acc, 2, kWave);
-        acc += __shfl_xor(acc, 1, kWave);
-        const float up = __shfl(acc, (lane + 32) & (kWave - 1), kWave);
-        if (lane == 0 || lane == 16) {
-            const int i = i0 + 2 * qd + grp;
-            hrow[((i & ~7) | pair_pos(i & 7)) - hbase] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
-        }
-    }
-}
 
 // Shared expert (INT6, group 64) gate/up for one token: same lane layout, 32
 // codes (six words) per chunk.
@@ -258,24 +226,93 @@ __device__ __forceinline__ void w13_int6_tile(const ExpertArgs &a, const Dims &d
     }
 }
 
-// grid (max(I, sh_I) / 16, S + (shared ? T : 0)); expert ids of the slots
-// from `ids` (written by the router's tail, or given by the caller).
+// Shared expert gate/up: grid (sh_I / 16, T).
+template <int CPL>
+__global__ __launch_bounds__(256) void w13_shared_kernel(ExpertArgs a, Dims d, Workspace ws)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    const int t = blockIdx.y;
+    w13_int6_tile<CPL>(a, d, t, ws.sh_h + (size_t)t * d.sh_I, blockIdx.x * kTileOut + wave * 4, lane);
+}
+
+// Routed gate/up: grid (I / 16, S); expert ids of the slots from `ids`
+// (written by the router's tail, or given by the caller).
+// Routed slots: wave w computes h[i] for i in [i0, i0 + 4), i0 = 16 x + 4 w:
+// the weight chunks are requested first, then the token's activations (already
+// in nibble-pair order, with their chunk sums) are staged in LDS, which keeps
+// them out of registers and lets more workgroups share a CU.  h is stored in
+// nibble-pair order (0,4)(1,5)(2,6)(3,7) within each 8-block: the order in
+// which the down projection's weight nibbles come out of a word.
 template <int CPL>
 __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Workspace ws,
                                                        const int32_t *__restrict__ ids)
 {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    __shared__ __align__(16) uint16_t s_x[kMaxHidden];
+    __shared__ float s_xs[kMaxHidden / 32];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int s = blockIdx.y;
     const int i0 = blockIdx.x * kTileOut + wave * 4;
-    if (s >= d.S) {  // shared expert of token s - S
-        if (blockIdx.x * kTileOut >= d.sh_I) return;
-        const int t = s - d.S;
-        w13_int6_tile<CPL>(a, d, t, ws.sh_h + (size_t)t * d.sh_I, i0, lane);
-        return;
-    }
     if (blockIdx.x * kTileOut >= d.I) return;
-    const int t = s / d.k;
-    w13_int4_tile<CPL>(a, d, clamp_expert(ids[s], d.E), t, ws.h + (size_t)s * d.I, i0, lane);
+    const int t = s / d.k, e = clamp_expert(ids[s], d.E);
+    const int grp = lane >> 4, q = lane & 15;
+    const int nck = d.H / 32, words = d.H / 8, nsc = d.H / kGroup;
+    // the token's activations first (cache-hot; the LDS store waits only for
+    // them, since loads complete in issue order), then the weights
+    constexpr int kXPer = kMaxHidden / 8 / 256;
+    uint4 xr[kXPer];
+    float xsr = 0.f;
+    {
+        const uint4 *xsrc = reinterpret_cast<const uint4 *>(ws.xp + (size_t)t * d.H);
+#pragma unroll
+        for (int j = 0; j < kXPer; ++j) {
+            const int i = tid + 256 * j;
+            xr[j] = xsrc[i < d.H / 8 ? i : 0];
+        }
+        xsr = ws.xs[(size_t)t * nck + (tid < nck ? tid : 0)];
+    }
+    uint4 w[2][CPL];
+    float sc[2][CPL];
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) {
+        const int i = i0 + 2 * qd;
+        const int row = (grp < 2) ? i + grp : d.I + i + (grp - 2);
+        const size_t r = (size_t)e * 2 * d.I + row;
+        const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w13p + r * words);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int kc = q + 16 * c, ok = kc < nck, kcl = ok ? kc : 0;
+            w[qd][c] = load_stream(wrow + kcl);
+            const float sv = bf16_to_f32(a.w13s[r * nsc + kcl / 4]);
+            sc[qd][c] = ok ? sv : 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+        const int i = tid + 256 * j;
+        if (i < d.H / 8) reinterpret_cast<uint4 *>(s_x)[i] = xr[j];
+    }
+    if (tid < nck) s_xs[tid] = xsr;
+    __syncthreads();
+    uint16_t *hrow = ws.h + (size_t)s * d.I;
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int kc = q + 16 * c, kcl = kc < nck ? kc : 0;
+            const uint32_t *xv = reinterpret_cast<const uint32_t *>(s_x + kcl * 32);
+            acc = fmaf(sc[qd][c], chunk_dot(w[qd][c], xv) - 136.f * s_xs[kcl], acc);
+        }
+        acc += __shfl_xor(acc, 8, kWave);
+        acc += __shfl_xor(acc, 4, kWave);
+        acc += __shfl_xor(acc, 2, kWave);
+        acc += __shfl_xor(acc, 1, kWave);
+        const float up = __shfl(acc, (lane + 32) & (kWave - 1), kWave);
+        if (lane == 0 || lane == 16) {
+            const int i = i0 + 2 * qd + grp;
+            hrow[(i & ~7) | pair_pos(i & 7)] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -428,7 +465,8 @@ static int cpl_of(int chunks, int lanes) { return (chunks + lanes - 1) / lanes; 
 static hipError_t launch_router(const RouterArgs &r, hipStream_t st)
 {
     const int rows = r.nrouted + (r.gate_w ? 1 : 0);
-    const int grid = (rows + kRtWaves - 1) / kRtWaves;
+    const int nchunk = r.d.T * (r.d.H / 32);
+    const int grid = max((rows + kRtWaves - 1) / kRtWaves, (nchunk + kRtWaves * kWave - 1) / (kRtWaves * kWave));
     switch (cpl_of(r.d.H / 8, kWave)) {
 #define MOE_CASE(N) \
     case N: router_kernel<N><<<grid, kRtWaves * kWave, 0, st>>>(r); break;
@@ -448,11 +486,21 @@ hipError_t launch_decode_route(const uint16_t *x, const uint16_t *router_w, cons
 static hipError_t launch_w13_slots(const ExpertArgs &a, const Dims &d, const Workspace &ws,
                                    const int32_t *ids, hipStream_t st)
 {
-    const int outs = d.I > d.sh_I ? d.I : d.sh_I;
-    dim3 grid(outs / kTileOut, d.S + (d.sh_I ? d.T : 0));
-    switch (cpl_of(d.H / 32, 16)) {
+    const int cpl = cpl_of(d.H / 32, 16);
+    dim3 grid(d.I / kTileOut, d.S);
+    switch (cpl) {
 #define MOE_CASE(N) \
     case N: w13_slot_kernel<N><<<grid, 256, 0, st>>>(a, d, ws, ids); break;
+        MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
+#undef MOE_CASE
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || d.sh_I == 0) return e;
+    dim3 sgrid(d.sh_I / kTileOut, d.T);
+    switch (cpl) {
+#define MOE_CASE(N) \
+    case N: w13_shared_kernel<N><<<sgrid, 256, 0, st>>>(a, d, ws); break;
         MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
     default: return hipErrorInvalidValue;
@@ -492,11 +540,10 @@ hipError_t launch_decode_experts(const ExpertArgs &a, const int32_t *ids, const 
                                  const Dims &d, const Workspace &ws, hipStream_t st)
 {
     hipError_t e;
-    if (d.sh_I > 0) {
-        RouteOut none{};
-        e = launch_router(RouterArgs{a.x, nullptr, a.sh_gate, 0, d, ws, none, kTailNone}, st);
-        if (e != hipSuccess) return e;
-    }
+    RouteOut none{};
+    // x in pair order (and the shared-expert gate logit, if any)
+    e = launch_router(RouterArgs{a.x, nullptr, a.sh_gate, 0, d, ws, none, kTailNone}, st);
+    if (e != hipSuccess) return e;
     if ((e = launch_w13_slots(a, d, ws, ids, st)) != hipSuccess) return e;
     return launch_w2_rows(a, d, ws, ids, wts, st);
 }
