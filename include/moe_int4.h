@@ -60,7 +60,8 @@ extern "C" {
 
 /* Layer dimensions.  Limits: tokens >= 0 (0 is a no-op); 1 <= top_k <=
  * min(experts, 32); experts <= 1024; group == 128; hidden a multiple of 256,
- * at most 4096; inter a multiple of 128, at most 1024. */
+ * at most 4096; inter a multiple of 128, at most 1024; tokens * hidden and
+ * tokens * top_k * inter (and tokens * shared inter) below 2^31. */
 typedef struct moe_int4_shape {
     int32_t tokens;  /* T */
     int32_t hidden;  /* H */

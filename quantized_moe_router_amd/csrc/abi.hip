@@ -138,6 +138,12 @@ int32_t check_shape(const moe_int4_shape *s, const moe_shared_int6 *sh, Dims *d)
             return fail(MOE_INT4_EALIGN, "a shared-expert pointer is not 16-byte aligned");
         d->sh_I = sh->inter;
     }
+    // element offsets inside one activation buffer are 32-bit in the kernels
+    const size_t lim = (size_t)1 << 31;
+    if ((size_t)d->T * d->H >= lim || (size_t)d->S * d->I >= lim || (size_t)d->T * d->sh_I >= lim)
+        return fail(MOE_INT4_EINVAL,
+                    "tokens=%d too many for one call: tokens*hidden and tokens*top_k*inter must stay "
+                    "below 2^31 (split the batch)", d->T);
     return MOE_INT4_OK;
 }
 

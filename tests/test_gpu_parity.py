@@ -161,6 +161,17 @@ def test_caller_routing_entry(T):
     check_output(bf16_to_f64(out.cpu().numpy()), ref)
 
 
+@pytest.mark.parametrize("T,shared", [(600, False), (1111, False), (700, True)])
+def test_many_rows_per_expert(T, shared):
+    """Over 128 rows per expert on average: every expert spans several
+    128-row tiles with a ragged last one, and the dense shared-expert GEMMs
+    end in a ragged token tile.  Every token checked against the oracle."""
+    shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=4, inter=256)
+    host = synth.make_layer(shape, seed=30 + T, shared=shared)
+    assert T * 4 >= 128 * 16
+    run_and_check(host, label=f"many rows per expert T={T} shared={shared}")
+
+
 @pytest.mark.parametrize("T", [2, 30])
 def test_deterministic(T):
     shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=2, inter=128)
