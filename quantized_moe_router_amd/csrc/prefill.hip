@@ -33,6 +33,8 @@
 //   * workgroup -> tile order is XCD-aware: the weight-row blocks of one token
 //     tile go to the same XCD back to back, so the gathered activations are
 //     re-read from that XCD's L2.
+#include <type_traits>
+
 #include "int6.h"
 
 namespace moe {
@@ -209,15 +211,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     const uint16_t *asrc;
     if constexpr (kW13) asrc = g.x + (size_t)s_tok[arow] * g.H + 32 * ahalf;
     else asrc = g.a16 + (size_t)(kRouted ? pbase + arow : s_tok[arow]) * K + 32 * ahalf;
-    uint4 ra[4];
-    auto load_a = [&](int s) {
+    // two register sets: stage s's activations are loaded two stages before
+    // they are used (set s % 2) and stored to LDS one stage before
+    uint4 ra[2][4];
+    auto load_a = [&](int s, int p) {
 #pragma unroll
-        for (int o = 0; o < 4; ++o) ra[o] = reinterpret_cast<const uint4 *>(asrc + s * kKS)[o];
+        for (int o = 0; o < 4; ++o) ra[p][o] = reinterpret_cast<const uint4 *>(asrc + s * kKS)[o];
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int buf, int p) {
         uint4 *dst = reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 32 * ahalf);
 #pragma unroll
-        for (int o = 0; o < 4; ++o) dst[o] = avalid ? ra[o] : make_uint4(0, 0, 0, 0);
+        for (int o = 0; o < 4; ++o) dst[o] = avalid ? ra[p][o] : make_uint4(0, 0, 0, 0);
     };
 
     // ---- weight fragments: lane -> (row n = base + lane % 32, octets 4 * half ..) ----
@@ -261,79 +265,97 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
     const int mtiles = (rows + 31) / 32;
 
-    // one K stage: stage s's weights (set q) against LDS buffer s % 2, while
-    // stage s+1's activations are stored and the next stages' loads are in flight
-    auto stage = [&](int s, int q) {
-        if (s + 1 < nsteps) store_a((s + 1) & 1);   // loaded one stage ago
-        // keep this stage's raw weights and scales; the set is reloaded below
-        uint4 w4[2];
-        uint32_t w6[2][7];
-        h2_t s2[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            s2[nt] = scale_pair(rsc[q][nt]);
-            if constexpr (!kInt6) w4[nt] = rb4[q][nt];
-            else
-#pragma unroll
-                for (int u = 0; u < 7; ++u) w6[nt][u] = rb6[q][nt][u];
-        }
-        {   // the last stages re-load the last one (no branch around loads)
-            load_a(min(s + 2, nsteps - 1));
-            load_b(min(s + 2, nsteps - 1), q);
-        }
-        // activation fragments of all four row tiles are read one MFMA step
-        // ahead (rows past the tile hold zeros); weight operands are converted
-        // per step, between the matrix instructions
-        const _Float16 *A = s_a[s & 1] + (lane & 31) * kLdsRow + 32 * half;
-        f16x8_t af[2][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            af[0][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kLdsRow);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < 3) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kLdsRow + 8 * (j + 1));
-            }
-            f16x8_t bf[2];
+    // The K loop, compiled once per number of active 32-row tiles (MA) and
+    // chosen once per workgroup: with the count known at compile time there
+    // is no branch between the matrix instructions, so the activation reads of
+    // the next MFMA step can be issued ahead of them (a branch per tile left
+    // each read waiting on its own).  Waves whose staging rows lie past the
+    // active tiles do not load or store activations.
+    auto kloop = [&](auto ma_c) {
+        constexpr int MA = decltype(ma_c)::value;
+        const bool astage = ar < 32 * MA;     // uniform per wave
+
+        // one K stage: stage s's weights (set q = s % 2) against LDS buffer q,
+        // while stage s+1's activations (set 1-q, loaded two stages ago) are
+        // stored and the loads of stages s+3 (activations) and s+2 (weights)
+        // are issued
+        auto stage = [&](int s, int q) {
+            if (astage && s + 1 < nsteps) store_a(q ^ 1, q ^ 1);
+            // keep this stage's raw weights and scales; the set is reloaded below
+            uint4 w4[2];
+            uint32_t w6[2][7];
+            h2_t s2[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                if constexpr (!kInt6) {
-                    const uint32_t wj = j == 0 ? w4[nt].x : j == 1 ? w4[nt].y : j == 2 ? w4[nt].z : w4[nt].w;
-                    bf[nt] = dequant_int4_f16(wj, s2[nt]);
-                } else {
-                    bf[nt] = j == 0 ? dequant_int6_octet<0>(w6[nt], s2[nt])
-                           : j == 1 ? dequant_int6_octet<1>(w6[nt], s2[nt])
-                           : j == 2 ? dequant_int6_octet<2>(w6[nt], s2[nt])
-                                    : dequant_int6_octet<3>(w6[nt], s2[nt]);
-                }
-            }
+                s2[nt] = scale_pair(rsc[q][nt]);
+                if constexpr (!kInt6) w4[nt] = rb4[q][nt];
+                else
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (mt < mtiles) {
+                    for (int u = 0; u < 7; ++u) w6[nt][u] = rb6[q][nt][u];
+            }
+            {   // the last stages re-load the last one (no branch around loads)
+                if (astage) load_a(min(s + 3, nsteps - 1), q ^ 1);
+                load_b(min(s + 2, nsteps - 1), q);
+            }
+            // activation fragments of the active row tiles are read one MFMA
+            // step ahead; weight operands are converted per step, between the
+            // matrix instructions
+            const _Float16 *A = s_a[s & 1] + (lane & 31) * kLdsRow + 32 * half;
+            f16x8_t af[2][MA];
+#pragma unroll
+            for (int mt = 0; mt < MA; ++mt)
+                af[0][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kLdsRow);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < 3) {
+#pragma unroll
+                    for (int mt = 0; mt < MA; ++mt)
+                        af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kLdsRow + 8 * (j + 1));
+                }
+                f16x8_t bf[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if constexpr (!kInt6) {
+                        const uint32_t wj = j == 0 ? w4[nt].x : j == 1 ? w4[nt].y : j == 2 ? w4[nt].z : w4[nt].w;
+                        bf[nt] = dequant_int4_f16(wj, s2[nt]);
+                    } else {
+                        bf[nt] = j == 0 ? dequant_int6_octet<0>(w6[nt], s2[nt])
+                               : j == 1 ? dequant_int6_octet<1>(w6[nt], s2[nt])
+                               : j == 2 ? dequant_int6_octet<2>(w6[nt], s2[nt])
+                                        : dequant_int6_octet<3>(w6[nt], s2[nt]);
+                    }
+                }
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt) {
                     acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bf[0], acc[mt][0], 0, 0, 0);
                     acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bf[1], acc[mt][1], 0, 0, 0);
                 }
             }
-        }
-        __syncthreads();
-    };
+            __syncthreads();
+        };
 
-    // prologue: stage 0 in LDS, stage 1 activations in registers, weights of
-    // stages 0 and 1 in flight
-    load_a(0);
-    load_b(0, 0);
-    store_a(0);
-    load_a(min(1, nsteps - 1));
-    load_b(min(1, nsteps - 1), 1);
-    __syncthreads();
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-        stage(s, 0);
-        stage(s + 1, 1);
+        // prologue: stage 0 in LDS, stages 1 and 2 activations in registers,
+        // weights of stages 0 and 1 in flight
+        if (astage) load_a(0, 0);
+        load_b(0, 0);
+        if (astage) load_a(min(1, nsteps - 1), 1);
+        load_b(min(1, nsteps - 1), 1);
+        if (astage) store_a(0, 0);
+        if (astage) load_a(min(2, nsteps - 1), 0);
+        __syncthreads();
+        int s = 0;
+        for (; s + 1 < nsteps; s += 2) {
+            stage(s, 0);
+            stage(s + 1, 1);
+        }
+        if (s < nsteps) stage(s, 0);
+    };
+    switch (mtiles) {
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    default: kloop(std::integral_constant<int, 4>{}); break;
     }
-    if (s < nsteps) stage(s, 0);
 
     // ---- epilogue ----
     const int col = lane & 31;
