@@ -32,9 +32,10 @@
  *     holding code+8 for a code in [-8, 7]; weight = code * scale[row][k/G].
  *   - Workspace: a caller-owned device buffer of at least
  *     moe_int4_workspace_bytes() bytes.  It must be ZERO-FILLED before its
- *     first use; every call leaves its counters at zero again when it
- *     completes, so a workspace can be reused without clearing.  Two calls
- *     in flight at the same time need two workspaces.
+ *     first use; its first 64 KiB (the few-token router's hand-off area,
+ *     whatever the shape) are zero again whenever a call completes, so a
+ *     workspace can be reused without clearing, also across shapes.  Two
+ *     calls in flight at the same time need two workspaces.
  *
  * Errors: every entry point returns 0 on success or a negative code.  All
  * checks run on the host before anything is enqueued, so a failing call has

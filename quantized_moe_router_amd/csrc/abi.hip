@@ -37,7 +37,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t route_ticket, tile_ticket, logits, ids, weights, counts, offsets, sorted_slots,
+    size_t dec_keys, logits, ids, weights, counts, offsets, sorted_slots,
         slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, xh, xp, xs, total;
 };
 
@@ -52,8 +52,7 @@ Layout layout(const Dims &d)
     };
     const size_t S = (size_t)d.S, T = (size_t)d.T;
     const size_t nchunks = (S + kPermChunk - 1) / kPermChunk;
-    L.route_ticket = take(4);
-    L.tile_ticket = take(4 * (size_t)(d.H / 64));
+    L.dec_keys = take(4 * (size_t)kDecodeMaxTokens * kMaxExperts);   // same size for every shape
     L.logits = take(4 * T * d.E);
     L.ids = take(4 * S);
     L.weights = take(4 * S);
@@ -170,8 +169,7 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
         return fail(MOE_INT4_EWORKSPACE, "workspace has %zu bytes, %zu needed", bytes, L.total);
     char *b = static_cast<char *>(ws);
     Workspace w{};
-    w.route_ticket = reinterpret_cast<uint32_t *>(b + L.route_ticket);
-    w.tile_ticket = reinterpret_cast<uint32_t *>(b + L.tile_ticket);
+    w.dec_keys = reinterpret_cast<uint32_t *>(b + L.dec_keys);
     w.logits = reinterpret_cast<float *>(b + L.logits);
     w.ids = reinterpret_cast<int32_t *>(b + L.ids);
     w.weights = reinterpret_cast<float *>(b + L.weights);

@@ -241,13 +241,44 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v)
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v)
+// Cross-lane sums with DPP lane moves (VALU only; a shuffle would go through
+// the LDS crossbar with a full wait per step).  Every lane of a quad / row /
+// wave gets the same sum: each step adds a value and its mirror image, and
+// fp32 addition is commutative.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, kWave);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within each 8
+constexpr int kDppMirror = 0x140;      // lane 15 - i within each 16
+
+// Sum over the 4 lanes of a quad.
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += dpp_move<kDppXor1>(v);
+    v += dpp_move<kDppXor2>(v);
     return v;
+}
+// Sum over the 16 lanes of a row.
+__device__ __forceinline__ float row_sum(float v)
+{
+    v = quad_sum(v);
+    v += dpp_move<kDppHalfMirror>(v);
+    v += dpp_move<kDppMirror>(v);
+    return v;
+}
+__device__ __forceinline__ float read_lane(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Sum over the wave (uniform result).
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row_sum(v);
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 // ---------------------------------------------------------------------------
@@ -255,9 +286,8 @@ __device__ __forceinline__ T wave_sum(T v)
 // the zero-state contract covers a fixed prefix.
 // ---------------------------------------------------------------------------
 struct Workspace {
-    // counters (must be zero between calls)
-    uint32_t *route_ticket;  // [1]
-    uint32_t *tile_ticket;   // [H / 64] (row tiles of the decode combine)
+    // zero between calls (a fixed prefix of every layout)
+    uint32_t *dec_keys;      // [kDecodeMaxTokens * kMaxExperts] decode router keys, 0 = unset
     // routing
     float *logits;           // [T][E]
     int32_t *ids;            // [T][k]   (forward: internal copy)

@@ -2,13 +2,13 @@
 //
 //   1. router_kernel        logits[t][e] = x_t . router_w[e]  (bf16, fp32 sum),
 //                           plus the shared-expert gate logit as one more row;
-//                           its last workgroup selects every token's experts
+//                           one extra workgroup selects every token's experts
 //                           (and builds the permutation for the routing-only
 //                           entry point)
 //   2. w13_slot_kernel      per (slot, 16-output tile): the INT4 gate/up GEMV
 //                           and a = silu(g) * u -> fp16 (w13_shared_kernel:
 //                           the INT6 shared expert's gate/up per token)
-//   3. w2_rows_kernel       each workgroup owns 16 output rows and sums, in a
+//   3. w2_rows_kernel       each workgroup owns 8 output rows and sums, in a
 //                           fixed order, every slot's down projection weighted
 //                           by its routing weight (plus sigmoid(gate) times the
 //                           shared expert), then rounds once to bf16
@@ -30,19 +30,26 @@ __device__ __forceinline__ int clamp_expert(int id, int E)
 }
 
 // ---------------------------------------------------------------------------
-// 1. Router GEMV with the routing tail in its last workgroup.
-//    One router row per wave (8 per workgroup; row E is the shared-expert gate
-//    when present), activations of four tokens in flight at a time.  Each
-//    workgroup stores its 8 logits of a token with one 32-byte coherent store,
-//    waits for its stores and takes a ticket; the workgroup that takes the
-//    last ticket selects every token's experts (one wave per token) and, for
-//    the routing-only entry point, builds the expert permutation.  ("MoE block
-//    (decode-05)": the CTA that finishes last does the top-k, the
+// 1. Router GEMV with the routing tail in one extra workgroup.
+//    Producer workgroups hold one router row per wave (8 per workgroup; row E
+//    is the shared-expert gate when present) and compute it for every token,
+//    NT tokens' activations in flight at a time.  A producer publishes the 8
+//    logits of a token with one 32-byte coherent store, as order-preserving
+//    keys, which are never zero; then it is done (no wait, no counter).
+//    The last workgroup, dispatched after every producer, first converts x to
+//    nibble-pair order with its chunk sums (for the gate/up kernel), then,
+//    one wave per token, reads the token's keys until none is zero, selects
+//    the experts, and sets the keys back to zero for the next call; for the
+//    routing-only entry point it then builds the expert permutation.  ("MoE
+//    block (decode-05)": the router's last CTA does the top-k, the
 //    renormalisation and the block alignment, with no separate kernel.)
-//    The ticket needs no cache write-back: the logits are written and read
-//    with agent-scope coherent accesses.
+//    The keys live in a fixed zeroed region of the workspace that no other
+//    path writes.  The wait for them is bounded, so the kernel always ends;
+//    every producer is resident or done by the time the last workgroup runs,
+//    so the bound is never reached in practice.
 // ---------------------------------------------------------------------------
 constexpr int kRtWaves = 8;
+constexpr uint32_t kKeySpinLimit = 1u << 22;   // reads of a token's keys before giving up
 enum RouteTail { kTailNone = 0, kTailTopk = 1, kTailPermute = 2 };
 
 struct RouterArgs {
@@ -54,16 +61,115 @@ struct RouterArgs {
     int tail;        // RouteTail
 };
 
-template <int CPL>
+// Key of a logit: the order-preserving map, never 0 (0 marks "not yet written").
+__device__ __forceinline__ uint32_t logit_key(float l)
+{
+    const uint32_t k = float_order(l);
+    return k == 0u ? 1u : k;
+}
+
+// One token's routing from its published keys (one wave).
+template <int KPL>
+__device__ TopkLane route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds)
+{
+    uint32_t val[KPL];
+    for (uint32_t spin = 0; spin < kKeySpinLimit; ++spin) {
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const int e = lane + kWave * i;
+            val[i] = e < E ? load_coherent(keys + e) : 0u;
+            missing |= e < E && val[i] == 0u;
+        }
+        if (!__ballot(missing)) break;
+    }
+    const TopkLane r = wave_topk_keys<KPL>(val, k, lane, lds);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E) store_coherent(keys + e, 0u);   // ready for the next call
+    }
+    return r;
+}
+
+__device__ __forceinline__ TopkLane route_token_any(uint32_t *keys, int E, int k, int lane,
+                                                    uint32_t *lds)
+{
+    if (E <= 64) return route_token<1>(keys, E, k, lane, lds);
+    if (E <= 128) return route_token<2>(keys, E, k, lane, lds);
+    if (E <= 256) return route_token<4>(keys, E, k, lane, lds);
+    if (E <= 512) return route_token<8>(keys, E, k, lane, lds);
+    return route_token<16>(keys, E, k, lane, lds);
+}
+
+// x of the T tokens in nibble-pair order (ws.xp) with the sums of its 32-value
+// chunks (ws.xs).  One 16-byte piece per thread and pass, four passes' loads
+// in flight; a chunk is 4 consecutive pieces, i.e. a lane quad.
+__device__ __forceinline__ void transform_x(const uint16_t *x, const Dims &d, const Workspace &ws,
+                                            int tid)
+{
+    const int npieces = d.T * d.H / 8;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x);
+    uint4 *dst = reinterpret_cast<uint4 *>(ws.xp);
+    constexpr int kStep = kRtWaves * kWave;
+    for (int p0 = 0; p0 < npieces; p0 += 4 * kStep) {
+        const int pa = p0 + tid, pb = pa + kStep, pc = pb + kStep, pd = pc + kStep;
+        const uint4 va = src[min(pa, npieces - 1)], vb = src[min(pb, npieces - 1)];
+        const uint4 vc = src[min(pc, npieces - 1)], vd = src[min(pd, npieces - 1)];
+        auto piece = [&](int pi, const uint4 v) {
+            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+            uint32_t pr[4];
+            octet_to_pair_order(in, pr);
+            float sum = 0.f;
+            sum = dot2(in[0], 0x3F803F80u, sum);  // bf16 (1.0, 1.0)
+            sum = dot2(in[1], 0x3F803F80u, sum);
+            sum = dot2(in[2], 0x3F803F80u, sum);
+            sum = dot2(in[3], 0x3F803F80u, sum);
+            sum = quad_sum(sum);                   // the whole 32-value chunk
+            if (pi < npieces) {
+                dst[pi] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+                if ((pi & 3) == 0) ws.xs[pi >> 2] = sum;
+            }
+        };
+        piece(pa, va); piece(pb, vb); piece(pc, vc); piece(pd, vd);
+    }
+}
+
+template <int CPL, int NT>
 __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
 {
     __shared__ float s_lg[kDecodeMaxTokens][kRtWaves];
     __shared__ uint32_t s_topk[kRtWaves][kTopkLds];
     __shared__ int32_t s_ids[kDecodeMaxTokens * kMaxTopK];
     __shared__ int32_t s_run[kMaxExperts];
-    __shared__ uint32_t s_last;
     const Dims &d = r.d;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const bool publish = r.tail != kTailNone;
+
+    if (blockIdx.x == gridDim.x - 1) {
+        // ---- routing workgroup ----
+        transform_x(r.x, d, r.ws, tid);
+        if (!publish) return;
+        for (int t = wave; t < d.T; t += kRtWaves) {
+            const TopkLane tk = route_token_any(r.ws.dec_keys + (size_t)t * d.E, d.E, d.k, lane,
+                                                s_topk[wave]);
+            if (lane < d.k) {
+                const int id = clamp_expert(tk.id, d.E);
+                r.ro.ids[t * d.k + lane] = id;
+                r.ro.weights[t * d.k + lane] = tk.w;
+                s_ids[t * d.k + lane] = id;
+            }
+        }
+        if (r.tail == kTailPermute) {
+            __syncthreads();
+            if (wave == 0)
+                wave_permute(s_ids, d.S, d.E, lane, s_run, r.ro.counts, r.ro.offsets,
+                             r.ro.sorted_slots, r.ws.slot_pos, r.ws.active);
+        }
+        return;
+    }
+
+    // ---- producer workgroup ----
     const int row = blockIdx.x * kRtWaves + wave;
     const bool gate = r.gate_w != nullptr && row == r.nrouted;
     if (row < r.nrouted || gate) {
@@ -77,10 +183,10 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
             const uint4 v = reinterpret_cast<const uint4 *>(wrow)[ok ? idx : 0];
             wr[c] = ok ? v : make_uint4(0, 0, 0, 0);
         }
-        for (int t0 = 0; t0 < d.T; t0 += 4) {
-            uint4 xv[4][CPL];
+        for (int t0 = 0; t0 < d.T; t0 += NT) {
+            uint4 xv[NT][CPL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < NT; ++u) {
                 const int t = min(t0 + u, d.T - 1);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
@@ -89,7 +195,7 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < NT; ++u) {
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
@@ -106,60 +212,13 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
             }
         }
     }
-    // x in nibble-pair order with its 32-value chunk sums, for the gate/up kernel
-    {
-        const int nchunk = d.T * (d.H / 32);
-        for (int ci = blockIdx.x * blockDim.x + tid; ci < nchunk; ci += gridDim.x * blockDim.x) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(r.x) + (size_t)ci * 4;
-            uint4 *dst = reinterpret_cast<uint4 *>(r.ws.xp) + (size_t)ci * 4;
-            float sum = 0.f;
-#pragma unroll
-            for (int o = 0; o < 4; ++o) {
-                const uint4 v = src[o];
-                const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-                uint32_t pr[4];
-                octet_to_pair_order(in, pr);
-                sum = dot2(in[0], 0x3F803F80u, sum);  // bf16 (1.0, 1.0)
-                sum = dot2(in[1], 0x3F803F80u, sum);
-                sum = dot2(in[2], 0x3F803F80u, sum);
-                sum = dot2(in[3], 0x3F803F80u, sum);
-                dst[o] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-            }
-            r.ws.xs[ci] = sum;
-        }
-    }
-    if (r.tail == kTailNone) return;
-
+    if (!publish) return;
     __syncthreads();
-    // the workgroup's logits of token t are 8 consecutive words: one 32-byte store
+    // the workgroup's keys of token t are 8 consecutive words: one 32-byte store
     if (tid < kRtWaves * d.T) {
         const int t = tid / kRtWaves, j = tid % kRtWaves, rr = blockIdx.x * kRtWaves + j;
         if (rr < r.nrouted)
-            store_coherent(reinterpret_cast<uint32_t *>(r.ws.logits) + (size_t)t * d.E + rr,
-                           __float_as_uint(s_lg[t][j]));
-    }
-    wait_memory();
-    __syncthreads();
-    if (tid == 0) s_last = atomic_add_agent(r.ws.route_ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
-    __syncthreads();
-    if (!s_last) return;
-
-    // last workgroup: routing of every token
-    if (tid == 0) *r.ws.route_ticket = 0;   // ready for the next call
-    for (int t = wave; t < d.T; t += kRtWaves) {
-        const TopkLane tk = topk_any<true>(r.ws.logits + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave]);
-        if (lane < d.k) {
-            const int id = clamp_expert(tk.id, d.E);
-            r.ro.ids[t * d.k + lane] = id;
-            r.ro.weights[t * d.k + lane] = tk.w;
-            s_ids[t * d.k + lane] = id;
-        }
-    }
-    if (r.tail == kTailPermute) {
-        __syncthreads();
-        if (wave == 0)
-            wave_permute(s_ids, d.S, d.E, lane, s_run, r.ro.counts, r.ro.offsets, r.ro.sorted_slots,
-                         r.ws.slot_pos, r.ws.active);
+            store_coherent(r.ws.dec_keys + (size_t)t * d.E + rr, logit_key(s_lg[t][j]));
     }
 }
 
@@ -216,13 +275,12 @@ __device__ __forceinline__ void w13_int6_tile(const ExpertArgs &a, const Dims &d
             for (int u = 0; u < 16; ++u) xs = dot2(xv[u], 0x3F803F80u, xs);
             acc = fmaf(sc[qd][c], chunk_dot6<false>(w[qd][c], xv) - 160.f * xs, acc);
         }
-        acc += __shfl_xor(acc, 8, kWave);
-        acc += __shfl_xor(acc, 4, kWave);
-        acc += __shfl_xor(acc, 2, kWave);
-        acc += __shfl_xor(acc, 1, kWave);
-        const float up = __shfl(acc, (lane + 32) & (kWave - 1), kWave);
+        // rows: lanes 0-15 gate i, 16-31 gate i+1, 32-47 up i, 48-63 up i+1
+        acc = row_sum(acc);
+        const float g0 = read_lane(acc, 0), g1 = read_lane(acc, 16);
+        const float u0 = read_lane(acc, 32), u1 = read_lane(acc, 48);
         if (lane == 0 || lane == 16)
-            hrow[i0 + 2 * qd + grp] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
+            hrow[i0 + 2 * qd + grp] = (uint16_t)f32_to_f16_sat(lane == 0 ? silu(g0) * u0 : silu(g1) * u1);
     }
 }
 
@@ -247,8 +305,8 @@ template <int CPL>
 __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Workspace ws,
                                                        const int32_t *__restrict__ ids)
 {
-    __shared__ __align__(16) uint16_t s_x[kMaxHidden];
-    __shared__ float s_xs[kMaxHidden / 32];
+    __shared__ __align__(16) uint16_t s_x[kMaxHidden];   // 256 threads x 2 chunks of 16 bytes
+    __shared__ float s_xs[256];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int s = blockIdx.y;
     const int i0 = blockIdx.x * kTileOut + wave * 4;
@@ -256,20 +314,16 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
     const int t = s / d.k, e = clamp_expert(ids[s], d.E);
     const int grp = lane >> 4, q = lane & 15;
     const int nck = d.H / 32, words = d.H / 8, nsc = d.H / kGroup;
-    // the token's activations first (cache-hot; the LDS store waits only for
-    // them, since loads complete in issue order), then the weights
-    constexpr int kXPer = kMaxHidden / 8 / 256;
-    uint4 xr[kXPer];
-    float xsr = 0.f;
-    {
-        const uint4 *xsrc = reinterpret_cast<const uint4 *>(ws.xp + (size_t)t * d.H);
-#pragma unroll
-        for (int j = 0; j < kXPer; ++j) {
-            const int i = tid + 256 * j;
-            xr[j] = xsrc[i < d.H / 8 ? i : 0];
-        }
-        xsr = ws.xs[(size_t)t * nck + (tid < nck ? tid : 0)];
-    }
+    // the token's activations first, then the weights: loads complete in
+    // issue order, so the LDS store of x then waits for x alone.  Every load
+    // and store here is unconditional (clamped indices; copies past the row end
+    // land in unused LDS), which keeps the compiler from serialising them.
+    static_assert(kMaxHidden / 8 == 2 * 256, "two 16-byte chunks of x per thread");
+    const uint4 *xsrc = reinterpret_cast<const uint4 *>(ws.xp + (size_t)t * d.H);
+    const uint4 xr0 = xsrc[min(tid, d.H / 8 - 1)];
+    const uint4 xr1 = xsrc[min(tid + 256, d.H / 8 - 1)];
+    const float xsr = ws.xs[(size_t)t * nck + min(tid, nck - 1)];
+    __builtin_amdgcn_sched_barrier(0);
     uint4 w[2][CPL];
     float sc[2][CPL];
 #pragma unroll
@@ -286,12 +340,10 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
             sc[qd][c] = ok ? sv : 0.f;
         }
     }
-#pragma unroll
-    for (int j = 0; j < kXPer; ++j) {
-        const int i = tid + 256 * j;
-        if (i < d.H / 8) reinterpret_cast<uint4 *>(s_x)[i] = xr[j];
-    }
-    if (tid < nck) s_xs[tid] = xsr;
+    __builtin_amdgcn_sched_barrier(0);   // every weight load issued before the wait for x
+    reinterpret_cast<uint4 *>(s_x)[tid] = xr0;
+    reinterpret_cast<uint4 *>(s_x)[tid + 256] = xr1;
+    s_xs[tid] = xsr;
     __syncthreads();
     uint16_t *hrow = ws.h + (size_t)s * d.I;
 #pragma unroll
@@ -303,14 +355,14 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
             const uint32_t *xv = reinterpret_cast<const uint32_t *>(s_x + kcl * 32);
             acc = fmaf(sc[qd][c], chunk_dot(w[qd][c], xv) - 136.f * s_xs[kcl], acc);
         }
-        acc += __shfl_xor(acc, 8, kWave);
-        acc += __shfl_xor(acc, 4, kWave);
-        acc += __shfl_xor(acc, 2, kWave);
-        acc += __shfl_xor(acc, 1, kWave);
-        const float up = __shfl(acc, (lane + 32) & (kWave - 1), kWave);
+        // rows: lanes 0-15 gate i, 16-31 gate i+1, 32-47 up i, 48-63 up i+1
+        acc = row_sum(acc);
+        const float g0 = read_lane(acc, 0), g1 = read_lane(acc, 16);
+        const float u0 = read_lane(acc, 32), u1 = read_lane(acc, 48);
         if (lane == 0 || lane == 16) {
             const int i = i0 + 2 * qd + grp;
-            hrow[(i & ~7) | pair_pos(i & 7)] = (uint16_t)f32_to_f16_sat(silu(acc) * up);
+            hrow[(i & ~7) | pair_pos(i & 7)] =
+                (uint16_t)f32_to_f16_sat(lane == 0 ? silu(g0) * u0 : silu(g1) * u1);
         }
     }
 }
@@ -322,15 +374,14 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
 //    workgroup has 16 groups; group g takes the slots g, g + 16, ...  Each
 //    group keeps its own partial sum per (token, row), and the partials are
 //    added in group order at the end (a fixed order: deterministic).  The
-//    weights of a batch of slots are requested before the activations are
-//    staged in LDS, so the two latencies overlap.  h arrives in nibble-pair
+//    activations and the first slot's weights are in flight together, and a
+//    group's next expert id is in flight with its current weights.  h arrives in nibble-pair
 //    order; each 32-value chunk's sum (for the +8 code bias) is formed once
 //    while staging, not once per output row.
 // ---------------------------------------------------------------------------
 constexpr int kDnWaves = 8;
 constexpr int kDnRows = 8;
 constexpr int kDnGroups = kDnWaves * 2;    // 32-lane slot groups per workgroup
-constexpr int kDnBatch = 1;               // slots per group with weights in flight
 constexpr int kDnHBytes = 64 * 1024;      // LDS for staged activations (holds k * I fp16 for k <= 32, I <= 1024)
 constexpr int kDnMaxGroup = 16;           // tokens per LDS group
 
@@ -356,73 +407,89 @@ __global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) 
         const int s0 = t0 * d.k, ns = nt * d.k;
         for (int i = tid; i < kDnGroups * kDnMaxGroup * kDnRows; i += kDnWaves * kWave)
             (&s_part[0][0][0])[i] = 0.f;
-        bool staged = false;
-        for (int b0 = grp; b0 < ns || !staged; b0 += kDnGroups * kDnBatch) {
-            // this group's next batch of slots: weights first
-            uint4 w[kDnBatch][CPL];
-            float sc[kDnBatch][CPL];
-            int sl[kDnBatch];
-            float rw[kDnBatch];
+        int sr = grp;
+        int sg = s0 + min(sr, ns - 1);
+        int e = clamp_expert(ids[sg], d.E);
+        float rw = wts[sg];
+        const uint4 *src = reinterpret_cast<const uint4 *>(ws.h + (size_t)s0 * d.I);
+        const int n16 = ns * d.I / 8;
+        auto load_weights = [&](int ex, uint4 (&w)[CPL], float (&sc)[CPL]) {
+            const size_t r = (size_t)ex * d.H + row;
+            const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w2p + r * words);
 #pragma unroll
-            for (int u = 0; u < kDnBatch; ++u) {
-                const int sr = b0 + u * kDnGroups;  // slot relative to the token group
-                sl[u] = sr;
-                const int sg = s0 + (sr < ns ? sr : 0);
-                const int e = clamp_expert(ids[sg], d.E);
-                rw[u] = sr < ns ? wts[sg] : 0.f;
-                const size_t r = (size_t)e * d.H + row;
-                const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w2p + r * words);
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int kc = q + 4 * c, ok = kc < nck, kcl = ok ? kc : 0;
-                    w[u][c] = load_stream(wrow + kcl);
-                    const float s = bf16_to_f32(a.w2s[r * nsc + kcl / 4]);
-                    sc[u][c] = ok ? s : 0.f;
-                }
+            for (int c = 0; c < CPL; ++c) {
+                const int kc = q + 4 * c, ok = kc < nck, kcl = ok ? kc : 0;
+                w[c] = load_stream(wrow + kcl);
+                const float sv = bf16_to_f32(a.w2s[r * nsc + kcl / 4]);
+                sc[c] = ok ? sv : 0.f;
             }
-            if (!staged) {
-                // the group's activations (ns x I fp16, nibble-pair order) into LDS, once
-                const uint4 *src = reinterpret_cast<const uint4 *>(ws.h + (size_t)s0 * d.I);
-                uint4 *dst = reinterpret_cast<uint4 *>(s_h);
-                const int n16 = ns * d.I / 8;
-                for (int i = tid; i < n16; i += kDnWaves * kWave) dst[i] = src[i];
-                __syncthreads();
-                for (int i = tid; i < ns * nck; i += kDnWaves * kWave) {
-                    const uint4 *cp = reinterpret_cast<const uint4 *>(s_h + (size_t)i * 32);
-                    float hs = 0.f;
+        };
+        auto accumulate = [&](int slot, float wt, const uint4 (&w)[CPL], const float (&sc)[CPL]) {
+            float acc = 0.f;
 #pragma unroll
-                    for (int o = 0; o < 4; ++o) {
-                        const uint4 v = cp[o];
-                        hs = dot2h(v.x, 0x3C003C00u, hs); hs = dot2h(v.y, 0x3C003C00u, hs);
-                        hs = dot2h(v.z, 0x3C003C00u, hs); hs = dot2h(v.w, 0x3C003C00u, hs);
-                    }
-                    s_hs[i] = hs;
+            for (int c = 0; c < CPL; ++c) {
+                const int kc = q + 4 * c, kcl = kc < nck ? kc : 0;
+                const uint4 *hp = reinterpret_cast<const uint4 *>(s_h + (size_t)slot * d.I + kcl * 32);
+                uint32_t hv[16];
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    const uint4 v = hp[o];
+                    hv[4 * o] = v.x; hv[4 * o + 1] = v.y; hv[4 * o + 2] = v.z; hv[4 * o + 3] = v.w;
                 }
-                __syncthreads();
-                staged = true;
+                const float hs = s_hs[slot * nck + kcl];
+                acc = fmaf(sc[c], chunk_dot_h(w[c], hv) - 136.f * hs, acc);
             }
+            acc = quad_sum(acc);
+            if (q == 0) s_part[grp][slot / d.k][rl] += wt * acc;
+        };
+        // first slot, with the staging of the activations
+        uint4 w[CPL];
+        float sc[CPL];
+        load_weights(e, w, sc);
+        // the group's next slot's routing, in flight with these weights
+        int sn = sr + kDnGroups;
+        int sgn = s0 + min(sn, ns - 1);
+        int en = clamp_expert(ids[sgn], d.E);
+        float rwn = wts[sgn];
+        // the activations straight to LDS (no registers held), issued after
+        // every load whose result is needed before the barrier: a wait on a
+        // load issued before these copies would also wait for the copies.
+        // Wave w copies the 16-byte chunks [64 w + 512 j, + 64) below n16; lanes
+        // past n16 re-read the last chunk into unused LDS (n16 <= 4096 chunks).
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            uint4 *dst = reinterpret_cast<uint4 *>(s_h);
+            for (int base = wave * kWave; base < n16; base += kDnWaves * kWave)
+                __builtin_amdgcn_global_load_lds(src + min(base + lane, n16 - 1), dst + base, 16, 0, 0);
+        }
+        {
+            // the token group's activations (ns x I fp16, nibble-pair order) are
+            // in LDS once this wave's copies have landed; then the chunk sums
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies
+            __syncthreads();
+            for (int i = tid; i < ns * nck; i += kDnWaves * kWave) {
+                const uint4 *cp = reinterpret_cast<const uint4 *>(s_h + (size_t)i * 32);
+                float hs = 0.f;
 #pragma unroll
-            for (int u = 0; u < kDnBatch; ++u) {
-                if (sl[u] >= ns) break;
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int kc = q + 4 * c, kcl = kc < nck ? kc : 0;
-                    const uint4 *hp = reinterpret_cast<const uint4 *>(s_h + (size_t)sl[u] * d.I + kcl * 32);
-                    uint32_t hv[16];
-#pragma unroll
-                    for (int o = 0; o < 4; ++o) {
-                        const uint4 v = hp[o];
-                        hv[4 * o] = v.x; hv[4 * o + 1] = v.y; hv[4 * o + 2] = v.z; hv[4 * o + 3] = v.w;
-                    }
-                    const float hs = s_hs[sl[u] * nck + kcl];
-                    acc = fmaf(sc[u][c], chunk_dot_h(w[u][c], hv) - 136.f * hs, acc);
+                for (int o = 0; o < 4; ++o) {
+                    const uint4 v = cp[o];
+                    hs = dot2h(v.x, 0x3C003C00u, hs); hs = dot2h(v.y, 0x3C003C00u, hs);
+                    hs = dot2h(v.z, 0x3C003C00u, hs); hs = dot2h(v.w, 0x3C003C00u, hs);
                 }
-                acc += __shfl_xor(acc, 2, kWave);
-                acc += __shfl_xor(acc, 1, kWave);
-                if (q == 0) s_part[grp][sl[u] / d.k][rl] += rw[u] * acc;
+                s_hs[i] = hs;
             }
-            if (b0 >= ns) break;   // a group with no slots only helped to stage
+            __syncthreads();
+        }
+        if (sr < ns) accumulate(sr, rw, w, sc);
+        // the group's remaining slots
+        while (sn < ns) {
+            sr = sn; e = en; rw = rwn;
+            load_weights(e, w, sc);
+            sn = sr + kDnGroups;
+            sgn = s0 + min(sn, ns - 1);
+            en = clamp_expert(ids[sgn], d.E);
+            rwn = wts[sgn];
+            accumulate(sr, rw, w, sc);
         }
         // shared expert: one extra slot per token, INT6 rows of the same outputs
         if (d.sh_I > 0) {
@@ -440,8 +507,7 @@ __global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) 
                     const float hs = load_act_natural<true>(ws.sh_h + (size_t)t * d.sh_I + kcl * 32, hv);
                     acc = fmaf(ok ? s : 0.f, chunk_dot6<true>(wv, hv) - 160.f * hs, acc);
                 }
-                acc += __shfl_xor(acc, 2, kWave);
-                acc += __shfl_xor(acc, 1, kWave);
+                acc = quad_sum(acc);
                 const float g = 1.f / (1.f + expf(-ws.shared_gate[t]));
                 if (q == 0) s_part[grp][tl][rl] += g * acc;
             }
@@ -465,11 +531,14 @@ static int cpl_of(int chunks, int lanes) { return (chunks + lanes - 1) / lanes; 
 static hipError_t launch_router(const RouterArgs &r, hipStream_t st)
 {
     const int rows = r.nrouted + (r.gate_w ? 1 : 0);
-    const int nchunk = r.d.T * (r.d.H / 32);
-    const int grid = max((rows + kRtWaves - 1) / kRtWaves, (nchunk + kRtWaves * kWave - 1) / (kRtWaves * kWave));
+    const int grid = (rows + kRtWaves - 1) / kRtWaves + 1;   // producers + the routing workgroup
+    const bool one = r.d.T == 1;
     switch (cpl_of(r.d.H / 8, kWave)) {
 #define MOE_CASE(N) \
-    case N: router_kernel<N><<<grid, kRtWaves * kWave, 0, st>>>(r); break;
+    case N:                                                                                   \
+        if (one) router_kernel<N, 1><<<grid, kRtWaves * kWave, 0, st>>>(r);                  \
+        else router_kernel<N, 4><<<grid, kRtWaves * kWave, 0, st>>>(r);                      \
+        break;
         MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8)
 #undef MOE_CASE
     default: return hipErrorInvalidValue;

@@ -199,10 +199,51 @@ def test_decode_repeated_calls_share_workspace(T):
         got = L.forward(dev["x"] if i % 2 == 0 else x2)
         torch.cuda.synchronize()
         assert torch.equal(got, first[i % 2]), f"call {i}"
-    assert not L.workspace(T)[:512].any(), "workspace counters were not returned to zero"
+    assert not L.workspace(T)[:65536].any(), "the hand-off area was not returned to zero"
     fresh = MoeInt4Layer(dev, shape.top_k).forward(dev["x"])   # a new zeroed workspace
     torch.cuda.synchronize()
     assert torch.equal(fresh, first[0])
+
+
+def test_one_workspace_across_shapes():
+    """One workspace buffer serves calls of different token counts (decode and
+    many-token paths, forward and routing-only) in any order: each result
+    equals the result on a fresh workspace, and the first 64 KiB are zero
+    after every call."""
+    base = dict(hidden=512, experts=64, top_k=4, inter=256)
+    host = synth.make_layer(synth.LayerShape(tokens=40, **base), seed=23)
+    dev = synth.to_device(host)
+    L = MoeInt4Layer(dev, base["top_k"])
+    xs = {T: synth.to_device(synth.make_layer(synth.LayerShape(tokens=T, **base), seed=23,
+                                              x_seed=100 + T))["x"] for T in (1, 4, 16, 40)}
+    nbytes = max(B.workspace_bytes(L.shape(T)) for T in xs)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    w = dev
+    for T, what in [(4, "forward"), (40, "forward"), (1, "forward"), (16, "route"), (4, "forward"),
+                    (16, "forward"), (1, "route")]:
+        say(f"T={T} {what}")
+        ref = MoeInt4Layer(dev, base["top_k"])   # fresh workspaces
+        if what == "forward":
+            want = ref.forward(xs[T])
+            got = torch.empty_like(want)
+            B.moe_int4_forward(xs[T], w["router_w"], w["w13_packed"], w["w13_scales"], w["w2_packed"],
+                               w["w2_scales"], base["top_k"], got, L.shape(T), None, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got, want), f"T={T} forward"
+        else:
+            want = ref.route(xs[T])
+            k = base["top_k"]
+            got = {"ids": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+                   "weights": torch.empty(T, k, dtype=torch.float32, device="cuda"),
+                   "counts": torch.empty(64, dtype=torch.int32, device="cuda"),
+                   "offsets": torch.empty(65, dtype=torch.int32, device="cuda"),
+                   "sorted_slots": torch.empty(T * k, dtype=torch.int32, device="cuda")}
+            B.moe_int4_route(xs[T], w["router_w"], L.shape(T), got["ids"], got["weights"], got["counts"],
+                             got["offsets"], got["sorted_slots"], ws)
+            torch.cuda.synchronize()
+            for key in got:
+                assert torch.equal(got[key], want[key]), f"T={T} route {key}"
+        assert not ws[:65536].any(), f"T={T} {what}: the hand-off area was not returned to zero"
 
 
 def test_tiny_shared_expert():
