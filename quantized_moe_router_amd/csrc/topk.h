@@ -9,15 +9,18 @@
 //
 // The selection is latency-bound (one wave, E = 512 logits, k = 10), so it
 // avoids k dependent wave-wide reductions:
-//   1. P = the k-th largest of the 64 per-lane maxima (a 32-step binary search
-//      on one value per lane, counting with ballots).  At least k logits are
-//      >= P, so every selected logit is >= P.
-//   2. The candidates (logits >= P; about k to 2k of them for continuous
-//      logits) are compacted into LDS, and each is ranked against all others
-//      by (value descending, id ascending).  Rank < k is selected, at that
-//      position.
+//   1. P = the k-th largest of the 64 per-lane maxima with its low 16 bits
+//      cleared (a 16-step binary search on one value per lane, counting with
+//      ballots).  At least k logits are >= P, so every selected logit is >= P,
+//      and for continuous logits only a few more than k are.
+//   2. The candidates (logits >= P) are compacted into LDS as 64-bit
+//      composites (key << 32 | ~id), which order as the selection does:
+//      larger key first, then lower id.  Each candidate's rank is the number
+//      of composites above its own, from broadcast LDS reads of all of them;
+//      rank < k is selected, at that position.
 //   3. If more than 64 logits are >= P (heavy ties), an exact fallback finds
-//      the k-th value itself by a binary search over all logits.
+//      the k-th value itself by a binary search over all logits and keeps
+//      exactly k candidates.
 #pragma once
 
 #include "common.h"
@@ -74,8 +77,9 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&val)[KPL], int k)
 }
 
 // Writes the keys with val >= thr (val > thr, plus the lowest-id `eq_take`
-// keys equal to thr if eq_take >= 0) as (key, id) pairs to lds[0..2n), in
-// ascending id order; returns n.
+// keys equal to thr if eq_take >= 0) to LDS as composites (~id, key) =
+// 64-bit (key << 32 | ~id), at positions 0..n-1 in ascending id order;
+// returns n.  The caller guarantees n <= 64.
 template <int KPL>
 __device__ __forceinline__ int compact_keys(const uint32_t (&val)[KPL], uint32_t thr, int eq_take,
                                             int lane, uint32_t *lds)
@@ -95,13 +99,14 @@ __device__ __forceinline__ int compact_keys(const uint32_t (&val)[KPL], uint32_t
         const uint64_t selm = __ballot(sel);
         if (sel) {
             const int pos = n + popc(selm & lt);
-            lds[2 * pos] = val[i];
-            lds[2 * pos + 1] = (uint32_t)(lane + kWave * i);
+            reinterpret_cast<uint2 *>(lds)[pos] = make_uint2(~(uint32_t)(lane + kWave * i), val[i]);
         }
         n += popc(selm);
     }
     return n;
 }
+
+__device__ __forceinline__ uint64_t as_u64(uint2 v) { return ((uint64_t)v.y << 32) | v.x; }
 
 // Top-k of one token from its order-preserving keys val[i] = key of expert
 // lane + 64 i (0 where the expert does not exist).  Requires 1 <= k <= 32 and
@@ -113,13 +118,20 @@ __device__ TopkLane wave_topk_keys(const uint32_t (&val)[KPL], int k_in, int lan
     uint32_t m = val[0];
 #pragma unroll
     for (int i = 1; i < KPL; ++i) m = max(m, val[i]);
-    uint32_t lm[1] = {m};
-    const uint32_t P = kth_key<1>(lm, k);
+    // 1. P: largest V with 16 low zero bits and #{lane maxima >= V} >= k
+    uint32_t P = 0;
+#pragma unroll
+    for (int b = 31; b >= 16; --b) {
+        const uint32_t cand = P | (1u << b);
+        P = popc(__ballot(m >= cand)) >= k ? cand : P;
+    }
     int n = 0;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) n += popc(__ballot(val[i] >= P));
+    for (int i = 0; i < KPL; ++i) n += popc(__ballot(val[i] >= P && val[i] != 0u));
 
-    uint32_t my_v = 0, my_e = 0xFFFFFFFFu;
+    // 2. candidates as composites; slots 0..15 start as zero (never above a candidate)
+    uint2 *slot = reinterpret_cast<uint2 *>(lds);
+    if (lane < 16) slot[lane] = make_uint2(0u, 0u);
     int ncand;
     if (n <= kWave) {
         ncand = compact_keys<KPL>(val, P, -1, lane, lds);
@@ -132,30 +144,33 @@ __device__ TopkLane wave_topk_keys(const uint32_t (&val)[KPL], int k_in, int lan
         ncand = compact_keys<KPL>(val, V, k - gt, lane, lds);
     }
     __builtin_amdgcn_wave_barrier();
-    if (lane < ncand) {
-        my_v = lds[2 * lane];
-        my_e = lds[2 * lane + 1];
-    }
-    // rank among the candidates: larger key first, then lower id
+    const uint64_t mine = as_u64(slot[lane]);   // meaningful on lanes < ncand
     int rank = 0;
-    for (int j = 0; j < ncand; ++j) {
-        const uint32_t vj = (uint32_t)__builtin_amdgcn_readlane((int)my_v, j);
-        const uint32_t ej = (uint32_t)__builtin_amdgcn_readlane((int)my_e, j);
-        rank += (vj > my_v || (vj == my_v && ej < my_e)) ? 1 : 0;
+    if (ncand <= 16) {
+        // all 16 slots, read unconditionally (a branch per slot would serialise the reads)
+        uint4 c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = reinterpret_cast<const uint4 *>(lds)[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            rank += as_u64(make_uint2(c[j].x, c[j].y)) > mine ? 1 : 0;
+            rank += as_u64(make_uint2(c[j].z, c[j].w)) > mine ? 1 : 0;
+        }
+    } else {
+        for (int j = 0; j < ncand; ++j) rank += as_u64(slot[j]) > mine ? 1 : 0;
     }
     __builtin_amdgcn_wave_barrier();
-    if (lane < ncand && rank < k) {
-        lds[128 + 2 * rank] = my_v;
-        lds[128 + 2 * rank + 1] = my_e;
-    }
+    if (lane < ncand && rank < k) slot[64 + rank] = make_uint2((uint32_t)mine, (uint32_t)(mine >> 32));
     __builtin_amdgcn_wave_barrier();
+    // 3. softmax over the k selected logits (the full denominator cancels)
     TopkLane out{0, 0.f};
     float l = 0.f;
     if (lane < k) {
-        l = order_float(lds[128 + 2 * lane]);
-        out.id = (int)lds[128 + 2 * lane + 1];
+        const uint2 c = slot[64 + lane];
+        l = order_float(c.y);
+        out.id = (int)~c.x;
     }
-    const float first = order_float(lds[128]);
+    const float first = order_float(slot[64].y);
     const float ex = lane < k ? expf(l - first) : 0.f;
     out.w = ex / wave_sum(ex);
     __builtin_amdgcn_wave_barrier();
