@@ -62,7 +62,7 @@ Layout layout(const Dims &d)
     L.slot_pos = take(4 * S);
     L.active = take(4 * ((size_t)d.E + 1));
     L.chunk_hist = take(4 * nchunks * d.E);
-    L.tiles = take(4 * ((S + 127) / 128 + (size_t)d.E));
+    L.tiles = take(4 * routed_tile_slots(d));
     L.n_tiles = take(4);
     L.h = take(2 * S * d.I);
     L.y = take(2 * T * ((size_t)d.k + 1) * d.H);

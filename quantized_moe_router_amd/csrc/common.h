@@ -318,6 +318,16 @@ struct Dims {
 
 constexpr int kPermChunk = 1024;  // slots per chunk of the large permutation
 
+// Slots of the grouped-GEMM tile list: 128-row tiles in pairs, pairs dealt
+// round-robin to the 8 XCDs, 16 slots per round.  At most S / 128 + 2 E tile
+// positions are used (each expert's tiles rounded up to a pair), which this
+// bound covers.
+inline size_t routed_tile_slots(const Dims &d)
+{
+    const size_t pairs = ((size_t)d.S + 127) / 128 / 2 + (size_t)d.E + 1;
+    return 16 * ((pairs + 7) / 8);
+}
+
 Workspace carve_workspace(void *base, const Dims &d);
 size_t workspace_size(const Dims &d);
 

@@ -311,7 +311,12 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
     const int s = blockIdx.y;
     const int i0 = blockIdx.x * kTileOut + wave * 4;
     if (blockIdx.x * kTileOut >= d.I) return;
-    const int t = s / d.k, e = clamp_expert(ids[s], d.E);
+    // the expert id as a vector load, used only after the activation loads are
+    // issued: a scalar load would make the wait for the kernel arguments
+    // (scalar loads complete out of order) wait for it too, and hold the
+    // activation loads back by a memory round trip
+    const int t = s / d.k;
+    const uint32_t e_raw = load_coherent(reinterpret_cast<const uint32_t *>(ids) + s);
     const int grp = lane >> 4, q = lane & 15;
     const int nck = d.H / 32, words = d.H / 8, nsc = d.H / kGroup;
     // the token's activations first, then the weights: loads complete in
@@ -324,6 +329,7 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
     const uint4 xr1 = xsrc[min(tid + 256, d.H / 8 - 1)];
     const float xsr = ws.xs[(size_t)t * nck + min(tid, nck - 1)];
     __builtin_amdgcn_sched_barrier(0);
+    const int e = clamp_expert(__builtin_amdgcn_readfirstlane((int)e_raw), d.E);
     uint4 w[2][CPL];
     float sc[2][CPL];
 #pragma unroll

@@ -32,7 +32,8 @@
 //     fp32-atomic alternative measured about 2x slower on this layer);
 //   * workgroup -> tile order is XCD-aware: the weight-row blocks of one token
 //     tile go to the same XCD back to back, so the gathered activations are
-//     re-read from that XCD's L2.
+//     re-read from that XCD's L2, and an expert's token tiles run in pairs on
+//     one XCD, so its weights are read from HBM once per pair.
 #include <type_traits>
 
 #include "int6.h"
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     if constexpr (kRouted) {
         if (tile >= *g.n_tiles) return;
         const int tv = g.tiles[tile];
+        if (tv < 0) return;   // empty slot of a pair
         e = tv & 0xFFFF;
         const int mb = tv >> 16;
         pbase = g.offsets[e] + mb * kMT;
@@ -499,28 +501,64 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint1
         }
 }
 
-// Tile list of the grouped GEMMs: expert e contributes ceil(count_e / 128)
-// tiles (e | mblock << 16), experts in id order.  One workgroup of 1024.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts, int E,
-                                                           int32_t *__restrict__ tiles,
-                                                           int32_t *__restrict__ n_tiles)
+// Tile list of the grouped GEMMs.  Expert e has ceil(count_e / 128) row
+// tiles (e | mblock << 16).  The list is a sequence of pairs of tiles: first
+// the experts with two or more tiles, each rounded up to whole pairs (an odd
+// count leaves one empty slot, -1), then the one-tile experts, two to a pair.
+// Pair q goes to XCD q % 8 as list slots (2 (q / 8) + j) * 8 + q % 8, j = 0, 1.
+// The GEMM gives list slot t to workgroups on XCD t % 8, in order, so the row
+// tiles of a pair run on one XCD at about the same time and share that
+// expert's weights through its L2; a large expert still spreads over the
+// XCDs two tiles at a time.  One workgroup of 1024.
+__device__ __forceinline__ int tile_slot(int pos)   // list slot of tile position pos
 {
-    __shared__ int s_sum[16];
-    const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
-    const int nt = e < E ? (counts[e] + kMT - 1) / kMT : 0;
-    int incl = nt;
+    const int q = pos >> 1;
+    return (2 * (q >> 3) + (pos & 1)) * 8 + (q & 7);
+}
+
+__device__ __forceinline__ int block_excl_sum(int v, int *s_sum, int &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int o = __shfl_up(incl, off, 64);
         if (lane >= off) incl += o;
     }
+    __syncthreads();
     if (lane == 63) s_sum[wave] = incl;
     __syncthreads();
     int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_sum[w];
-    const int start = base + incl - nt;
-    for (int i = 0; i < nt; ++i) tiles[start + i] = e | (i << 16);
-    if (e == 1023) *n_tiles = start + nt;
+    total = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+        base += w < wave ? s_sum[w] : 0;
+        total += s_sum[w];
+    }
+    return base + incl - v;
+}
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts, int E,
+                                                           int32_t *__restrict__ tiles,
+                                                           int32_t *__restrict__ n_tiles)
+{
+    __shared__ int s_sum[16];
+    const int e = threadIdx.x;
+    const int nt = e < E ? (counts[e] + kMT - 1) / kMT : 0;
+    const int multi = nt >= 2 ? (nt + 1) & ~1 : 0;   // positions of a multi-tile expert
+    int nmulti, nsingle;
+    const int pm = block_excl_sum(multi, s_sum, nmulti);
+    const int ps = block_excl_sum(nt == 1 ? 1 : 0, s_sum, nsingle);
+    if (nt >= 2) {
+        for (int i = 0; i < multi; ++i) tiles[tile_slot(pm + i)] = i < nt ? (e | (i << 16)) : -1;
+    } else if (nt == 1) {
+        tiles[tile_slot(nmulti + ps)] = e;
+    }
+    if (e == 1023) {
+        const int used = nmulti + nsingle;
+        const int rounds = (used + 15) / 16;           // 8 pairs of 2 positions per round
+        for (int pos = used; pos < 16 * rounds; ++pos) tiles[tile_slot(pos)] = -1;
+        *n_tiles = 16 * rounds;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -537,7 +575,6 @@ hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const
     return hipGetLastError();
 }
 
-static int max_routed_tiles(const Dims &d) { return (d.S + kMT - 1) / kMT + d.E; }
 
 template <int MODE>
 static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st)
@@ -557,7 +594,7 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint16_t *y = ws.y;
     // routed gate/up -> h (sorted slot order)
-    const int tmax = max_routed_tiles(d);
+    const int tmax = (int)routed_tile_slots(d);
     GemmArgs g{};
     g.x = ws.xh; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
     g.offsets = ro.offsets; g.counts = ro.counts; g.sorted_slots = ro.sorted_slots;
