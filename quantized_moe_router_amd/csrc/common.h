@@ -60,9 +60,21 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 // same way gives sum (128 + n) x; the stored nibble is code + 8, so the true
 // sum of code * x is that minus 136 * sum x.
 // ---------------------------------------------------------------------------
+// A constant in a vector register, opaque to constant folding.  gfx9 VOP3
+// instructions (v_and_or_b32 and its like) take no literal and read at most
+// one scalar register, so (x & mask) | pattern with both constants as
+// literals is emitted as two instructions; with both in vector registers it
+// is one v_and_or_b32.
+__device__ __forceinline__ uint32_t vconst(uint32_t c)
+{
+    uint32_t v;
+    asm("; vconst" : "=v"(v) : "0"(c));
+    return v;
+}
+
 __device__ __forceinline__ void nib_pairs(uint32_t w, uint32_t p[4])
 {
-    const uint32_t m = 0x000F000Fu, b = 0x43004300u;
+    const uint32_t m = vconst(0x000F000Fu), b = vconst(0x43004300u);
     p[0] = (w & m) | b;
     p[1] = ((w >> 4) & m) | b;
     p[2] = ((w >> 8) & m) | b;
@@ -156,7 +168,7 @@ __device__ __forceinline__ uint32_t f32_to_f16_sat(float f)
 // (128+n3,128+n7).
 __device__ __forceinline__ void nib_pairs_h(uint32_t w, uint32_t p[4])
 {
-    const uint32_t m = 0x00780078u, b = 0x58005800u;
+    const uint32_t m = vconst(0x00780078u), b = vconst(0x58005800u);
     p[0] = ((w << 3) & m) | b;
     p[1] = ((w >> 1) & m) | b;
     p[2] = ((w >> 5) & m) | b;

@@ -81,10 +81,11 @@ struct GemmArgs {
 __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, h2_t s2)
 {
     const h2_t bias = {(_Float16)-136.f, (_Float16)-136.f};
+    const uint32_t m = vconst(0x00780078u), b = vconst(0x58005800u);
     f16x8_t out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t p = (((w >> (4 * j)) << 3) & 0x00780078u) | 0x58005800u;  // 128 + n
+        const uint32_t p = (((w >> (4 * j)) << 3) & m) | b;  // 128 + n
         h2_t v = __builtin_bit_cast(h2_t, p);
         v = (v + bias) * s2;  // (n - 8) * s, exact
         out[2 * j] = v[0];
