@@ -352,17 +352,34 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
     s_xs[tid] = xsr;
     __syncthreads();
     uint16_t *hrow = ws.h + (size_t)s * d.I;
+    // chunk-outer: each x chunk is read from LDS once for both row sets
+    struct XChunk {
+        uint32_t v[16];
+        float sum;
+    };
+    auto read_x = [&](int c, XChunk &xc) {
+        const int kc = q + 16 * c, kcl = kc < nck ? kc : 0;
+        const uint4 *xp4 = reinterpret_cast<const uint4 *>(s_x + kcl * 32);
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            const uint4 v = xp4[o];
+            xc.v[4 * o] = v.x; xc.v[4 * o + 1] = v.y; xc.v[4 * o + 2] = v.z; xc.v[4 * o + 3] = v.w;
+        }
+        xc.sum = s_xs[kcl];
+    };
+    float accs[2] = {0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        XChunk xc;
+        read_x(c, xc);
+#pragma unroll
+        for (int qd = 0; qd < 2; ++qd)
+            accs[qd] = fmaf(sc[qd][c], chunk_dot(w[qd][c], xc.v) - 136.f * xc.sum, accs[qd]);
+    }
 #pragma unroll
     for (int qd = 0; qd < 2; ++qd) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int kc = q + 16 * c, kcl = kc < nck ? kc : 0;
-            const uint32_t *xv = reinterpret_cast<const uint32_t *>(s_x + kcl * 32);
-            acc = fmaf(sc[qd][c], chunk_dot(w[qd][c], xv) - 136.f * s_xs[kcl], acc);
-        }
         // rows: lanes 0-15 gate i, 16-31 gate i+1, 32-47 up i, 48-63 up i+1
-        acc = row_sum(acc);
+        const float acc = row_sum(accs[qd]);
         const float g0 = read_lane(acc, 0), g1 = read_lane(acc, 16);
         const float u0 = read_lane(acc, 32), u1 = read_lane(acc, 48);
         if (lane == 0 || lane == 16) {
