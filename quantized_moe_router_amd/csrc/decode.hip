@@ -515,7 +515,8 @@ __global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) 
             accumulate(sr, rw, w, sc);
         }
         // shared expert: one extra slot per token, INT6 rows of the same outputs
-        if (d.sh_I > 0) {
+        // (SHCPL = 0: compiled without, for layers that have none)
+        if (SHCPL > 0 && d.sh_I > 0) {
             const int snck = d.sh_I / 32, swords = d.sh_I / 32 * 6, snsc = d.sh_I / kShGroup;
             for (int tl = grp; tl < nt; tl += kDnGroups) {
                 const int t = t0 + tl;
@@ -605,10 +606,10 @@ static hipError_t launch_w2_rows(const ExpertArgs &a, const Dims &d, const Works
 {
     const int grid = d.H / kDnRows;
     const int cpl = cpl_of(d.I / 32, 4);
-    const int shcpl = d.sh_I ? cpl_of(d.sh_I / 32, 4) : 1;
+    const int shcpl = d.sh_I ? cpl_of(d.sh_I / 32, 4) : 0;
 #define MOE_CASE(N, M) \
     if (cpl == N && shcpl == M) { w2_rows_kernel<N, M><<<grid, kDnWaves * kWave, 0, st>>>(a, d, ws, ids, wts); return hipGetLastError(); }
-#define MOE_ROW(N) MOE_CASE(N, 1) MOE_CASE(N, 2) MOE_CASE(N, 3) MOE_CASE(N, 4) MOE_CASE(N, 5) MOE_CASE(N, 6) MOE_CASE(N, 7) MOE_CASE(N, 8)
+#define MOE_ROW(N) MOE_CASE(N, 0) MOE_CASE(N, 1) MOE_CASE(N, 2) MOE_CASE(N, 3) MOE_CASE(N, 4) MOE_CASE(N, 5) MOE_CASE(N, 6) MOE_CASE(N, 7) MOE_CASE(N, 8)
     MOE_ROW(1) MOE_ROW(2) MOE_ROW(3) MOE_ROW(4) MOE_ROW(5) MOE_ROW(6) MOE_ROW(7) MOE_ROW(8)
 #undef MOE_ROW
 #undef MOE_CASE
