@@ -264,7 +264,7 @@ def main():
     layer_us = ms_per_step * 1e3
 
     decode = T <= 16
-    kernels = {"route": "router_kernel (router GEMV; top-k in its last workgroup)",
+    kernels = {"route": "router_kernel (router GEMV; top-k in one extra routing workgroup)",
                "gate_up": "w13_slot_kernel (INT4 gate/up dequant GEMV + SiLU-gate)",
                "down_combine": "w2_rows_kernel (INT4 down dequant GEMV + weighted combine)"}
     if decode:
