@@ -330,6 +330,24 @@ struct Dims {
 
 constexpr int kPermChunk = 1024;  // slots per chunk of the large permutation
 
+// Split of the many-token router GEMM's reduction over H: the smallest divisor
+// of its 64-wide stage count that gives at least 512 workgroups of 128 tokens
+// x 128 experts, keeping at least two stages per split and at most 8 splits.
+// Each split writes its own fp32 partial logits ([split][T][E]); the top-k
+// adds them in split order.
+inline int router_ksplit(const Dims &d)
+{
+    const int nsteps = d.H / 64;
+    const long tiles = (long)((d.T + 127) / 128) * ((d.E + 127) / 128);
+    int best = 1;
+    for (int ks = 1; 2 * ks <= nsteps && ks <= 8; ++ks) {
+        if (nsteps % ks) continue;
+        best = ks;
+        if (tiles * ks >= 512) break;
+    }
+    return best;
+}
+
 // Slots of the grouped-GEMM tile list: 128-row tiles in pairs, pairs dealt
 // round-robin to the 8 XCDs, 16 slots per round.  At most S / 128 + 2 E tile
 // positions are used (each expert's tiles rounded up to a pair), which this

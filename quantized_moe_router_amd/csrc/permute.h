@@ -42,33 +42,57 @@ __device__ __forceinline__ int id_bits(int E)
     return b;
 }
 
+// The ids of slots [beg, end), end - beg <= kPermChunk, loaded all at once
+// (lane l holds slots beg + l + 64 j; clamped addresses, no branch around a
+// load, so no iteration waits on its own load).
+constexpr int kPermPer = kPermChunk / kWave;
+
+__device__ __forceinline__ void load_chunk_ids(const int32_t *ids, int beg, int end, int E, int lane,
+                                               int (&idv)[kPermPer])
+{
+#pragma unroll
+    for (int j = 0; j < kPermPer; ++j) idv[j] = clamp_id(ids[min(beg + lane + kWave * j, end - 1)], E);
+}
+
 // Count slots per expert over slots [beg, end) into run[] (LDS, E ints, must
-// be zero on entry).  One wave.
+// be zero on entry).  One wave; end - beg <= kPermChunk.
 __device__ inline void wave_count(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run)
 {
+    if (end <= beg) return;
     const int nbits = id_bits(E);
-    for (int base = beg; base < end; base += kWave) {
-        int s = base + lane;
-        bool valid = s < end;
-        int id = valid ? clamp_id(ids[s], E) : 0;
-        uint64_t m = match_id(id, valid, nbits);
-        bool leader = valid && ((m & ((1ull << lane) - 1)) == 0);
+    int idv[kPermPer];
+    load_chunk_ids(ids, beg, end, E, lane, idv);
+#pragma unroll
+    for (int j = 0; j < kPermPer; ++j) {
+        const int base = beg + kWave * j;
+        if (base >= end) break;   // uniform
+        const bool valid = base + lane < end;
+        const int id = valid ? idv[j] : 0;
+        const uint64_t m = match_id(id, valid, nbits);
+        const bool leader = valid && ((m & ((1ull << lane) - 1)) == 0);
         if (leader) run[id] += __popcll(m);
     }
 }
 
 // Place slots [beg, end) at run[id] + (rank among equal ids), advancing run[].
+// One wave; end - beg <= kPermChunk.
 __device__ inline void wave_scatter(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run,
                              int32_t *sorted_slots, int32_t *slot_pos)
 {
+    if (end <= beg) return;
     const int nbits = id_bits(E);
-    for (int base = beg; base < end; base += kWave) {
-        int s = base + lane;
-        bool valid = s < end;
-        int id = valid ? clamp_id(ids[s], E) : 0;
-        uint64_t m = match_id(id, valid, nbits);
-        uint64_t below = m & ((1ull << lane) - 1);
-        int pos = valid ? run[id] + __popcll(below) : 0;
+    int idv[kPermPer];
+    load_chunk_ids(ids, beg, end, E, lane, idv);
+#pragma unroll
+    for (int j = 0; j < kPermPer; ++j) {
+        const int base = beg + kWave * j;
+        if (base >= end) break;   // uniform
+        const int s = base + lane;
+        const bool valid = s < end;
+        const int id = valid ? idv[j] : 0;
+        const uint64_t m = match_id(id, valid, nbits);
+        const uint64_t below = m & ((1ull << lane) - 1);
+        const int pos = valid ? run[id] + __popcll(below) : 0;
         if (valid) {
             sorted_slots[pos] = s;
             slot_pos[s] = pos;

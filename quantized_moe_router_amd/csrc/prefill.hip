@@ -439,6 +439,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint1
     __shared__ __align__(16) uint16_t s_a[2][kMT * kLdsRow];
     __shared__ __align__(16) uint16_t s_b[2][kRT_N * kLdsRow];
     const int m0 = blockIdx.x * kMT, e0 = blockIdx.y * kRT_N;
+    // this split's share of the reduction over H, and its partial-logit plane
+    const int nsteps = H / kKS / gridDim.z, s0 = blockIdx.z * nsteps;
+    logits += (size_t)blockIdx.z * T * E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int mh = wave & 1, nq = wave >> 1;
     // staging: A 128 x 64 bf16 (2 octets per thread), B 128 x 64 (2 octets per
@@ -470,13 +473,12 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint1
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
-    const int nsteps = H / kKS;
-    load_stage(0);
+    load_stage(s0);
     store_stage(0);
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
         const int buf = s & 1;
-        if (s + 1 < nsteps) load_stage(s + 1);
+        if (s + 1 < nsteps) load_stage(s0 + s + 1);
 #pragma unroll
         for (int ks = 0; ks < kKS / 16; ++ks) {
             const int kk = 16 * ks + 8 * (lane >> 5);
@@ -571,7 +573,7 @@ hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, const D
 hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                               float *logits, hipStream_t st)
 {
-    dim3 grid((d.T + kMT - 1) / kMT, (d.E + kRT_N - 1) / kRT_N);
+    dim3 grid((d.T + kMT - 1) / kMT, (d.E + kRT_N - 1) / kRT_N, router_ksplit(d));
     router_mfma_kernel<<<grid, kRouterThreads, 0, st>>>(x, router_w, d.T, d.H, d.E, logits);
     return hipGetLastError();
 }

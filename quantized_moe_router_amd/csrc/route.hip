@@ -24,14 +24,17 @@ namespace moe {
 // ---------------------------------------------------------------------------
 
 // One wave per token.
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, Dims d,
+// The logits arrive as nsplit partial sums over H ([split][T][E]), added here
+// in split order.
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int nsplit, Dims d,
                                                    int32_t *ids, float *weights)
 {
     __shared__ uint32_t s_topk[4][kTopkLds];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= d.T) return;
-    const TopkLane r = topk_any(logits + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave]);
+    const TopkLane r = topk_any(logits + (size_t)t * d.E, nsplit, (size_t)d.T * d.E, d.E, d.k, lane,
+                                s_topk[wave]);
     if (lane < d.k) {
         ids[(size_t)t * d.k + lane] = r.id;
         weights[(size_t)t * d.k + lane] = r.w;
@@ -66,9 +69,17 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
 {
     __shared__ int s_sum[16], s_nz[16];
     const int e = threadIdx.x, lane = e & (kWave - 1), wave = e >> 6;
+    const int ec = e < d.E ? e : 0;
+    // eight chunks' loads in flight per pass (clamped addresses), summed in order
     int total = 0;
-    if (e < d.E)
-        for (int c = 0; c < nchunks; ++c) total += ws.chunk_hist[(size_t)c * d.E + e];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + ec];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) total += c0 + u < nchunks ? v[u] : 0;
+    }
+    if (e >= d.E) total = 0;
     int nz = (e < d.E && total > 0) ? 1 : 0;
     int incl = wave_incl_scan(total, lane), nz_incl = wave_incl_scan(nz, lane);
     if (lane == kWave - 1) { s_sum[wave] = incl; s_nz[wave] = nz_incl; }
@@ -82,10 +93,16 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
         ro.offsets[e] = off;
         if (nz) ws.active[1 + nz_pos] = e;
         int run = off;
-        for (int c = 0; c < nchunks; ++c) {
-            int v = ws.chunk_hist[(size_t)c * d.E + e];
-            ws.chunk_hist[(size_t)c * d.E + e] = run;
-            run += v;
+        for (int c0 = 0; c0 < nchunks; c0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (c0 + u < nchunks) {
+                    ws.chunk_hist[(size_t)(c0 + u) * d.E + e] = run;
+                    run += v[u];
+                }
         }
     }
     if (e == d.E - 1) {
@@ -132,7 +149,7 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims 
     if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
     hipError_t e = launch_router_mfma(x, router_w, d, ws.logits, st);
     if (e != hipSuccess) return e;
-    topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, d, ro.ids, ro.weights);
+    topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, router_ksplit(d), d, ro.ids, ro.weights);
     return launch_permute(d, ws, ro, st);
 }
 
