@@ -246,6 +246,19 @@ def test_one_workspace_across_shapes():
         assert not ws[:65536].any(), f"T={T} {what}: the hand-off area was not returned to zero"
 
 
+@pytest.mark.parametrize("H,I,E,k", [(768, 384, 40, 6), (1280, 128, 100, 3)])
+@pytest.mark.parametrize("T", [1, 3, 19, 70])
+@pytest.mark.parametrize("shared", [False, True])
+def test_ragged_widths(H, I, E, k, T, shared):
+    """Widths that leave partial lane chunks: hidden 768 / 1280 is 24 / 40
+    chunks of 32 over the 16 lanes of a decode row group, 3 / 5 blocks of 256
+    rows in the many-token down GEMM; 40 and 100 experts leave the last
+    64-expert key block partly empty."""
+    shape = synth.LayerShape(tokens=T, hidden=H, experts=E, top_k=k, inter=I)
+    host = synth.make_layer(shape, seed=31 + T + H, shared=shared)
+    run_and_check(host, label=f"ragged widths H={H} I={I} E={E} k={k} T={T} shared={shared}")
+
+
 def test_tiny_shared_expert():
     for T in (3, 40):
         shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=2, inter=128)
