@@ -51,7 +51,7 @@ Layout layout(const Dims &d)
         return o;
     };
     const size_t S = (size_t)d.S, T = (size_t)d.T;
-    const size_t nchunks = (S + kPermChunk - 1) / kPermChunk;
+    const size_t chunk = (size_t)perm_chunk(d.S), nchunks = (S + chunk - 1) / chunk;
     L.dec_keys = take(4 * (size_t)kDecodeMaxTokens * kMaxExperts);   // same size for every shape
     L.logits = take(4 * T * d.E * (size_t)(d.T > kDecodeMaxTokens ? router_ksplit(d) : 1));
     L.ids = take(4 * S);

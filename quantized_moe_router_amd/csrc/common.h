@@ -328,7 +328,16 @@ struct Dims {
     int sh_I;  // 0 = no shared expert
 };
 
-constexpr int kPermChunk = 1024;  // slots per chunk of the large permutation
+constexpr int kPermChunk = 1024;  // most slots per chunk of the large permutation
+
+// Slots per chunk of the large permutation (S > kPermChunk): about 128 chunks
+// (one wave each in the count and scatter passes), a multiple of 64 between 64
+// and kPermChunk.
+__host__ __device__ inline int perm_chunk(int S)
+{
+    const int c = ((S + 127) / 128 + 63) / 64 * 64;
+    return c < 64 ? 64 : (c > kPermChunk ? kPermChunk : c);
+}
 
 // Split of the many-token router GEMM's reduction over H: the smallest divisor
 // of its 64-wide stage count that gives at least 512 workgroups of 128 tokens

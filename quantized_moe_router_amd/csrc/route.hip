@@ -57,7 +57,8 @@ __global__ __launch_bounds__(kWave) void perm_hist_kernel(const int32_t *__restr
     __shared__ int32_t s_run[kMaxExperts];
     const int c = blockIdx.x, lane = threadIdx.x;
     for (int e = lane; e < d.E; e += kWave) s_run[e] = 0;
-    int beg = c * kPermChunk, end = min(d.S, beg + kPermChunk);
+    const int chunk = perm_chunk(d.S);
+    int beg = c * chunk, end = min(d.S, beg + chunk);
     wave_count(ids, beg, end, d.E, lane, s_run);
     for (int e = lane; e < d.E; e += kWave) ws.chunk_hist[(size_t)c * d.E + e] = s_run[e];
 }
@@ -118,7 +119,8 @@ __global__ __launch_bounds__(kWave) void perm_scatter_kernel(const int32_t *__re
     __shared__ int32_t s_run[kMaxExperts];
     const int c = blockIdx.x, lane = threadIdx.x;
     for (int e = lane; e < d.E; e += kWave) s_run[e] = ws.chunk_hist[(size_t)c * d.E + e];
-    int beg = c * kPermChunk, end = min(d.S, beg + kPermChunk);
+    const int chunk = perm_chunk(d.S);
+    int beg = c * chunk, end = min(d.S, beg + chunk);
     wave_scatter(ids, beg, end, d.E, lane, s_run, ro.sorted_slots, ws.slot_pos);
 }
 
@@ -131,7 +133,7 @@ hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro
         permute_small_kernel<<<1, kWave, 0, st>>>(ro.ids, d, ws, ro);
         return hipGetLastError();
     }
-    int nchunks = (d.S + kPermChunk - 1) / kPermChunk;
+    const int chunk = perm_chunk(d.S), nchunks = (d.S + chunk - 1) / chunk;
     perm_hist_kernel<<<nchunks, kWave, 0, st>>>(ro.ids, d, ws);
     perm_scan_kernel<<<1, 1024, 0, st>>>(d, ws, ro, nchunks);
     perm_scatter_kernel<<<nchunks, kWave, 0, st>>>(ro.ids, d, ws, ro);
