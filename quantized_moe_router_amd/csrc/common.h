@@ -160,7 +160,7 @@ __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c)
 // fp32 -> fp16 bits, round to nearest even, saturating at +-65504.
 __device__ __forceinline__ uint32_t f32_to_f16_sat(float f)
 {
-    f = fminf(fmaxf(f, -65504.f), 65504.f);
+    f = __builtin_amdgcn_fmed3f(f, -65504.f, 65504.f);
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
@@ -210,7 +210,14 @@ __device__ __forceinline__ float act_pairs_h(const ActRaw &r, uint32_t x[16])
     return s;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (each within
+// about 1 ulp of fp32); every caller rounds the product to fp16 (2^-11)
+// right after, so the shortcut is far below the result's own rounding.  For
+// g << 0, e^-g overflows to inf and the reciprocal gives 0.
+__device__ __forceinline__ float silu(float g)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+}
 
 // ---------------------------------------------------------------------------
 // Hand-over between workgroups of one launch.  Agent-scope relaxed atomic

@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     constexpr bool kInt6 = !kRouted;
     __shared__ __align__(16) _Float16 s_a[2][kMT * kLdsRow];
     __shared__ int s_tok[kMT];     // token of each tile row (-1: none)
-    __shared__ int s_slot[kMT];    // routed: slot of each tile row
+    __shared__ int s_yrow[kMT];    // down modes: row of y that each tile row writes
+    __shared__ float s_wgt[kMT];   // down modes: output factor of each tile row
 
     // ---- tile assignment (XCD-aware: the n-blocks of one tile share an XCD) ----
     const int wid = blockIdx.x;
@@ -188,18 +189,24 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
         rows = min(kMT, g.T - m0);
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // down modes: the factor of each row (routing weight, or the shared
+    // expert's gate logit) is loaded here and only written to LDS after the K
+    // loop, so its latency is hidden; rows past the tile load row 0's
+    float wraw = 0.f;
     if (tid < kMT) {
-        int tok = -1, slot = -1;
-        if (tid < rows) {
-            if constexpr (kRouted) {
-                slot = g.sorted_slots[pbase + tid];
-                tok = slot / g.k;
-            } else {
-                tok = m0 + tid;
-            }
+        const int i = tid < rows ? tid : 0;
+        int tok, slot = 0;
+        if constexpr (kRouted) {
+            slot = g.sorted_slots[pbase + i];
+            tok = slot / g.k;
+        } else {
+            tok = m0 + i;
         }
-        s_tok[tid] = tok;
-        s_slot[tid] = slot;
+        if constexpr (!kW13) {
+            wraw = kRouted ? g.weights[slot] : g.gate[tok];
+            s_yrow[tid] = tok * (g.k + 1) + (kRouted ? slot - tok * g.k : g.k);
+        }
+        s_tok[tid] = tid < rows ? tok : -1;
     }
     __syncthreads();
 
@@ -361,10 +368,30 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     }
 
     // ---- epilogue ----
+    if constexpr (!kW13) {
+        // weighted row of slot (t, j) -> y[t][j][:]; the shared expert is slot k
+        // with factor sigmoid(gate); the 2^-10 of the weight scale is folded in
+        if (tid < kMT) s_wgt[tid] = (kRouted ? wraw : 1.f / (1.f + expf(-wraw))) * kScaleDown;
+        __syncthreads();
+    }
     const int col = lane & 31;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         if (mt >= mtiles) continue;
+        // output rows (and factors) of the lane's 16 rows of this tile, read
+        // from LDS before the first store
+        int rowv[16];
+        float wv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int m = 32 * mt + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            if constexpr (kW13) {
+                rowv[j] = kRouted ? pbase + m : s_tok[m];
+            } else {
+                rowv[j] = s_yrow[m];
+                wv[j] = s_wgt[m];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int m = 32 * mt + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
@@ -373,26 +400,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
                 const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
                 const int i = 128 * nb + 32 * wave + col;
                 const int ip = (i & ~7) | pair_pos(i & 7);
-                const size_t row_out = kRouted ? (size_t)(pbase + m) : (size_t)s_tok[m];
-                g.h_out[row_out * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
+                g.h_out[(size_t)rowv[j] * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
             } else {
-                // weighted row of slot (t, j) -> y[t][j][:]; the shared expert is slot k
-                float wgt;
-                size_t yrow;
-                const int t = s_tok[m];
-                if constexpr (kRouted) {
-                    const int slot = s_slot[m];
-                    wgt = g.weights[slot];
-                    yrow = (size_t)t * (g.k + 1) + (slot - t * g.k);
-                } else {
-                    wgt = 1.f / (1.f + expf(-g.gate[t]));
-                    yrow = (size_t)t * (g.k + 1) + g.k;
-                }
+                uint16_t *yr = g.y_out + (size_t)rowv[j] * g.H + kNT * nb + 64 * wave + col;
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int n = kNT * nb + 64 * wave + 32 * nt + col;
-                    g.y_out[yrow * g.H + n] = (uint16_t)f32_to_f16_sat(wgt * acc[mt][nt][j] * kScaleDown);
-                }
+                for (int nt = 0; nt < 2; ++nt) yr[32 * nt] = (uint16_t)f32_to_f16_sat(wv[j] * acc[mt][nt][j]);
             }
         }
     }
