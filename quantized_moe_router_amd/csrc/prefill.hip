@@ -76,18 +76,26 @@ struct GemmArgs {
     size_t b_scales;           // scales per expert
 };
 
-// INT4 word -> one MFMA operand: 8 fp16 values code * s in pair order
-// (0,4)(1,5)(2,6)(3,7); s2 = fp16 pair (s, s).
+// INT4 word -> one MFMA operand: 8 fp16 values (n - 8) * s in pair order
+// (0,4)(1,5)(2,6)(3,7); s2 = fp16 pair (s, s).  fp16 0x6400 is 1024 with
+// mantissa step 1, so a nibble OR-ed into mantissa bits 0-3 gives 1024 + n and
+// into bits 4-7 gives 1024 + 16 n, both exact, as are (1024 + n) - 1032 and
+// (1024 + 16 n) / 16 - 72, i.e. n - 8.  One mask picks nibbles j and j + 4 of
+// the word at once: a word takes one shift, four AND-ORs and two packed fp16
+// operations per pair.
 __device__ __forceinline__ f16x8_t dequant_int4_f16(uint32_t w, h2_t s2)
 {
-    const h2_t bias = {(_Float16)-136.f, (_Float16)-136.f};
-    const uint32_t m = vconst(0x00780078u), b = vconst(0x58005800u);
+    const uint32_t m0 = vconst(0x000F000Fu), m1 = vconst(0x00F000F0u), b = vconst(0x64006400u);
+    const h2_t c0 = {(_Float16)-1032.f, (_Float16)-1032.f};
+    const h2_t k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, c1 = {(_Float16)-72.f, (_Float16)-72.f};
+    const uint32_t w2 = w >> 8;
+    const uint32_t p[4] = {(w & m0) | b, (w & m1) | b, (w2 & m0) | b, (w2 & m1) | b};
     f16x8_t out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t p = (((w >> (4 * j)) << 3) & m) | b;  // 128 + n
-        h2_t v = __builtin_bit_cast(h2_t, p);
-        v = (v + bias) * s2;  // (n - 8) * s, exact
+        h2_t v = __builtin_bit_cast(h2_t, p[j]);
+        v = (j & 1) ? v * k16 + c1 : v + c0;   // n - 8, exact
+        v = v * s2;                            // (n - 8) * s, exact
         out[2 * j] = v[0];
         out[2 * j + 1] = v[1];
     }
@@ -213,9 +221,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     const int K = g.K, nsteps = K / kKS;
     // ---- activation staging: thread -> (row ar, 32 values at 32 * ahalf) ----
     const int ar = tid >> 1, ahalf = tid & 1;
-    // rows past the tile read a valid row (row 0) and are stored as zeros, so
-    // no load sits behind a branch (a guarded load makes the compiler wait for
-    // every outstanding load at the next use)
+    // rows past the tile read a valid row (row 0), so no load sits behind a
+    // branch (a guarded load makes the compiler wait for every outstanding
+    // load at the next use); what such a row accumulates is never stored
     const bool avalid = s_tok[ar] >= 0;
     const int arow = avalid ? ar : 0;
     const uint16_t *asrc;
@@ -223,15 +231,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     else asrc = g.a16 + (size_t)(kRouted ? pbase + arow : s_tok[arow]) * K + 32 * ahalf;
     // two register sets: stage s's activations are loaded two stages before
     // they are used (set s % 2) and stored to LDS one stage before
-    uint4 ra[2][4];
+    u32x4_t ra[2][4];   // vector type: copied to LDS by value, never through memory
     auto load_a = [&](int s, int p) {
 #pragma unroll
-        for (int o = 0; o < 4; ++o) ra[p][o] = reinterpret_cast<const uint4 *>(asrc + s * kKS)[o];
+        for (int o = 0; o < 4; ++o) ra[p][o] = reinterpret_cast<const u32x4_t *>(asrc + s * kKS)[o];
     };
     auto store_a = [&](int buf, int p) {
-        uint4 *dst = reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 32 * ahalf);
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(s_a[buf] + ar * kLdsRow + 32 * ahalf);
 #pragma unroll
-        for (int o = 0; o < 4; ++o) dst[o] = avalid ? ra[p][o] : make_uint4(0, 0, 0, 0);
+        for (int o = 0; o < 4; ++o) dst[o] = ra[p][o];
     };
 
     // ---- weight fragments: lane -> (row n = base + lane % 32, octets 4 * half ..) ----
@@ -262,7 +270,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
                 rb4[q][nt] = *reinterpret_cast<const uint4 *>(bp + brow[nt] * bstride + k0 / 8);
             else
                 load_block6(bp + brow[nt] * bstride + k0 / 32 * 6, rb6[q][nt]);
-            rsc[q][nt] = bs[(size_t)brow[nt] * (K / sgroup) + k0 / sgroup];
+            // INT4: one scale serves the two stages of a 128-wide group
+            // (stage pairs start at even s, set 0), so set 1 loads none
+            if (kInt6 || q == 0) rsc[q][nt] = bs[(size_t)brow[nt] * (K / sgroup) + k0 / sgroup];
         }
     };
 
@@ -284,6 +294,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     auto kloop = [&](auto ma_c) {
         constexpr int MA = decltype(ma_c)::value;
         const bool astage = ar < 32 * MA;     // uniform per wave
+        h2_t s2[2];                           // fp16 scale pairs of the current stage
 
         // one K stage: stage s's weights (set q = s % 2) against LDS buffer q,
         // while stage s+1's activations (set 1-q, loaded two stages ago) are
@@ -294,10 +305,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
             // keep this stage's raw weights and scales; the set is reloaded below
             uint4 w4[2];
             uint32_t w6[2][7];
-            h2_t s2[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                s2[nt] = scale_pair(rsc[q][nt]);
+                if (kInt6 || q == 0) s2[nt] = scale_pair(rsc[q][nt]);
                 if constexpr (!kInt6) w4[nt] = rb4[q][nt];
                 else
 #pragma unroll
