@@ -219,28 +219,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     __syncthreads();
 
     const int K = g.K, nsteps = K / kKS;
-    // ---- activation staging: thread -> (row ar, 32 values at 32 * ahalf) ----
-    const int ar = tid >> 1, ahalf = tid & 1;
+    // ---- activation staging: thread -> 16-byte chunk c8 of rows r8 + 32 o,
+    // o < 4 (row tile o): eight lanes read one row's 128 bytes of a stage, so
+    // each load instruction reads eight whole cache lines ----
+    const int c8 = tid & 7, r8 = tid >> 3;
     // rows past the tile read a valid row (row 0), so no load sits behind a
     // branch (a guarded load makes the compiler wait for every outstanding
     // load at the next use); what such a row accumulates is never stored
-    const bool avalid = s_tok[ar] >= 0;
-    const int arow = avalid ? ar : 0;
-    const uint16_t *asrc;
-    if constexpr (kW13) asrc = g.x + (size_t)s_tok[arow] * g.H + 32 * ahalf;
-    else asrc = g.a16 + (size_t)(kRouted ? pbase + arow : s_tok[arow]) * K + 32 * ahalf;
+    const uint16_t *asrc[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        const int row = r8 + 32 * o, arow = s_tok[row] >= 0 ? row : 0;
+        if constexpr (kW13) asrc[o] = g.x + (size_t)s_tok[arow] * g.H + 8 * c8;
+        else asrc[o] = g.a16 + (size_t)(kRouted ? pbase + arow : s_tok[arow]) * K + 8 * c8;
+    }
     // two register sets: stage s's activations are loaded two stages before
     // they are used (set s % 2) and stored to LDS one stage before
     u32x4_t ra[2][4];   // vector type: copied to LDS by value, never through memory
-    auto load_a = [&](int s, int p) {
-#pragma unroll
-        for (int o = 0; o < 4; ++o) ra[p][o] = reinterpret_cast<const u32x4_t *>(asrc + s * kKS)[o];
-    };
-    auto store_a = [&](int buf, int p) {
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(s_a[buf] + ar * kLdsRow + 32 * ahalf);
-#pragma unroll
-        for (int o = 0; o < 4; ++o) dst[o] = ra[p][o];
-    };
 
     // ---- weight fragments: lane -> (row n = base + lane % 32, octets 4 * half ..) ----
     const int half = lane >> 5;
@@ -289,19 +284,27 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     // chosen once per workgroup: with the count known at compile time there
     // is no branch between the matrix instructions, so the activation reads of
     // the next MFMA step can be issued ahead of them (a branch per tile left
-    // each read waiting on its own).  Waves whose staging rows lie past the
-    // active tiles do not load or store activations.
+    // each read waiting on its own).
     auto kloop = [&](auto ma_c) {
         constexpr int MA = decltype(ma_c)::value;
-        const bool astage = ar < 32 * MA;     // uniform per wave
         h2_t s2[2];                           // fp16 scale pairs of the current stage
+        // only the active row tiles are staged
+        auto load_a = [&](int s, int p) {
+#pragma unroll
+            for (int o = 0; o < MA; ++o) ra[p][o] = *reinterpret_cast<const u32x4_t *>(asrc[o] + s * kKS);
+        };
+        auto store_a = [&](int buf, int p) {
+#pragma unroll
+            for (int o = 0; o < MA; ++o)
+                *reinterpret_cast<u32x4_t *>(s_a[buf] + (r8 + 32 * o) * kLdsRow + 8 * c8) = ra[p][o];
+        };
 
         // one K stage: stage s's weights (set q = s % 2) against LDS buffer q,
         // while stage s+1's activations (set 1-q, loaded two stages ago) are
         // stored and the loads of stages s+3 (activations) and s+2 (weights)
         // are issued
         auto stage = [&](int s, int q) {
-            if (astage && s + 1 < nsteps) store_a(q ^ 1, q ^ 1);
+            if (s + 1 < nsteps) store_a(q ^ 1, q ^ 1);
             // keep this stage's raw weights and scales; the set is reloaded below
             uint4 w4[2];
             uint32_t w6[2][7];
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
                     for (int u = 0; u < 7; ++u) w6[nt][u] = rb6[q][nt][u];
             }
             {   // the last stages re-load the last one (no branch around loads)
-                if (astage) load_a(min(s + 3, nsteps - 1), q ^ 1);
+                load_a(min(s + 3, nsteps - 1), q ^ 1);
                 load_b(min(s + 2, nsteps - 1), q);
             }
             // activation fragments of the active row tiles are read one MFMA
@@ -356,12 +359,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
 
         // prologue: stage 0 in LDS, stages 1 and 2 activations in registers,
         // weights of stages 0 and 1 in flight
-        if (astage) load_a(0, 0);
+        load_a(0, 0);
         load_b(0, 0);
-        if (astage) load_a(min(1, nsteps - 1), 1);
+        load_a(min(1, nsteps - 1), 1);
         load_b(min(1, nsteps - 1), 1);
-        if (astage) store_a(0, 0);
-        if (astage) load_a(min(2, nsteps - 1), 0);
+        store_a(0, 0);
+        load_a(min(2, nsteps - 1), 0);
         __syncthreads();
         int s = 0;
         for (; s + 1 < nsteps; s += 2) {
