@@ -251,24 +251,55 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     const uint16_t *bs = g.bs + (size_t)e * g.b_scales;
     const size_t bstride = kInt6 ? (size_t)K / 32 * 6 : (size_t)K / 8;
     const int sgroup = kInt6 ? kShGroup : kGroup;
-    // weights for two stages in flight: set q holds stage s with s % 2 == q
-    uint4 rb4[2][2];
+    // INT6 (shared expert): each lane loads its own weight fragments, two
+    // stages ahead, set q holding stage s with s % 2 == q
     uint32_t rb6[2][2][7];
     uint16_t rsc[2][2];
-    auto load_b = [&](int s, int q) {
+    auto load_b6 = [&](int s, int q) {
         const int k0 = s * kKS + 32 * half;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            if constexpr (!kInt6)
-                // plain load: the rest of this 128-byte line is used by the next
-                // three stages, so it must not be marked for early eviction
-                rb4[q][nt] = *reinterpret_cast<const uint4 *>(bp + brow[nt] * bstride + k0 / 8);
-            else
-                load_block6(bp + brow[nt] * bstride + k0 / 32 * 6, rb6[q][nt]);
-            // INT4: one scale serves the two stages of a 128-wide group
-            // (stage pairs start at even s, set 0), so set 1 loads none
-            if (kInt6 || q == 0) rsc[q][nt] = bs[(size_t)brow[nt] * (K / sgroup) + k0 / sgroup];
+            load_block6(bp + brow[nt] * bstride + k0 / 32 * 6, rb6[q][nt]);
+            rsc[q][nt] = bs[(size_t)brow[nt] * (K / sgroup) + k0 / sgroup];
         }
+    };
+    // INT4 (routed experts): weights go through LDS one 128-wide K group (two
+    // stages, one scale) at a time.  Thread t loads 16-byte chunk t % 4 of the
+    // group's 64 bytes for tile rows t / 4 + 64 i (i < 4), so a load
+    // instruction reads sixteen whole 64-byte sectors, and the scale of tile
+    // row t.  A group is stored to LDS one group ahead of its use while the
+    // next is in flight.  In LDS, chunk c of tile row r sits at position
+    // c ^ ((r >> 1) & 3), so the fragment reads of eight consecutive rows hit
+    // distinct banks.  Tile row r = 64 w + 32 nt + l is the row wave w uses as
+    // MFMA column l of its weight tile nt.
+    constexpr int QB = kInt6 ? 1 : 2;
+    __shared__ u32x4_t s_bq[QB][kInt6 ? 1 : kNT * 4];
+    __shared__ uint16_t s_bqs[QB][kInt6 ? 1 : kNT];
+    auto tile_row = [&](int r) {
+        const int w = r >> 6, nt = (r >> 5) & 1, l = r & 31;
+        if constexpr (kW13) return nt == 0 ? 128 * nb + 32 * w + l : g.I + 128 * nb + 32 * w + l;
+        else return kNT * nb + r;
+    };
+    const int c4 = tid & 3;
+    const uint8_t *bq = reinterpret_cast<const uint8_t *>(bp) + 16 * c4;
+    uint32_t qoff[4];      // byte offsets of this thread's four rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qoff[i] = (uint32_t)(tile_row((tid >> 2) + 64 * i) * bstride * 4);
+    const uint16_t *qs = bs + (size_t)tile_row(tid) * (K / kGroup);
+    u32x4_t rq[4];         // vector type: stored to LDS by value
+    uint16_t rqs = 0;
+    auto load_q = [&](int grp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rq[i] = *reinterpret_cast<const u32x4_t *>(bq + qoff[i] + 64 * grp);
+        rqs = qs[grp];
+    };
+    auto store_q = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 2) + 64 * i;
+            s_bq[buf][r * 4 + (c4 ^ ((r >> 1) & 3))] = rq[i];
+        }
+        s_bqs[buf][tid] = rqs;
     };
 
     f32x16_t acc[4][2];
@@ -304,21 +335,38 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
         // stored and the loads of stages s+3 (activations) and s+2 (weights)
         // are issued
         auto stage = [&](int s, int q) {
+            const int grp = s >> 1, ngrp = nsteps >> 1;
             if (s + 1 < nsteps) store_a(q ^ 1, q ^ 1);
-            // keep this stage's raw weights and scales; the set is reloaded below
+            if constexpr (!kInt6) {
+                if (q == 0) store_q((grp + 1) & 1);
+            }
+            // keep this stage's raw weights; the set is reloaded below
             uint4 w4[2];
             uint32_t w6[2][7];
+            if constexpr (kInt6) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                if (kInt6 || q == 0) s2[nt] = scale_pair(rsc[q][nt]);
-                if constexpr (!kInt6) w4[nt] = rb4[q][nt];
-                else
+                for (int nt = 0; nt < 2; ++nt) {
+                    s2[nt] = scale_pair(rsc[q][nt]);
 #pragma unroll
                     for (int u = 0; u < 7; ++u) w6[nt][u] = rb6[q][nt][u];
+                }
             }
             {   // the last stages re-load the last one (no branch around loads)
                 load_a(min(s + 3, nsteps - 1), q ^ 1);
-                load_b(min(s + 2, nsteps - 1), q);
+                if constexpr (kInt6) load_b6(min(s + 2, nsteps - 1), q);
+                else if (q == 0) load_q(min(grp + 2, ngrp - 1));
+            }
+            if constexpr (!kInt6) {
+                // this stage's fragments: chunk 2 q + half of tile rows
+                // 64 wave + 32 nt + lane % 32, stored a group ago
+                const int buf = grp & 1;
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int r = 64 * wave + 32 * nt + (lane & 31);
+                    const u32x4_t v = s_bq[buf][r * 4 + ((2 * q + half) ^ ((r >> 1) & 3))];
+                    w4[nt] = make_uint4(v[0], v[1], v[2], v[3]);
+                    if (q == 0) s2[nt] = scale_pair(s_bqs[buf][r]);
+                }
             }
             // activation fragments of the active row tiles are read one MFMA
             // step ahead; weight operands are converted per step, between the
@@ -357,13 +405,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
             __syncthreads();
         };
 
-        // prologue: stage 0 in LDS, stages 1 and 2 activations in registers,
-        // weights of stages 0 and 1 in flight
+        // prologue: stage 0's activations and (INT4) weight group 0 in LDS;
+        // stages 1 and 2 activations, weights of stages 0 and 1 (INT6) or
+        // group 1 (INT4) in flight
         load_a(0, 0);
-        load_b(0, 0);
+        if constexpr (kInt6) {
+            load_b6(0, 0);
+            load_b6(min(1, nsteps - 1), 1);
+        } else {
+            load_q(0);
+        }
         load_a(min(1, nsteps - 1), 1);
-        load_b(min(1, nsteps - 1), 1);
         store_a(0, 0);
+        if constexpr (!kInt6) {
+            store_q(0);
+            load_q(min(1, (nsteps >> 1) - 1));
+        }
         load_a(min(2, nsteps - 1), 0);
         __syncthreads();
         int s = 0;
