@@ -481,7 +481,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
 }
 
 // out[t][n] = bf16( sum_j y[t][j][n] (+ y[t][k][n] for the shared expert) ),
-// fixed order; one thread per 8 outputs.
+// fixed order; one thread per 8 outputs.  The slot rows are loaded four at a
+// time, all four in flight together (clamped, unconditional loads; a clamped
+// duplicate adds +0), instead of one load waited for per slot.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ y, int T, int H,
                                                       int k, int nslots, uint16_t *__restrict__ out)
 {
@@ -489,15 +491,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     const size_t n8 = (size_t)T * H / 8;
     if (i >= n8) return;
     const size_t t = i / (H / 8), c = i % (H / 8);
+    const uint4 *src = reinterpret_cast<const uint4 *>(y + t * (k + 1) * H) + c;
+    const size_t stride = H / 8;   // 16-byte pieces per slot row
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < nslots; ++j) {
-        const uint4 v = reinterpret_cast<const uint4 *>(y + (t * (k + 1) + j) * H)[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int j0 = 0; j0 < nslots; j0 += 4) {
+        uint4 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const h2_t hv = __builtin_bit_cast(h2_t, w[q]);
-            acc[2 * q] += (float)hv[0];
-            acc[2 * q + 1] += (float)hv[1];
+        for (int u = 0; u < 4; ++u) v[u] = src[(size_t)min(j0 + u, nslots - 1) * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // a duplicate adds +0 (a select, not a branch, so the loads stay
+            // ahead of the first use)
+            const bool dup = j0 + u >= nslots;
+            const uint32_t w[4] = {dup ? 0u : v[u].x, dup ? 0u : v[u].y, dup ? 0u : v[u].z, dup ? 0u : v[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const h2_t hv = __builtin_bit_cast(h2_t, w[q]);
+                acc[2 * q] += (float)hv[0];
+                acc[2 * q + 1] += (float)hv[1];
+            }
         }
     }
     uint32_t o[4];
