@@ -38,7 +38,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t dec_keys, logits, ids, weights, counts, offsets, sorted_slots,
-        slot_pos, active, chunk_hist, tiles, n_tiles, h, y, shared_gate, sh_h, xh, xp, xs, total;
+        slot_pos, active, chunk_hist, tiles, h, y, shared_gate, sh_h, xh, xp, xs, total;
 };
 
 Layout layout(const Dims &d)
@@ -62,8 +62,7 @@ Layout layout(const Dims &d)
     L.slot_pos = take(4 * S);
     L.active = take(4 * ((size_t)d.E + 1));
     L.chunk_hist = take(4 * nchunks * d.E);
-    L.tiles = take(4 * routed_tile_slots(d));
-    L.n_tiles = take(4);
+    L.tiles = take(16 * routed_tile_slots(d));
     L.h = take(2 * S * d.I);
     L.y = take(2 * T * ((size_t)d.k + 1) * d.H);
     L.shared_gate = take(4 * T);
@@ -179,8 +178,7 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
     w.slot_pos = reinterpret_cast<int32_t *>(b + L.slot_pos);
     w.active = reinterpret_cast<int32_t *>(b + L.active);
     w.chunk_hist = reinterpret_cast<int32_t *>(b + L.chunk_hist);
-    w.tiles = reinterpret_cast<int32_t *>(b + L.tiles);
-    w.n_tiles = reinterpret_cast<int32_t *>(b + L.n_tiles);
+    w.tiles = reinterpret_cast<int4 *>(b + L.tiles);
     w.h = reinterpret_cast<uint16_t *>(b + L.h);
     w.y = reinterpret_cast<uint16_t *>(b + L.y);
     w.shared_gate = reinterpret_cast<float *>(b + L.shared_gate);

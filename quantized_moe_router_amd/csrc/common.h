@@ -317,8 +317,7 @@ struct Workspace {
     int32_t *slot_pos;       // [S]   inverse of sorted_slots
     int32_t *active;         // [E+1] active[0] = n_active, then expert ids
     int32_t *chunk_hist;     // [nchunks][E]
-    int32_t *tiles;          // [ceil(S/128) + E] grouped-GEMM tiles
-    int32_t *n_tiles;        // [1]
+    int4 *tiles;             // [routed_tile_slots] grouped-GEMM tiles {expert | block << 16, first row, rows, 0}
     // expert intermediates
     uint16_t *h;             // [S][I] fp16, sorted order
     uint16_t *y;             // [T][k+1][H] fp16 weighted slot outputs (many-token path)

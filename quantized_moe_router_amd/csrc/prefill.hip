@@ -61,8 +61,7 @@ struct GemmArgs {
     const uint16_t *a16;       // fp16 activation rows (down modes), pair order
     const int32_t *bp;         // packed weights (expert 0)
     const uint16_t *bs;        // bf16 scales (expert 0)
-    const int32_t *tiles;      // routed: (mblock << 16) | expert
-    const int32_t *n_tiles;    // routed: number of tiles (device)
+    const int4 *tiles;         // routed: {(mblock << 16) | expert or -1, first row, rows, 0}
     const int32_t *offsets;
     const int32_t *counts;
     const int32_t *sorted_slots;
@@ -184,13 +183,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     const int nb = r % nblocks, tile = (r / nblocks) * 8 + xcd;
     int e = 0, m0 = 0, rows = 0, pbase = 0;
     if constexpr (kRouted) {
-        if (tile >= *g.n_tiles) return;
-        const int tv = g.tiles[tile];
-        if (tv < 0) return;   // empty slot of a pair
-        e = tv & 0xFFFF;
-        const int mb = tv >> 16;
-        pbase = g.offsets[e] + mb * kMT;
-        rows = min(kMT, g.counts[e] - mb * kMT);
+        // one load gives the expert, the tile's first sorted row and its rows
+        const int4 tv = g.tiles[tile];
+        if (tv.x < 0) return;   // empty slot
+        e = tv.x & 0xFFFF;
+        pbase = tv.y;
+        rows = tv.z;
     } else {
         m0 = tile * kMT;
         if (m0 >= g.T) return;
@@ -634,28 +632,28 @@ __device__ __forceinline__ int block_excl_sum(int v, int *s_sum, int &total)
     return base + incl - v;
 }
 
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts, int E,
-                                                           int32_t *__restrict__ tiles,
-                                                           int32_t *__restrict__ n_tiles)
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts,
+                                                           const int32_t *__restrict__ offsets, int E,
+                                                           int nslots, int4 *__restrict__ tiles)
 {
     __shared__ int s_sum[16];
     const int e = threadIdx.x;
-    const int nt = e < E ? (counts[e] + kMT - 1) / kMT : 0;
+    const int cnt = e < E ? counts[e] : 0;
+    const int nt = (cnt + kMT - 1) / kMT;
     const int multi = nt >= 2 ? (nt + 1) & ~1 : 0;   // positions of a multi-tile expert
     int nmulti, nsingle;
     const int pm = block_excl_sum(multi, s_sum, nmulti);
     const int ps = block_excl_sum(nt == 1 ? 1 : 0, s_sum, nsingle);
+    const int off = e < E ? offsets[e] : 0;
+    auto entry = [&](int i) { return make_int4(e | (i << 16), off + i * kMT, min(kMT, cnt - i * kMT), 0); };
     if (nt >= 2) {
-        for (int i = 0; i < multi; ++i) tiles[tile_slot(pm + i)] = i < nt ? (e | (i << 16)) : -1;
+        for (int i = 0; i < multi; ++i) tiles[tile_slot(pm + i)] = i < nt ? entry(i) : make_int4(-1, 0, 0, 0);
     } else if (nt == 1) {
-        tiles[tile_slot(nmulti + ps)] = e;
+        tiles[tile_slot(nmulti + ps)] = entry(0);
     }
-    if (e == 1023) {
-        const int used = nmulti + nsingle;
-        const int rounds = (used + 15) / 16;           // 8 pairs of 2 positions per round
-        for (int pos = used; pos < 16 * rounds; ++pos) tiles[tile_slot(pos)] = -1;
-        *n_tiles = 16 * rounds;
-    }
+    // every other slot the GEMM grid covers is empty
+    const int used = nmulti + nsingle;
+    for (int pos = used + (int)threadIdx.x; pos < nslots; pos += blockDim.x) tiles[tile_slot(pos)] = make_int4(-1, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -687,13 +685,13 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     hipError_t e;
     const size_t xn8 = (size_t)d.T * d.H / 8;
     convert_x_kernel<<<(unsigned)((xn8 + 255) / 256), 256, 0, st>>>(a.x, ws.xh, xn8);
-    build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, d.E, ws.tiles, ws.n_tiles);
+    build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, ro.offsets, d.E, (int)routed_tile_slots(d), ws.tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint16_t *y = ws.y;
     // routed gate/up -> h (sorted slot order)
     const int tmax = (int)routed_tile_slots(d);
     GemmArgs g{};
-    g.x = ws.xh; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles; g.n_tiles = ws.n_tiles;
+    g.x = ws.xh; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles;
     g.offsets = ro.offsets; g.counts = ro.counts; g.sorted_slots = ro.sorted_slots;
     g.h_out = ws.h; g.T = d.T; g.H = d.H; g.I = d.I; g.k = d.k; g.K = d.H;
     g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H / kGroup);
