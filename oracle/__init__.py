@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_shared_int6.argtypes = [_ptr] * 6 + [_c_i64] * 4 + [_ptr, _ptr, _ptr, ctypes.c_int]
         L.oracle_forward.argtypes = ([_ptr] * 6 + [_c_i64] * 6 + [_ptr] * 5 + [_c_i64] * 3
                                      + [_ptr, _ptr, _ptr, _ptr, _ptr, ctypes.c_int])
+        L.oracle_quantize_int4.argtypes = [_ptr, _c_i64, _c_i64, _c_i64, _ptr, _ptr, _ptr, _ptr]
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -117,6 +118,25 @@ def dequant_int6(packed: np.ndarray, scales: np.ndarray, group: int = 64) -> np.
     out = np.empty((rows, K), np.float64)
     lib().oracle_dequant_int6(_p(p), _p(s), rows, K, group, _p(out))
     return out
+
+
+def quantize_int4(w: np.ndarray, group: int = 128):
+    """bf16-bits uint16 [rows, K] -> (packed int32 [rows, K/8], scales uint16
+    [rows, K/group], best_err fp32 [rows, K/group], second_err fp32 [...]).
+
+    Round to nearest, group 128, symmetric, per-group clip search minimising
+    the squared error ("Running 125B MoE on Three 3090s - vLLM Optimization
+    Edition", section 7); the readings are listed in moe_oracle.c."""
+    w = _c(w, np.uint16)
+    rows, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group")
+    packed = np.empty((rows, K // 8), np.int32)
+    scales = np.empty((rows, K // group), np.uint16)
+    e1 = np.empty((rows, K // group), np.float32)
+    e2 = np.empty((rows, K // group), np.float32)
+    lib().oracle_quantize_int4(_p(w), rows, K, group, _p(packed), _p(scales), _p(e1), _p(e2))
+    return packed, scales, e1, e2
 
 
 def router_logits(x: np.ndarray, router_w: np.ndarray) -> np.ndarray:

@@ -397,6 +397,130 @@ void oracle_forward(const uint16_t *x, const uint16_t *router_w,
     }
 }
 
+/* ---------------------------------------------------------------------
+ * Load-time INT4 quantizer ([VO] section 7: the experts are quantized
+ * round-to-nearest, group 128, symmetric, with a per-group search for the
+ * clip that minimizes the squared error).
+ *
+ * Readings (the page names the method only):
+ *   - candidate clips: twenty ratios c_j = 1 - j/40, j = 0..19 (1 down to
+ *     0.525) of the group's largest magnitude; the scale of candidate j is
+ *     bf16(fp32(amax * k_j)) with k_j = fp32(c_j / 7), so the clipped
+ *     magnitude maps to the largest positive code 7 (codes span [-8, 7]);
+ *   - codes: the nearest integer to w / s, ties to even, clamped to [-8, 7];
+ *   - the error of a candidate is sum_i (w_i - q_i s)^2 accumulated in fp32
+ *     in index order (each term rounded to fp32, then added): the choice
+ *     between candidates is an integer decision, taken in the precision of
+ *     the GPU kernel, which makes the same operations in the same order;
+ *   - the first candidate with the smallest error wins; candidates whose
+ *     scale is below the smallest normal fp32 (2^-126) are skipped, and a
+ *     group with none left (all zeros) gets scale 0 and codes 0.
+ * Output layout is the path's own: element k of a row is nibble k%8 of
+ * word k/8, stored as code+8; scales bf16 [rows][K/group].
+ * ------------------------------------------------------------------- */
+
+static float bf16_bits_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> bf16 bits, round to nearest even (finite inputs). */
+static uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+#define ORACLE_QCLIPS 20
+
+/* One group of n values: writes codes (in [-8, 7]) and the bf16 scale, and
+ * the errors of the best and second-best candidates (for near-tie checks). */
+void oracle_quantize_group(const uint16_t *w, int64_t n, int8_t *codes,
+                           uint16_t *scale, float *best_err, float *second_err)
+{
+    float amax = 0.f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(bf16_bits_to_float(w[i]));
+        if (a > amax) amax = a;
+    }
+    int best = -1;
+    float e_best = INFINITY, e_second = INFINITY;
+    uint16_t s_best = 0;
+    for (int j = 0; j < ORACLE_QCLIPS; ++j) {
+        const float kj = (float)((1.0 - j / 40.0) / 7.0);
+        const float t = amax * kj;
+        const uint16_t sb = float_to_bf16_rne(t);
+        const float s = bf16_bits_to_float(sb);
+        if (!(s >= 1.17549435e-38f)) continue;   /* below 2^-126: skipped */
+        float err = 0.f;
+        for (int64_t i = 0; i < n; ++i) {
+            const float x = bf16_bits_to_float(w[i]);
+            double q = rint((double)x / (double)s);
+            if (q < -8.0) q = -8.0;
+            if (q > 7.0) q = 7.0;
+            const float d = x - (float)q * s;        /* exact */
+            const float d2 = d * d;
+            err = err + d2;
+        }
+        if (err < e_best) {
+            e_second = e_best;
+            e_best = err;
+            best = j;
+            s_best = sb;
+        } else if (err < e_second) {
+            e_second = err;
+        }
+    }
+    if (best < 0) {   /* all-zero (or subnormal-only) group */
+        for (int64_t i = 0; i < n; ++i) codes[i] = 0;
+        *scale = 0;
+        if (best_err) *best_err = 0.f;
+        if (second_err) *second_err = INFINITY;
+        return;
+    }
+    const float s = bf16_bits_to_float(s_best);
+    for (int64_t i = 0; i < n; ++i) {
+        double q = rint((double)bf16_bits_to_float(w[i]) / (double)s);
+        if (q < -8.0) q = -8.0;
+        if (q > 7.0) q = 7.0;
+        codes[i] = (int8_t)q;
+    }
+    *scale = s_best;
+    if (best_err) *best_err = e_best;
+    if (second_err) *second_err = e_second;
+}
+
+/* W bf16 [rows][K] -> packed int32 [rows][K/8], scales bf16 [rows][K/group],
+ * and per group the best and second-best candidate errors (may be NULL). */
+void oracle_quantize_int4(const uint16_t *w, int64_t rows, int64_t K, int64_t group,
+                          int32_t *packed, uint16_t *scales, float *best_err,
+                          float *second_err)
+{
+    const int64_t ng = K / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int8_t *codes = (int8_t *)malloc((size_t)group);
+        for (int64_t g = 0; g < ng; ++g) {
+            const int64_t gi = r * ng + g;
+            oracle_quantize_group(w + r * K + g * group, group, codes, scales + gi,
+                                  best_err ? best_err + gi : NULL,
+                                  second_err ? second_err + gi : NULL);
+            for (int64_t i = 0; i < group; i += 8) {
+                uint32_t word = 0;
+                for (int b = 0; b < 8; ++b)
+                    word |= (uint32_t)(codes[i + b] + 8) << (4 * b);
+                packed[r * (K / 8) + (g * group + i) / 8] = (int32_t)word;
+            }
+        }
+        free(codes);
+    }
+}
+
 /* Threads the OpenMP runtime will use by default (for reporting). */
 int oracle_max_threads(void)
 {

@@ -383,3 +383,125 @@ def test_token_subset_equals_full():
     full = oracle.forward(layer)
     sub = oracle.forward(layer, tokens=[5, 1])
     assert np.array_equal(sub["out"], full["out"][[5, 1]])
+
+
+# ---------------------------------------------------------------------------
+# Load-time INT4 quantizer ([VO] section 7: round to nearest, group 128,
+# symmetric, per-group clip search minimising the squared error)
+# ---------------------------------------------------------------------------
+from fractions import Fraction
+
+
+def _to_bf16_bits(a):
+    """fp32 array -> bf16 bit patterns, round to nearest even (finite)."""
+    u = np.asarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bits_to_float(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32)
+
+
+def _unpack_codes(packed):
+    """int32 words -> codes, element k = nibble k % 8 of word k // 8, minus 8
+    (written independently of the oracle's unpacking)."""
+    u = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
+    nib = np.stack([(u >> (4 * b)) & 15 for b in range(8)], axis=-1)
+    return nib.reshape(u.shape[0], -1) - 8
+
+
+def test_quantizer_reproduces_exact_groups():
+    # values n * 2^-6 with |n| <= 7 and 7 present: the unclipped candidate
+    # has scale exactly 2^-6 and zero error; any clip would saturate the 7s
+    rng = np.random.default_rng(3)
+    n = rng.integers(-7, 8, (6, 256))
+    n[:, 0] = 7
+    n[:, 128] = -7
+    n[3, 128] = 7
+    w = _to_bf16_bits(n * 2.0 ** -6)
+    packed, scales, e1, _ = oracle.quantize_int4(w)
+    assert np.all(_bits_to_float(scales) == 2.0 ** -6)
+    assert np.all(e1 == 0)
+    assert np.array_equal(_unpack_codes(packed), n)
+
+
+def test_quantizer_scale_invariance():
+    # the search is scale-free: w * 2^m gives the same codes and scales * 2^m
+    rng = np.random.default_rng(5)
+    f = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    f[2, 17] = 0.3   # an outlier
+    base = oracle.quantize_int4(_to_bf16_bits(f))
+    for m in (-4, 3, 9):
+        sc = oracle.quantize_int4(_to_bf16_bits(f * np.float32(2.0 ** m)))
+        assert np.array_equal(sc[0], base[0])
+        assert np.array_equal(_bits_to_float(sc[1]), _bits_to_float(base[1]) * np.float32(2.0 ** m))
+
+
+def test_quantizer_codes_are_nearest_levels_ties_even():
+    # given the returned scale, every code is the nearest level in [-8, 7] to
+    # w / s with ties to the even level (checked in exact rationals); the
+    # groups hold exact half-level values to exercise the ties
+    rng = np.random.default_rng(7)
+    f = (rng.standard_normal((4, 128)) * 0.02).astype(np.float32)
+    f[0, :8] = np.array([7, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5], np.float32) * 2.0 ** -6
+    f[0, 8:] = np.round(f[0, 8:] * 64 * 2) / 128   # more exact halves
+    f[0, 8:] = np.clip(f[0, 8:], -7 * 2.0 ** -6, 7 * 2.0 ** -6)
+    w = _to_bf16_bits(f)
+    packed, scales, _, _ = oracle.quantize_int4(w)
+    codes = _unpack_codes(packed)
+    for r in range(w.shape[0]):
+        s = Fraction(float(_bits_to_float(scales[r, 0])))
+        assert s > 0
+        for k in range(128):
+            x = Fraction(float(_bits_to_float(w[r, k])))
+            t = x / s
+            lo = math.floor(t)
+            if t - lo == Fraction(1, 2):
+                q = lo if lo % 2 == 0 else lo + 1
+            else:
+                q = lo if t - lo < Fraction(1, 2) else lo + 1
+            q = max(-8, min(7, q))
+            assert codes[r, k] == q, (r, k, t)
+    # the hand-worked ties of row 0 (scale 2^-6 there: 7 sets the maximum)
+    if float(_bits_to_float(scales[0, 0])) == 2.0 ** -6:
+        assert list(codes[0, :8]) == [7, 2, 4, -2, -4, 0, 0, 2]
+
+
+def _exact_sq_error(wbits, codes, sbits):
+    s = Fraction(float(_bits_to_float(sbits)))
+    return sum((Fraction(float(_bits_to_float(b))) - int(q) * s) ** 2 for b, q in zip(wbits, codes))
+
+
+def test_quantizer_clips_an_outlier_group_and_beats_plain_rtn():
+    # 127 small values and one large one: plain round-to-nearest with the
+    # full range wastes most levels; the search must clip (a smaller scale
+    # than amax/7) and its exact squared error must be below plain RTN's
+    rng = np.random.default_rng(11)
+    f = (rng.standard_normal(128) * 0.02).astype(np.float32)
+    f[40] = 0.4
+    w = _to_bf16_bits(f)[None, :]
+    packed, scales, _, _ = oracle.quantize_int4(w)
+    codes = _unpack_codes(packed)[0]
+    s = float(_bits_to_float(scales[0, 0]))
+    amax = float(np.abs(_bits_to_float(w)).max())
+    assert s < amax / 7
+    # plain RTN, written independently: scale bf16(amax / 7), nearest codes
+    s_rtn = _to_bf16_bits(np.float32(amax / 7))
+    sr = Fraction(float(_bits_to_float(s_rtn)))
+    rtn_codes = []
+    for b in w[0]:
+        t = Fraction(float(_bits_to_float(b))) / sr
+        rtn_codes.append(max(-8, min(7, round(t))))
+    assert _exact_sq_error(w[0], codes, scales[0, 0]) < _exact_sq_error(w[0], rtn_codes, s_rtn)
+
+
+def test_quantizer_zero_group_and_packing():
+    w = np.zeros((2, 256), np.uint16)
+    w[1, 128:] = _to_bf16_bits(np.full(128, 0.25, np.float32))
+    packed, scales, _, _ = oracle.quantize_int4(w)
+    assert np.all(packed[0] == np.int32(-2004318072))   # 0x88888888: every code 0
+    assert scales[0, 0] == 0 and scales[0, 1] == 0 and scales[1, 0] == 0
+    # a constant group: the unclipped scale, every code 7 (0xFFFFFFFF words)
+    assert np.all(_unpack_codes(packed)[1, 128:] == 7)
+    assert np.all(packed[1, 16:] == -1)
+    assert float(_bits_to_float(scales[1, 1])) == float(_bits_to_float(_to_bf16_bits(np.float32(0.25) * np.float32(1.0 / 7.0))))
