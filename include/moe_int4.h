@@ -151,6 +151,24 @@ int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
                                 size_t workspace_bytes, void *hip_stream,
                                 void *const *events);
 
+/* Load-time INT4 quantizer ("Running 125B MoE on Three 3090s - vLLM
+ * Optimization Edition", section 7: round to nearest, group 128, symmetric,
+ * with a per-group search for the clip that minimizes the squared error):
+ *   w       bf16  [rows][cols]        in   weights (finite values)
+ *   packed  int32 [rows][cols/8]      out  codes in the layout above
+ *   scales  bf16  [rows][cols/group]  out
+ * For each group of 128 inputs of a row, with amax its largest magnitude,
+ * the candidates are the scales s_j = bf16(fp32(amax * fp32((1 - j/40) / 7)))
+ * for j = 0..19 (clips of 1 down to 0.525 of amax, the clip mapped to code
+ * 7); a candidate's codes are the nearest integers to w / s_j (ties to even)
+ * clamped to [-8, 7], and its error is the sum of (w - code * s_j)^2 in fp32
+ * in input order.  The first candidate with the smallest error is written.
+ * Scales below 2^-126 are not candidates; a group without any (all zeros)
+ * gets scale 0 and codes 0.  group must be 128, cols a multiple of it and
+ * rows * cols below 2^31; rows = 0 is a no-op.  Needs no workspace. */
+int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t group,
+                          int32_t *packed, uint16_t *scales, void *hip_stream);
+
 /* Message for the calling thread's most recent failing call ("" if none). */
 const char *moe_int4_last_error(void);
 

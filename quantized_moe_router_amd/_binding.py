@@ -52,17 +52,19 @@ def lib() -> ctypes.CDLL:
         L.moe_int4_experts.argtypes = [P] * 11 + [ctypes.c_size_t, P]
         L.moe_int4_forward.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P]
         L.moe_int4_forward_traced.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_int4_quantize.argtypes = [P, _c_i32, _c_i32, _c_i32, P, P, P]
         L.moe_int4_last_error.restype = ctypes.c_char_p
         L.moe_int4_version.restype = ctypes.c_char_p
         for f in ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts", "moe_int4_forward",
-                  "moe_int4_forward_traced"):
+                  "moe_int4_forward_traced", "moe_int4_quantize"):
             getattr(L, f).restype = _c_i32
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts",
-            "moe_int4_forward", "moe_int4_forward_traced", "moe_int4_last_error", "moe_int4_version")
+            "moe_int4_forward", "moe_int4_forward_traced", "moe_int4_quantize",
+            "moe_int4_last_error", "moe_int4_version")
 
 
 def _check(rc: int):
@@ -144,6 +146,12 @@ def moe_int4_forward_traced(x, router_w, w13_packed, w13_scales, w2_packed, w2_s
                                          _ptr(w2_packed), _ptr(w2_scales), int(top_k), _ptr(out),
                                          ctypes.byref(shape), ctypes.byref(shared) if shared else None,
                                          _ptr(workspace), workspace.numel(), _stream(stream), arr))
+
+
+def moe_int4_quantize(w, rows: int, cols: int, packed, scales, group: int = 128, stream=None):
+    """w bf16 [rows, cols] (device) -> packed int32 [rows, cols/8], scales bf16 [rows, cols/group]."""
+    _check(lib().moe_int4_quantize(_ptr(w), int(rows), int(cols), int(group), _ptr(packed),
+                                   _ptr(scales), _stream(stream)))
 
 
 def version() -> str:

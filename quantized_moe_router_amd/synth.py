@@ -65,6 +65,18 @@ def _words(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.integers(0, 2**32, size=shape, dtype=np.uint32).view(np.int32)
 
 
+def make_dense_weights(rows: int, cols: int, seed: int, std: float = 0.02,
+                       outlier_frac: float = 1e-3, outlier_scale: float = 15.0) -> np.ndarray:
+    """Dense bf16 weights before quantization, uint16 bits [rows, cols]:
+    N(0, std), with a seeded fraction of entries multiplied by outlier_scale
+    (the heavy tail a clip search exists for)."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((rows, cols)).astype(np.float32) * np.float32(std)
+    mask = rng.random((rows, cols)) < outlier_frac
+    w[mask] *= np.float32(outlier_scale)
+    return bf16_bits(w)
+
+
 def make_weights(shape: LayerShape, seed: int = 0) -> dict:
     """Router and expert weights of one layer (independent of the token count)."""
     H, E, I, G = shape.hidden, shape.experts, shape.inter, shape.group

@@ -104,3 +104,22 @@ def test_no_device_is_reported_not_crashed():
         pytest.skip("a GPU is present")
     rc = _forward(_shape())
     assert rc == B.EDEVICE
+
+
+@pytest.mark.parametrize("rows,cols,group,msg", [
+    (4, 256, 64, "group"),
+    (4, 200, 128, "cols"),
+    (-1, 256, 128, "rows"),
+    (4, 0, 128, "cols"),
+    (1 << 16, 1 << 15, 128, "2^31"),
+])
+def test_quantize_bad_arguments_rejected(rows, cols, group, msg):
+    rc = B.lib().moe_int4_quantize(None, rows, cols, group, None, None, None)
+    assert rc == B.EINVAL
+    assert msg in B.lib().moe_int4_last_error().decode()
+
+
+def test_quantize_zero_rows_is_a_no_op_and_null_buffers_rejected():
+    assert B.lib().moe_int4_quantize(None, 0, 256, 128, None, None, None) == 0
+    rc = B.lib().moe_int4_quantize(None, 2, 256, 128, None, None, None)
+    assert rc == B.EINVAL and "w" in B.lib().moe_int4_last_error().decode()

@@ -1,0 +1,97 @@
+"""GPU parity of the load-time INT4 quantizer ("Running 125B MoE on Three
+3090s - vLLM Optimization Edition", section 7: round to nearest, group 128,
+symmetric, per-group clip search for the smallest squared error): the HIP
+kernel, through the C ABI, against the CPU oracle on the same bf16 inputs.
+
+The codes and the scale of a group are integers decided by floating point;
+both sides take the decision in fp32 with the same operations in the same
+order, so packed words and scales must match bit for bit."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_router_amd import _binding as B
+from quantized_moe_router_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    yield
+
+
+def gpu_quantize(w: np.ndarray):
+    rows, cols = w.shape
+    wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).cuda()
+    packed = torch.empty((rows, cols // 8), dtype=torch.int32, device="cuda")
+    scales = torch.empty((rows, cols // 128), dtype=torch.int16, device="cuda")
+    B.moe_int4_quantize(wd, rows, cols, packed, scales)
+    torch.cuda.synchronize()
+    return packed.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+
+
+def check(w: np.ndarray, label: str):
+    say(f"quantize case {label}: {w.shape}")
+    gp, gs = gpu_quantize(w)
+    op, os_, _, _ = oracle.quantize_int4(w)
+    bad_s = np.argwhere(gs != os_)
+    assert bad_s.size == 0, f"{label}: {len(bad_s)} scales differ, first {bad_s[:3].tolist()}"
+    bad_w = np.argwhere(gp != op)
+    assert bad_w.size == 0, f"{label}: {len(bad_w)} packed words differ, first {bad_w[:3].tolist()}"
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(7, 128, 1), (300, 2560, 2), (64, 640, 3), (1, 4096, 4)])
+def test_quantize_random(rows, cols, seed):
+    check(synth.make_dense_weights(rows, cols, seed), f"random {rows}x{cols}")
+
+
+def test_quantize_special_groups():
+    f = (np.random.default_rng(9).standard_normal((12, 256)) * 0.02).astype(np.float32)
+    f[0] = 0.0                                                  # zero groups
+    f[1, :128] = 0.25                                           # constant group
+    f[1, 128:] = -0.125
+    n = np.random.default_rng(10).integers(-7, 8, 256)
+    n[0] = 7
+    n[128] = -7
+    f[2] = n * 2.0 ** -6                                        # exactly representable
+    f[3, :8] = np.array([7, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5]) * 2.0 ** -6   # exact ties
+    f[4, 40] = 0.4                                              # one outlier
+    f[5] *= np.float32(1e-30)                                   # tiny magnitudes
+    f[6] *= np.float32(1e30)                                    # huge magnitudes
+    f[7, :128] = 0.0
+    f[7, 5] = 1e-39                                             # a lone subnormal
+    f[8, ::2] = 0.0                                             # half zeros
+    f[9] = -np.abs(f[9])                                        # one-signed
+    f[10, :128] = -8 * 2.0 ** -4                                # the code -8 level
+    f[10, 1] = 7 * 2.0 ** -4
+    check(synth.bf16_bits(f), "special groups")
+
+
+def test_quantize_real_expert_shapes():
+    # one expert's fused gate/up [2I, H] and down [H, I] at the real shape
+    check(synth.make_dense_weights(1280, 2560, 21), "gate/up 1280x2560")
+    check(synth.make_dense_weights(2560, 640, 22), "down 2560x640")
+
+
+def test_quantized_weights_drive_the_layer():
+    # the quantizer's output is a valid weight set for the layer: dequantized
+    # by the oracle it reproduces the input within the quantization error
+    w = synth.make_dense_weights(256, 256, 30)
+    gp, gs = gpu_quantize(w)
+    deq = oracle.dequant_int4(gp, gs)
+    x = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s = (gs.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(deq - x).reshape(256, 2, 128)
+    clip = np.abs(x).reshape(256, 2, 128) > 7.5 * s[:, :, None]
+    # unclipped inputs are within half a level of their code
+    assert np.all(err[~clip] <= 0.5 * np.broadcast_to(s[:, :, None], err.shape)[~clip] * (1 + 1e-12))
