@@ -1,6 +1,6 @@
 """Benchmark of the INT4 routed-expert MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode1|decode4|decode64|prefill512|prefill8192]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode1|decode4|decode64|prefill512|prefill8192|quantize64]
 
 A step is one forward of the whole layer (router, top-k, permutation, gate/up
 projection with SiLU-gate, down projection with the weighted combine) over one
@@ -43,7 +43,11 @@ CONFIGS = {
     "decode64": dict(tokens=64, layers=48, zipf=None, shared=False),
     "prefill512": dict(tokens=512, layers=16, zipf=1.1, shared=False),
     "prefill8192": dict(tokens=8192, layers=4, zipf=None, shared=True),
+    # the load-time quantizer (not the layer): 64 experts' bf16 gate/up and
+    # down weights at the real shape per step
+    "quantize64": dict(experts=64),
 }
+VALU_PEAK_TOPS = 39.3        # MI355X vector ALU, non-packed fp32 lane operations per second (T)
 
 
 def parse():
@@ -121,6 +125,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     B.lib()
+    if args.config == "quantize64":
+        return bench_quantize(args)
     cfg = dict(CONFIGS[args.config])
     if args.layers:
         cfg["layers"] = args.layers
@@ -279,7 +285,8 @@ def main():
     else:
         achieved = w13_flops / (w13_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": "moe_gemm_kernel<kRoutedW13> (routed gate/up grouped GEMM, "
-                                           "fp16 MFMA on INT4 dequantised in registers) + tile list",
+                                           "fp16 MFMA, INT4 weight groups staged through LDS and "
+                                           "dequantised in registers) + tile list",
                 "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": w13_flops, "launch_us": round(w13_us, 3)}
@@ -328,6 +335,96 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers[0], xs, T, k, args.cpu_seconds, synth)
+    print(json.dumps(result), flush=True)
+
+
+def bench_quantize(args):
+    """The load-time INT4 quantizer on 64 experts' weights per step: gate/up
+    [64 * 2I, H] and down [64 * H, I] bf16, N(0, 0.02) with 0.1 % outliers x15
+    (generated on the device).  Work per weight: 20 candidate clips, each
+    costing at least a multiply, a rounding, a residual FMA and a squared-error
+    FMA (4 vector operations), so 80 operations per weight against the
+    non-packed fp32 vector rate."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_router_amd import _binding as B
+    from quantized_moe_router_amd import synth
+
+    E, H, I = CONFIGS["quantize64"]["experts"], 2560, 640
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(4242)
+    mats = []
+    for rows, cols in ((E * 2 * I, H), (E * H, I)):
+        w = torch.randn(rows, cols, generator=g, device=dev) * 0.02
+        mask = torch.rand(rows, cols, generator=g, device=dev) < 1e-3
+        w = torch.where(mask, w * 15.0, w)
+        wb = w.to(torch.bfloat16).view(torch.int16).contiguous()
+        del w, mask
+        packed = torch.empty(rows, cols // 8, dtype=torch.int32, device=dev)
+        scales = torch.empty(rows, cols // 128, dtype=torch.int16, device=dev)
+        mats.append((wb, rows, cols, packed, scales))
+    nweights = sum(r * c for _, r, c, _, _ in mats)
+
+    def step():
+        for wb, rows, cols, packed, scales in mats:
+            B.moe_int4_quantize(wb, rows, cols, packed, scales)
+
+    K, W = max(1, min(args.steps, 50)), max(1, min(args.warmup, 5))
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    TE = TimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = [TE.create() for _ in range(3 * K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        TE.record(ev[3 * i], stream)
+        B.moe_int4_quantize(*mats[0][:3], mats[0][3], mats[0][4])
+        TE.record(ev[3 * i + 1], stream)
+        B.moe_int4_quantize(*mats[1][:3], mats[1][3], mats[1][4])
+        TE.record(ev[3 * i + 2], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    l0 = np.mean([TE.ms(ev[3 * i], ev[3 * i + 1]) for i in range(K)])
+    l1 = np.mean([TE.ms(ev[3 * i + 1], ev[3 * i + 2]) for i in range(K)])
+    ms = float(l0 + l1)
+    per_s = nweights / (ms * 1e-3)
+    n0 = mats[0][1] * mats[0][2]
+    achieved = 80 * n0 / (l0 * 1e-3) / 1e12
+    result = {
+        "metric": "INT4 load-time quantizer: weights quantized per second",
+        "value": round(per_s / 1e9, 3), "unit": "Gweights/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, int4 codes + bf16 scales out, fp32 search",
+        "data": "synthetic (seeded, device-generated bf16 weights)",
+        "config": {"workload": f"quantize64: {E} experts' gate/up [{E * 2 * I}x{H}] and down "
+                               f"[{E * H}x{I}] bf16 weights per step, group 128, 20 clip ratios",
+                   "weights": nweights},
+        "roofline": {"bound": "alu", "kernel": "quantize_int4_kernel (gate/up launch)",
+                     "achieved": round(achieved, 3), "peak": VALU_PEAK_TOPS, "unit": "Top/s",
+                     "frac": round(achieved / VALU_PEAK_TOPS, 4), "traffic": None,
+                     "algorithmic_ops_per_launch": 80 * n0, "launch_us": round(float(l0) * 1e3, 2)},
+        "wall_s": round(wall, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 64
+        wh = synth.make_dense_weights(rows, H, 4242)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.quantize_int4(wh)
+            n += rows * H
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n / el / 1e9, 6), "unit": "Gweights/s",
+                                  "cores": oracle.max_threads(), "kind": "oracle",
+                                  "sample": f"{n // (rows * H)} calls on {rows}x{H} weights of the same "
+                                            f"distribution (host-generated), {el:.1f} s"}
     print(json.dumps(result), flush=True)
 
 
