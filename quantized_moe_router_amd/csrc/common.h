@@ -363,13 +363,13 @@ inline int router_ksplit(const Dims &d)
     return best;
 }
 
-// Slots of the grouped-GEMM tile list: 128-row tiles in pairs, pairs dealt
-// round-robin to the 8 XCDs, 16 slots per round.  At most S / 128 + 2 E tile
-// positions are used (each expert's tiles rounded up to a pair), which this
-// bound covers.
+// Slots of the grouped-GEMM tile list: row tiles (128 rows, or 64 when the
+// slots per expert are few) in pairs, pairs dealt round-robin to the 8 XCDs,
+// 16 slots per round.  At most S / 64 + 2 E tile positions are used (each
+// expert's tiles rounded up to a pair), which this bound covers.
 inline size_t routed_tile_slots(const Dims &d)
 {
-    const size_t pairs = ((size_t)d.S + 127) / 128 / 2 + (size_t)d.E + 1;
+    const size_t pairs = ((size_t)d.S + 63) / 64 / 2 + (size_t)d.E + 1;
     return 16 * ((pairs + 7) / 8);
 }
 

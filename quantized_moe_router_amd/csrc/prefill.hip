@@ -65,6 +65,7 @@ struct GemmArgs {
     const int32_t *offsets;
     const int32_t *counts;
     const int32_t *sorted_slots;
+    int small_rows;            // routed: tiles of at most this many rows are left to the small-tile launch
     const float *weights;      // routing weights per slot
     const float *gate;         // shared-expert gate logits [T]
     uint16_t *h_out;           // fp16 activation out (gate/up modes)
@@ -166,13 +167,20 @@ __device__ __forceinline__ h2_t scale_pair(uint16_t bf)
 // byte is read and converted once per workgroup.  Within a 64-wide K stage,
 // MFMA step j uses, on lanes 0-31, octet j and, on lanes 32-63, octet 4 + j:
 // that makes each lane's weight bytes for the stage contiguous.
-template <int MODE>
-__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, int nblocks)
+//
+// MAXMA is the most 32-row tiles a workgroup takes: 4 (the 128-row tile, two
+// workgroups per CU), or 2 for routed tiles of at most 64 rows, which then
+// fit three workgroups per CU (fewer accumulators, half the activation LDS):
+// with few slots per expert the tiles are small and the extra workgroup per
+// CU hides more of the weights' memory latency.
+template <int MODE, int MAXMA = 4>
+__global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_kernel(GemmArgs g, int nblocks)
 {
     constexpr bool kW13 = (MODE == kRoutedW13 || MODE == kSharedW13);
     constexpr bool kRouted = (MODE == kRoutedW13 || MODE == kRoutedW2);
     constexpr bool kInt6 = !kRouted;
-    __shared__ __align__(16) _Float16 s_a[2][kMT * kLdsRow];
+    static_assert(MAXMA == 4 || (MAXMA == 2 && kRouted), "small tiles are a routed-GEMM variant");
+    __shared__ __align__(16) _Float16 s_a[2][32 * MAXMA * kLdsRow];
     __shared__ int s_tok[kMT];     // token of each tile row (-1: none)
     __shared__ int s_yrow[kMT];    // down modes: row of y that each tile row writes
     __shared__ float s_wgt[kMT];   // down modes: output factor of each tile row
@@ -189,6 +197,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
         e = tv.x & 0xFFFF;
         pbase = tv.y;
         rows = tv.z;
+        // with a small-tile launch beside it, each launch takes its own tiles
+        if (MAXMA == 2 ? rows > 64 : rows <= g.small_rows) return;
     } else {
         m0 = tile * kMT;
         if (m0 >= g.T) return;
@@ -300,9 +310,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
         s_bqs[buf][tid] = rqs;
     };
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[MAXMA][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MAXMA; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -428,11 +438,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
         }
         if (s < nsteps) stage(s, 0);
     };
-    switch (mtiles) {
-    case 1: kloop(std::integral_constant<int, 1>{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}); break;
-    default: kloop(std::integral_constant<int, 4>{}); break;
+    if constexpr (MAXMA == 2) {
+        if (mtiles == 1) kloop(std::integral_constant<int, 1>{});
+        else kloop(std::integral_constant<int, 2>{});
+    } else {
+        switch (mtiles) {
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        default: kloop(std::integral_constant<int, 4>{}); break;
+        }
     }
 
     // ---- epilogue ----
@@ -444,7 +459,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs g, i
     }
     const int col = lane & 31;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MAXMA; ++mt) {
         if (mt >= mtiles) continue;
         // output rows (and factors) of the lane's 16 rows of this tile, read
         // from LDS before the first store
@@ -634,18 +649,18 @@ __device__ __forceinline__ int block_excl_sum(int v, int *s_sum, int &total)
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts,
                                                            const int32_t *__restrict__ offsets, int E,
-                                                           int nslots, int4 *__restrict__ tiles)
+                                                           int nslots, int mt, int4 *__restrict__ tiles)
 {
     __shared__ int s_sum[16];
     const int e = threadIdx.x;
     const int cnt = e < E ? counts[e] : 0;
-    const int nt = (cnt + kMT - 1) / kMT;
+    const int nt = (cnt + mt - 1) / mt;
     const int multi = nt >= 2 ? (nt + 1) & ~1 : 0;   // positions of a multi-tile expert
     int nmulti, nsingle;
     const int pm = block_excl_sum(multi, s_sum, nmulti);
     const int ps = block_excl_sum(nt == 1 ? 1 : 0, s_sum, nsingle);
     const int off = e < E ? offsets[e] : 0;
-    auto entry = [&](int i) { return make_int4(e | (i << 16), off + i * kMT, min(kMT, cnt - i * kMT), 0); };
+    auto entry = [&](int i) { return make_int4(e | (i << 16), off + i * mt, min(mt, cnt - i * mt), 0); };
     if (nt >= 2) {
         for (int i = 0; i < multi; ++i) tiles[tile_slot(pm + i)] = i < nt ? entry(i) : make_int4(-1, 0, 0, 0);
     } else if (nt == 1) {
@@ -675,6 +690,12 @@ template <int MODE>
 static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st)
 {
     const int groups = (ntiles_max + 7) / 8;
+    if constexpr (MODE == kRoutedW13 || MODE == kRoutedW2) {
+        if (g.small_rows > 0) {
+            moe_gemm_kernel<MODE, 2><<<groups * 8 * nblocks, kGemmThreads, 0, st>>>(g, nblocks);
+            return hipGetLastError();
+        }
+    }
     moe_gemm_kernel<MODE><<<groups * 8 * nblocks, kGemmThreads, 0, st>>>(g, nblocks);
     return hipGetLastError();
 }
@@ -685,7 +706,9 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     hipError_t e;
     const size_t xn8 = (size_t)d.T * d.H / 8;
     convert_x_kernel<<<(unsigned)((xn8 + 255) / 256), 256, 0, st>>>(a.x, ws.xh, xn8);
-    build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, ro.offsets, d.E, (int)routed_tile_slots(d), ws.tiles);
+    const bool small = (long)d.S < 32L * d.E;
+    build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, ro.offsets, d.E, (int)routed_tile_slots(d),
+                                           small ? 64 : kMT, ws.tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint16_t *y = ws.y;
     // routed gate/up -> h (sorted slot order)
@@ -694,6 +717,10 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     g.x = ws.xh; g.bp = a.w13p; g.bs = a.w13s; g.tiles = ws.tiles;
     g.offsets = ro.offsets; g.counts = ro.counts; g.sorted_slots = ro.sorted_slots;
     g.h_out = ws.h; g.T = d.T; g.H = d.H; g.I = d.I; g.k = d.k; g.K = d.H;
+    // fewer than 32 slots per expert on average: 64-row tiles and the
+    // three-workgroups-per-CU kernel, so the few busy experts of a skewed
+    // routing are spread over twice as many workgroups
+    g.small_rows = small ? 64 : 0;
     g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H / kGroup);
     if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st)) != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
