@@ -10,10 +10,11 @@
 // contraction, so it runs on matrix cores.
 //
 // gfx950 design
-//   * tile 128 rows x 256 weight rows per workgroup, 4 waves each owning all
-//     128 rows x 64 weight rows (v_mfma_f32_32x32x16_f16), K stages of 64;
-//     activations through double-buffered LDS, weights straight into
-//     registers (no LDS, no redundant conversion);
+//   * tile 128 rows (64 when the slots per expert are few) x 256 weight rows
+//     per workgroup, 4 waves each owning all rows x 64 weight rows
+//     (v_mfma_f32_32x32x16_f16), K stages of 64; activations through
+//     double-buffered LDS, read as whole 128-byte lines; INT4 weights through
+//     LDS one 128-wide group at a time, read as whole 64-byte sectors;
 //   * weights are dequantized once per workgroup, in registers, as
 //     fp16 values (code * scale * 2^10): a 4-bit code times a bf16 scale has
 //     at most 11 significant bits, so the value is exact in fp16 (the 2^10
@@ -25,6 +26,8 @@
 //   * nibble pairs (n_j, n_j+4) are formed with one mask, so the 8 K values a
 //     lane holds are in the order 0,4,1,5,2,6,3,7 on both operands (the dot
 //     product does not care);
+//   * the down projection's per-row factors and output rows are placed in
+//     LDS during the K loop, so the epilogue waits on no global load;
 //   * gate and up rows of the same outputs sit in the same wave, so
 //     silu(gate) * up is formed in registers;
 //   * the down projection writes each slot's weighted output (fp16) and a
@@ -32,8 +35,8 @@
 //     fp32-atomic alternative measured about 2x slower on this layer);
 //   * workgroup -> tile order is XCD-aware: the weight-row blocks of one token
 //     tile go to the same XCD back to back, so the gathered activations are
-//     re-read from that XCD's L2, and an expert's token tiles run in pairs on
-//     one XCD, so its weights are read from HBM once per pair.
+//     re-read from that XCD's L2, and an expert's token tiles are dealt to
+//     the XCDs in pairs.
 #include <type_traits>
 
 #include "int6.h"
@@ -161,12 +164,12 @@ __device__ __forceinline__ h2_t scale_pair(uint16_t bf)
 
 // Grouped / dense GEMM.  Workgroup tile: 128 rows (tokens or sorted slots) x
 // 256 weight rows; wave w owns all 128 rows and weight rows [64 w, +64) as two
-// 32-wide MFMA tiles.  Activations go through double-buffered LDS; each lane
-// loads its weight fragments straight from global memory (16 bytes = 32 codes
-// of one row per K stage) and dequantizes them in registers, so every weight
-// byte is read and converted once per workgroup.  Within a 64-wide K stage,
-// MFMA step j uses, on lanes 0-31, octet j and, on lanes 32-63, octet 4 + j:
-// that makes each lane's weight bytes for the stage contiguous.
+// 32-wide MFMA tiles.  Activations go through double-buffered LDS.  INT4
+// weights go through LDS a 128-wide K group at a time (below); INT6 weights
+// are loaded by each lane straight from global memory.  Either way every
+// weight byte is read and converted once per workgroup.  Within a 64-wide K
+// stage, MFMA step j uses, on lanes 0-31, octet j and, on lanes 32-63,
+// octet 4 + j.
 //
 // MAXMA is the most 32-row tiles a workgroup takes: 4 (the 128-row tile, two
 // workgroups per CU), or 2 for routed tiles of at most 64 rows, which then
