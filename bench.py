@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="decode1", choices=sorted(CONFIGS))
     p.add_argument("--layers", type=int, default=0, help="resident layers (0: config default)")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="tokens per step (0: config default); for sweeps over the batch size")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -130,6 +132,8 @@ def main():
     cfg = dict(CONFIGS[args.config])
     if args.layers:
         cfg["layers"] = args.layers
+    if args.tokens:
+        cfg["tokens"] = args.tokens
     T, L = cfg["tokens"], cfg["layers"]
     shape = synth.LayerShape(tokens=T)
     H, E, I, k = shape.hidden, shape.experts, shape.inter, shape.top_k
