@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_forward.argtypes = ([_ptr] * 6 + [_c_i64] * 6 + [_ptr] * 5 + [_c_i64] * 3
                                      + [_ptr, _ptr, _ptr, _ptr, _ptr, ctypes.c_int])
         L.oracle_quantize_int4.argtypes = [_ptr, _c_i64, _c_i64, _c_i64, _ptr, _ptr, _ptr, _ptr]
+        L.oracle_int8_code.restype = ctypes.c_int
+        L.oracle_int8_code.argtypes = [_ptr, _c_i64]
+        L.oracle_int8_linear.argtypes = [_ptr, _ptr, _ptr] + [_c_i64] * 4 + [_ptr]
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +140,31 @@ def quantize_int4(w: np.ndarray, group: int = 128):
     e2 = np.empty((rows, K // group), np.float32)
     lib().oracle_quantize_int4(_p(w), rows, K, group, _p(packed), _p(scales), _p(e1), _p(e2))
     return packed, scales, e1, e2
+
+
+def int8_code(row_words: np.ndarray, k: int) -> int:
+    w = _c(row_words, np.int32)
+    return int(lib().oracle_int8_code(_p(w), k))
+
+
+def int8_linear(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, group: int) -> np.ndarray:
+    """x bf16-bits uint16 [T, K], packed int32 [N, K/4], scales uint16
+    [N, K/group] -> fp64 [T, N] = x . dequant(W)^T, exact up to fp64 sums.
+
+    INT8 pack-quantized words ("Running 125B MoE on Three 3090s - vLLM
+    Optimization Edition", section 3.3, "Hyper-connection (decode-04)"),
+    symmetric groups of 64 or 128 (model card "What is quantized", groups C
+    and D)."""
+    x = _c(x, np.uint16)
+    p = _c(packed, np.int32)
+    s = _c(scales, np.uint16)
+    T, K = x.shape
+    N = p.shape[0]
+    if p.shape[1] * 4 != K or s.shape != (N, K // group) or K % group:
+        raise ValueError("inconsistent INT8 linear shapes")
+    y = np.empty((T, N), np.float64)
+    lib().oracle_int8_linear(_p(x), _p(p), _p(s), T, N, K, group, _p(y))
+    return y
 
 
 def router_logits(x: np.ndarray, router_w: np.ndarray) -> np.ndarray:

@@ -521,6 +521,42 @@ void oracle_quantize_int4(const uint16_t *w, int64_t rows, int64_t K, int64_t gr
     }
 }
 
+/* ---------------------------------------------------------------------
+ * INT8 W8A16 linear layer ([VO] decode-04: four codes per 32-bit word,
+ * least significant byte first, each stored as value + 128; [MC] groups C
+ * and D: symmetric, group 64 for the hyper-connection mixers, group 128 for
+ * lm_head and the embeddings)
+ * ------------------------------------------------------------------- */
+
+/* Signed INT8 code of element k of one packed row. */
+int oracle_int8_code(const int32_t *row_words, int64_t k)
+{
+    uint32_t word = (uint32_t)row_words[k / 4];
+    int byte = (int)((word >> (8 * (k % 4))) & 0xFFu);
+    return byte - 128;
+}
+
+/* y[t][n] = sum_k x[t][k] * code[n][k] * scale[n][k / group], in fp64, one
+ * output at a time (x bf16 [T][K], packed [N][K/4], scales bf16
+ * [N][K/group]).  Not rounded: the comparison is made against the exact
+ * value. */
+void oracle_int8_linear(const uint16_t *x, const int32_t *packed, const uint16_t *scales,
+                        int64_t T, int64_t N, int64_t K, int64_t group, double *y)
+{
+    int64_t tn;
+#pragma omp parallel for schedule(static)
+    for (tn = 0; tn < T * N; ++tn) {
+        int64_t t = tn / N, n = tn % N;
+        const int32_t *row = packed + n * (K / 4);
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double w = (double)oracle_int8_code(row, k) * bf16_to_double(scales[n * (K / group) + k / group]);
+            acc += bf16_to_double(x[t * K + k]) * w;
+        }
+        y[t * N + n] = acc;
+    }
+}
+
 /* Threads the OpenMP runtime will use by default (for reporting). */
 int oracle_max_threads(void)
 {

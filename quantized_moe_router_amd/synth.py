@@ -77,6 +77,28 @@ def make_dense_weights(rows: int, cols: int, seed: int, std: float = 0.02,
     return bf16_bits(w)
 
 
+# INT8 W8A16 linear layers: the hyper-connection low-rank mixers (down
+# [320, 10240] and up [10240, 320], group 64) and lm_head ([248320, 2560],
+# group 128).  Packed int32 [N, K/4], four codes per word, least significant
+# byte first, each stored as code + 128: random words are uniform codes in
+# [-128, 127].  Scales bf16(|N(0,1)| * 0.0004), about amax / 127 of an
+# N(0, 0.02) weight group; activations bf16(N(0, 1)).
+INT8_SCALE_STD = 0.0004
+
+
+def make_int8_linear(tokens: int, n: int, k: int, group: int, seed: int = 0,
+                     x_seed: int | None = None) -> dict:
+    """Host INT8 linear layer {x, packed, scales, group}; the weights come from
+    `seed`, the activations from `x_seed` (default seed + 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    packed = _words(rng, (n, k // 4))
+    scales = bf16_bits(np.abs(rng.standard_normal((n, k // group), dtype=np.float32))
+                       * np.float32(INT8_SCALE_STD))
+    xrng = np.random.Generator(np.random.PCG64(seed + 1 if x_seed is None else x_seed))
+    x = bf16_bits(xrng.standard_normal((tokens, k), dtype=np.float32))
+    return {"x": x, "packed": packed, "scales": scales, "group": group}
+
+
 def make_weights(shape: LayerShape, seed: int = 0) -> dict:
     """Router and expert weights of one layer (independent of the token count)."""
     H, E, I, G = shape.hidden, shape.experts, shape.inter, shape.group

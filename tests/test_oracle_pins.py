@@ -505,3 +505,85 @@ def test_quantizer_zero_group_and_packing():
     assert np.all(_unpack_codes(packed)[1, 128:] == 7)
     assert np.all(packed[1, 16:] == -1)
     assert float(_bits_to_float(scales[1, 1])) == float(_bits_to_float(_to_bf16_bits(np.float32(0.25) * np.float32(1.0 / 7.0))))
+
+
+# ---- INT8 W8A16 linear ([VO] decode-04 layout; [MC] groups C and D) ----
+
+def _int8_bytes_view(packed):
+    """The page's observation about the layout: the int32 words viewed as
+    little-endian bytes already are the codes + 128, row by row."""
+    N = packed.shape[0]
+    return packed.astype("<i4").view(np.uint8).reshape(N, -1).astype(np.int64) - 128
+
+
+def test_int8_word_hand_example():
+    g = _golden("int8_words.json")
+    word = np.array([np.uint32(int(g["word"], 16))], np.uint32).view(np.int32)
+    assert [oracle.int8_code(word, k) for k in range(4)] == g["codes"]
+    packed = np.full((1, 16), np.uint32(0x80808080).view(np.int32), np.int32)
+    packed[0, 0] = word[0]
+    x = np.zeros((1, 64), np.float32)
+    x[0, :4] = g["x"]
+    x16 = np.array([_bf16(float(v)) for v in x[0]], np.uint16)[None, :]
+    scales = np.array([[g["scale_bits"]]], np.uint16)
+    y = oracle.int8_linear(x16, packed, scales, 64)
+    assert y.shape == (1, 1) and y[0, 0] == g["output"]
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_int8_linear_matches_byte_view_matmul(group):
+    # dequantized through the byte view (not the oracle's shifts), then a
+    # library matmul in float64
+    rng = np.random.default_rng(7)
+    T, N, K = 3, 5, 384
+    packed = rng.integers(0, 2**32, size=(N, K // 4), dtype=np.uint32).view(np.int32)
+    scales = (np.abs(rng.standard_normal((N, K // group))) * 0.01).astype(np.float32)
+    s16 = torch.from_numpy(scales).to(torch.bfloat16)
+    x16 = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16)
+    W = _int8_bytes_view(packed) * np.repeat(s16.double().numpy(), group, axis=1)
+    ref = x16.double().numpy() @ W.T
+    y = oracle.int8_linear(x16.view(torch.int16).numpy().view(np.uint16), packed,
+                           s16.view(torch.int16).numpy().view(np.uint16), group)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_int8_linear_group_index(group):
+    # only group g of each row has a non-zero scale: the output is that
+    # slice's integer dot product times the scale (exact), so a wrong group
+    # index or a transposed operand fails
+    rng = np.random.default_rng(11)
+    T, N, K = 2, 4, 4 * group
+    packed = rng.integers(0, 2**32, size=(N, K // 4), dtype=np.uint32).view(np.int32)
+    codes = _int8_bytes_view(packed)
+    xi = rng.integers(-3, 4, size=(T, K))
+    x16 = np.array([[_bf16(float(v)) for v in row] for row in xi], np.uint16)
+    for g in range(K // group):
+        scales = np.zeros((N, K // group), np.uint16)
+        scales[:, g] = _bf16(0.25)
+        y = oracle.int8_linear(x16, packed, scales, group)
+        sl = slice(g * group, (g + 1) * group)
+        expect = (xi[:, sl] @ codes[:, sl].T) * 0.25   # integers: exact
+        assert np.array_equal(y, expect.astype(np.float64))
+
+
+def test_int8_linear_extreme_codes_and_linearity():
+    # all codes -128 (bytes 0x00) or all 127 (0xFF): closed forms; doubling
+    # every scale doubles the output exactly
+    K, group = 128, 64
+    x16 = np.array([[_bf16(1.0)] * K, [_bf16(-2.0)] * K], np.uint16)
+    lo = np.zeros((1, K // 4), np.int32)
+    hi = np.full((1, K // 4), -1, np.int32)
+    s = np.full((1, K // group), _bf16(2.0 ** -7), np.uint16)
+    y_lo = oracle.int8_linear(x16, lo, s, group)
+    y_hi = oracle.int8_linear(x16, hi, s, group)
+    assert y_lo[0, 0] == -128 * K * 2.0 ** -7 and y_lo[1, 0] == 256 * K * 2.0 ** -7
+    assert y_hi[0, 0] == 127 * K * 2.0 ** -7 and y_hi[1, 0] == -254 * K * 2.0 ** -7
+    rng = np.random.default_rng(3)
+    packed = rng.integers(0, 2**32, size=(6, K // 4), dtype=np.uint32).view(np.int32)
+    sc = np.array([[_bf16(2.0 ** -int(e)) for e in row] for row in rng.integers(6, 12, size=(6, K // group))],
+                  np.uint16)
+    x = np.array([[_bf16(float(v)) for v in row] for row in rng.integers(-8, 9, size=(3, K))], np.uint16)
+    y1 = oracle.int8_linear(x, packed, sc, group)
+    y2 = oracle.int8_linear(x, packed, (sc + 0x80).astype(np.uint16), group)   # exponent + 1
+    assert np.array_equal(y2, 2 * y1)
