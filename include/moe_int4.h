@@ -169,6 +169,36 @@ int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
 int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t group,
                           int32_t *packed, uint16_t *scales, void *hip_stream);
 
+/* INT8 W8A16 linear layer ("Running 125B MoE on Three 3090s - vLLM
+ * Optimization Edition", section 3.3, "Hyper-connection (decode-04)": the
+ * INT8 pack-quantized weight holds four codes per int32 word, least
+ * significant byte first, each stored as code + 128, and is read in place;
+ * model card "What is quantized", groups C and D: symmetric, group 64 for the
+ * hyper-connection low-rank mixers, 128 for lm_head):
+ *   x         bf16  [tokens][k]        in   activations
+ *   w_packed  int32 [n][k/4]           in   byte j of word i of row r is the
+ *                                           code of input 4 i + j, plus 128
+ *   w_scales  bf16  [n][k/group]       in   one per (row, group of inputs)
+ *   out       bf16  [tokens][n]        out  overwritten; must not alias x
+ * out[t][r] = bf16(sum_i x[t][i] * (byte[r][i] - 128) * scale[r][i / group]),
+ * accumulated in fp32 and rounded once (to nearest even).  Activations are
+ * taken as fp16 (exact for finite bf16 values of magnitude 2^-14 .. 65504;
+ * smaller ones lose low bits, larger ones saturate).  At most 4 tokens with
+ * tokens * k <= 32768 run as a GEMV; more run as a matrix-core GEMM whose
+ * K may be split over workgroups, the fp32 partials then living in the
+ * caller's workspace and being summed in a fixed order (the result does not
+ * depend on the split schedule's timing).  group is 64 or 128, k a multiple
+ * of it (at most 65536), n in [1, 2^24], tokens in [0, 2^20] with tokens * n
+ * and tokens * k below 2^31; tokens = 0 is a no-op.  Pointers must be
+ * 16-byte aligned; the workspace may be NULL when
+ * moe_int8_linear_workspace_bytes reports 0 for the same shape.
+ * Asynchronous on hip_stream; no allocation, no host synchronisation. */
+int32_t moe_int8_linear_workspace_bytes(int32_t tokens, int32_t n, int32_t k, int32_t group,
+                                        size_t *bytes);
+int32_t moe_int8_linear(const uint16_t *x, const int32_t *w_packed, const uint16_t *w_scales,
+                        int32_t tokens, int32_t n, int32_t k, int32_t group, uint16_t *out,
+                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Message for the calling thread's most recent failing call ("" if none). */
 const char *moe_int4_last_error(void);
 

@@ -53,10 +53,13 @@ def lib() -> ctypes.CDLL:
         L.moe_int4_forward.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P]
         L.moe_int4_forward_traced.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P, P]
         L.moe_int4_quantize.argtypes = [P, _c_i32, _c_i32, _c_i32, P, P, P]
+        L.moe_int8_linear_workspace_bytes.argtypes = [_c_i32] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_int8_linear.argtypes = [P, P, P] + [_c_i32] * 4 + [P, P, ctypes.c_size_t, P]
         L.moe_int4_last_error.restype = ctypes.c_char_p
         L.moe_int4_version.restype = ctypes.c_char_p
         for f in ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts", "moe_int4_forward",
-                  "moe_int4_forward_traced", "moe_int4_quantize"):
+                  "moe_int4_forward_traced", "moe_int4_quantize", "moe_int8_linear_workspace_bytes",
+                  "moe_int8_linear"):
             getattr(L, f).restype = _c_i32
         _lib = L
     return _lib
@@ -64,6 +67,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts",
             "moe_int4_forward", "moe_int4_forward_traced", "moe_int4_quantize",
+            "moe_int8_linear_workspace_bytes", "moe_int8_linear",
             "moe_int4_last_error", "moe_int4_version")
 
 
@@ -152,6 +156,22 @@ def moe_int4_quantize(w, rows: int, cols: int, packed, scales, group: int = 128,
     """w bf16 [rows, cols] (device) -> packed int32 [rows, cols/8], scales bf16 [rows, cols/group]."""
     _check(lib().moe_int4_quantize(_ptr(w), int(rows), int(cols), int(group), _ptr(packed),
                                    _ptr(scales), _stream(stream)))
+
+
+def moe_int8_linear_workspace_bytes(tokens: int, n: int, k: int, group: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().moe_int8_linear_workspace_bytes(int(tokens), int(n), int(k), int(group), ctypes.byref(b)))
+    return b.value
+
+
+def moe_int8_linear(x, w_packed, w_scales, tokens: int, n: int, k: int, group: int, out,
+                    workspace=None, stream=None):
+    """x bf16 [tokens, k], w_packed int32 [n, k/4], w_scales bf16 [n, k/group] ->
+    out bf16 [tokens, n] (device tensors; workspace uint8, may be None when the
+    shape needs none)."""
+    _check(lib().moe_int8_linear(_ptr(x), _ptr(w_packed), _ptr(w_scales), int(tokens), int(n), int(k),
+                                 int(group), _ptr(out), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream(stream)))
 
 
 def version() -> str:

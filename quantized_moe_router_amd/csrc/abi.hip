@@ -200,6 +200,21 @@ int32_t launched(hipError_t e, const char *what)
     return MOE_INT4_OK;
 }
 
+int32_t check_int8_shape(int32_t tokens, int32_t n, int32_t k, int32_t group)
+{
+    if (group != 64 && group != 128)
+        return fail(MOE_INT4_EINVAL, "group=%d, INT8 supports 64 and 128", group);
+    if (tokens < 0 || tokens > (1 << 20))
+        return fail(MOE_INT4_EINVAL, "tokens=%d outside [0, 1048576]", tokens);
+    if (n <= 0 || n > (1 << 24))
+        return fail(MOE_INT4_EINVAL, "n=%d outside [1, 16777216]", n);
+    if (k <= 0 || k % group || k > 65536)
+        return fail(MOE_INT4_EINVAL, "k=%d must be a positive multiple of group=%d, at most 65536", k, group);
+    if ((long long)tokens * n >= (1LL << 31) || (long long)tokens * k >= (1LL << 31))
+        return fail(MOE_INT4_EINVAL, "tokens * n and tokens * k must stay below 2^31");
+    return MOE_INT4_OK;
+}
+
 }  // namespace
 
 size_t workspace_size(const Dims &d) { return layout(d).total; }
@@ -363,6 +378,40 @@ int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t
     if ((rc = check_device())) return rc;
     return launched(launch_quantize_int4(w, rows, cols, packed, scales, (hipStream_t)hip_stream),
                     "quantize");
+}
+
+int32_t moe_int8_linear_workspace_bytes(int32_t tokens, int32_t n, int32_t k, int32_t group,
+                                        size_t *bytes)
+{
+    g_error.clear();
+    int32_t rc = check_int8_shape(tokens, n, k, group);
+    if (rc) return rc;
+    if (!bytes) return fail(MOE_INT4_EINVAL, "bytes is NULL");
+    *bytes = int8_plan(tokens, n, k, group).part_bytes;
+    return MOE_INT4_OK;
+}
+
+int32_t moe_int8_linear(const uint16_t *x, const int32_t *w_packed, const uint16_t *w_scales,
+                        int32_t tokens, int32_t n, int32_t k, int32_t group, uint16_t *out,
+                        void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    g_error.clear();
+    int32_t rc = check_int8_shape(tokens, n, k, group);
+    if (rc) return rc;
+    if (tokens == 0) return MOE_INT4_OK;
+    rc = check_ptrs({{"x", x}, {"w_packed", w_packed}, {"w_scales", w_scales}, {"out", out}});
+    if (rc) return rc;
+    const size_t need = int8_plan(tokens, n, k, group).part_bytes;
+    if (need) {
+        if (!workspace) return fail(MOE_INT4_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+        if (!aligned16(workspace)) return fail(MOE_INT4_EALIGN, "workspace is not 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(MOE_INT4_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    }
+    if ((rc = check_device())) return rc;
+    return launched(launch_int8_linear(x, w_packed, w_scales, tokens, n, k, group, out, workspace,
+                                       (hipStream_t)hip_stream),
+                    "int8 linear");
 }
 
 }  // extern "C"

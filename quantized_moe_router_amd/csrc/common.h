@@ -414,4 +414,24 @@ struct ExpertArgs {
 hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
                                   const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid);
 
+// ---------------------------------------------------------------------------
+// INT8 W8A16 linear layer (int8_linear.hip)
+// ---------------------------------------------------------------------------
+constexpr int kInt8GemvMaxTokens = 4;          // GEMV up to this many tokens, GEMM above
+constexpr size_t kInt8GemvMaxLds = 65536;      // GEMV keeps T x K fp16 activations in LDS
+constexpr int kInt8GemvMaxBlocks = 2048;       // persistent GEMV grid (8 per CU)
+constexpr long kInt8GemmTargetTiles = 256;     // K is split until about this many workgroups
+constexpr int kInt8MinSplitK = 256;            // shortest K range of one split
+constexpr int kInt8MaxSplitK = 16;
+
+struct Int8Plan {
+    bool gemv;
+    int mtiles, ntiles, ksplit, kslice;
+    size_t pstride;      // floats per split in the partials (T * N rounded up to 4)
+    size_t part_bytes;   // fp32 split-K partials (workspace)
+};
+Int8Plan int8_plan(int T, int N, int K, int G);
+hipError_t launch_int8_linear(const uint16_t *x, const int32_t *wq, const uint16_t *ws, int T, int N,
+                              int K, int G, uint16_t *out, void *workspace, hipStream_t st);
+
 }  // namespace moe

@@ -1,0 +1,504 @@
+// INT8 W8A16 linear layer:
+//   y[t][n] = bf16( sum_k x[t][k] * (q[n][k] - 128) * s[n][k / G] ),
+// fp32 accumulation, one bf16 rounding (round to nearest even) per output.
+//
+// Method ("Running 125B MoE on Three 3090s - vLLM Optimization Edition",
+// section 3.3, "Hyper-connection (decode-04)": an INT8 pack-quantized weight
+// holds four codes per 32-bit word, least significant byte first, each stored
+// as code + 128, so the word array viewed as bytes already is the stored code
+// matrix and is read in place, with no repack; a GEMV serves a few tokens and
+// a W8A16 GEMM serves more.  Model card "What is quantized", groups C and D:
+// symmetric groups of 64 (hyper-connection low-rank mixers) and 128 (lm_head,
+// embeddings).)
+//
+// gfx950 design
+//   * codes become exact fp16 values with one byte permute per pair: fp16
+//     0x6400 is 1024 with mantissa step 1, so the stored byte placed in the
+//     low mantissa byte reads 1024 + q, and one packed fp16 add of -1152
+//     leaves q - 128 (every integer of magnitude <= 2048 is exact in fp16);
+//   * activations are fp16 (bf16 inputs convert exactly in fp16's normal
+//     range; the conversion saturates outside it, as in the expert GEMMs);
+//   * the scale is applied in fp32 to a partial sum that covers one group
+//     only, so code * x products are exact and nothing is rounded before the
+//     fp32 accumulator: no dequantized weight is ever formed;
+//   * few tokens (GEMV): x sits in LDS; a wave streams four weight rows at a
+//     time, every lane on the same 16-byte column chunk of the four rows, so
+//     one LDS read of x serves four rows; rows are spread over the waves of
+//     a persistent grid; per-lane sums are reduced across the wave by
+//     halving exchanges that leave one (row, token) result per lane group;
+//   * many tokens (GEMM): 128 tokens x 128 weight rows per workgroup, each
+//     wave all tokens x 32 weight rows (v_mfma_f32_32x32x16_f16); a group's
+//     MFMA sums start from zero and are folded into the accumulator with the
+//     group's scale (one FMA per output and group); K is split over
+//     workgroups when the output tiles alone would leave the chip idle, with
+//     fp32 partials summed in a fixed order (deterministic).
+#include <type_traits>
+
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Stored bytes 2i and 2i+1 of a word -> fp16 pair (q - 128), exact.  The
+// permute takes result bytes from {0x64646464 (bytes 4-7), w (bytes 0-3)}.
+template <int I>
+__device__ __forceinline__ h2_t code_pair(uint32_t w)
+{
+    constexpr uint32_t sel = I == 0 ? 0x04010400u : 0x04030402u;
+    const uint32_t p = __builtin_amdgcn_perm(0x64646464u, w, sel);
+    return __builtin_bit_cast(h2_t, p) + h2_t{(_Float16)-1152.f, (_Float16)-1152.f};
+}
+
+// 8 bf16 (natural order) -> 8 fp16 (natural order); exact in fp16's normal
+// range, toward zero outside it (saturating at 65504).
+__device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t v)
+{
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(v[j]), bf16_hi(v[j])));
+    return o;
+}
+
+__device__ __forceinline__ float xor_shfl(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// ---------------------------------------------------------------------------
+// GEMV (T <= kInt8GemvMaxTokens)
+// ---------------------------------------------------------------------------
+constexpr int kGvThreads = 256;
+constexpr int kGvRows = 4;   // weight rows per wave block
+
+// Sum v[0..M) over the 64 lanes of a wave.  Each halving step sends the half
+// of the values this lane gives up to its partner and keeps the other half,
+// so after log2(M) steps lane l holds one value, index l >> (6 - log2 M),
+// summed over the lanes that share those bits; plain exchanges over the
+// remaining bits finish the sum.
+template <int M>
+__device__ __forceinline__ float wave_transpose_sum(float (&v)[M], int lane)
+{
+    static_assert(M >= 1 && M <= 64 && (M & (M - 1)) == 0, "power of two");
+    constexpr int kSteps = M == 1 ? 0 : M == 2 ? 1 : M == 4 ? 2 : M == 8 ? 3 : M == 16 ? 4 : M == 32 ? 5 : 6;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+        const int h = (M >> st) / 2, bit = 32 >> st;
+        // the choice is made on the values' bits (a select of two array
+        // elements would otherwise become a select of their addresses, which
+        // moves the array to scratch memory)
+        const uint32_t m = (lane & bit) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int j = 0; j < M / 2; ++j) {
+            if (j < h) {
+                const uint32_t lo = __float_as_uint(v[j]), hi = __float_as_uint(v[j + h]);
+                const float give = __uint_as_float((lo & m) | (hi & ~m));
+                const float keep = __uint_as_float((hi & m) | (lo & ~m));
+                v[j] = keep + xor_shfl(give, bit);
+            }
+        }
+    }
+    float s = v[0];
+#pragma unroll
+    for (int bit = 32 / M; bit >= 1; bit >>= 1) s += xor_shfl(s, bit);
+    return s;
+}
+
+template <int T>
+__global__ __launch_bounds__(kGvThreads) void int8_gemv_kernel(const uint16_t *__restrict__ x,
+                                                               const int32_t *__restrict__ wq,
+                                                               const uint16_t *__restrict__ wscale,
+                                                               int N, int K, int gshift,
+                                                               uint16_t *__restrict__ out)
+{
+    // x as fp16 in LDS: chunk c (16 inputs) of token t is split into two
+    // planes of 8 inputs, [t][p][c], so the 16-byte reads of consecutive
+    // lanes are consecutive (no bank conflicts)
+    extern __shared__ u32x4_t s_x[];
+    const int CPR = K >> 4;   // 16-input chunks per row
+    for (int i = threadIdx.x; i < T * CPR * 2; i += kGvThreads) {
+        const int t = i / (2 * CPR), r = i - t * 2 * CPR, c = r >> 1, p = r & 1;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(x + (size_t)t * K + 16 * c + 8 * p);
+        s_x[(t * 2 + p) * CPR + c] = bf16x8_to_f16x8(v);
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (kGvThreads / 64) + (threadIdx.x >> 6);
+    const int W = gridDim.x * (kGvThreads / 64);
+    const int nrb = (N + kGvRows - 1) / kGvRows;
+    if (gw >= nrb) return;
+    const int NI = (CPR + 63) >> 6;                   // column passes per row block
+    const int my_blocks = (nrb - gw + W - 1) / W;
+    const int U = my_blocks * NI;                     // (row block, pass) units of this wave
+    const size_t rstride = (size_t)K / 4;             // words per row
+    const int nsc = K >> gshift;                      // scales per row
+
+    // one unit's raw weights and scales
+    struct Raw {
+        u32x4_t w[kGvRows];
+        uint16_t s[kGvRows];
+    };
+    auto load = [&](int u, Raw &r) {
+        const int b = u / NI, i = u - b * NI;
+        const int rb = gw + b * W;
+        const int c = min(i * 64 + lane, CPR - 1);   // a lane past the row re-reads a valid chunk
+#pragma unroll
+        for (int j = 0; j < kGvRows; ++j) {
+            const int row = min(rb * kGvRows + j, N - 1);
+            r.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(wq + row * rstride) + c);
+            r.s[j] = wscale[(size_t)row * nsc + ((16 * c) >> gshift)];
+        }
+    };
+
+    constexpr int M = T == 1 ? 4 : T == 2 ? 8 : 16;   // kGvRows * T, padded to a power of two
+    float acc[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) acc[j] = 0.f;
+
+    auto compute = [&](int u, const Raw &r) {
+        const int b = u / NI, i = u - b * NI;
+        const int c0 = i * 64 + lane, c = min(c0, CPR - 1);
+        const bool valid = c0 < CPR;
+        h2_t xv[T][8];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const u32x4_t v = s_x[(t * 2 + p) * CPR + c];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // element copied out first: a bit cast of a vector
+                    // element itself reads the vector's first element
+                    const uint32_t e = v[q];
+                    xv[t][4 * p + q] = __builtin_bit_cast(h2_t, e);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kGvRows; ++j) {
+            h2_t cp[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cp[2 * q] = code_pair<0>(r.w[j][q]);
+                cp[2 * q + 1] = code_pair<1>(r.w[j][q]);
+            }
+            const float sf = valid ? bf16_to_f32(r.s[j]) : 0.f;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float p = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) p = __builtin_amdgcn_fdot2(cp[q], xv[t][q], p, false);
+                acc[j * T + t] = fmaf(sf, p, acc[j * T + t]);
+            }
+        }
+        if (i == NI - 1) {
+            // row block done: reduce over the wave and store
+            const float s = wave_transpose_sum<M>(acc, lane);
+            constexpr int shift = M == 4 ? 4 : M == 8 ? 3 : 2;   // 6 - log2 M
+            const int idx = lane >> shift;
+            const int j = idx / T, t = idx - j * T;
+            const int row = (gw + b * W) * kGvRows + j;
+            if ((lane & ((1 << shift) - 1)) == 0 && idx < kGvRows * T && row < N)
+                out[(size_t)t * N + row] = (uint16_t)f32_to_bf16(s);
+#pragma unroll
+            for (int q = 0; q < M; ++q) acc[q] = 0.f;
+        }
+    };
+
+    // two explicit register sets, the next unit's loads in flight while the
+    // current one is computed
+    Raw r0, r1;
+    load(0, r0);
+    int u = 0;
+    for (; u + 1 < U; u += 2) {
+        load(u + 1, r1);
+        compute(u, r0);
+        if (u + 2 < U) load(u + 2, r0);
+        compute(u + 1, r1);
+    }
+    if (u < U) compute(u, r0);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM (MFMA)
+// ---------------------------------------------------------------------------
+constexpr int kGmM = 128;           // tokens per tile
+constexpr int kGmN = 128;           // weight rows per tile (4 waves x 32)
+constexpr int kGmKS = 64;           // K per stage
+constexpr int kGmLds = kGmKS + 8;   // padded LDS row (fp16 elements)
+constexpr int kGmThreads = 256;
+
+struct Int8GemmArgs {
+    const uint16_t *x;        // bf16 [T][K]
+    const int32_t *wq;        // [N][K/4]
+    const uint16_t *ws;       // bf16 [N][K/G]
+    uint16_t *out;            // bf16 [T][N] (one K split)
+    float *part;              // fp32 [ksplit][pstride] (several K splits)
+    size_t pstride;           // T * N rounded up to a multiple of 4
+    int T, N, K, gshift;
+    int mtiles, ntiles, ksplit, kslice;
+};
+
+// Tile: 128 tokens x 128 weight rows, K range [k0, k0 + len).  Wave w owns
+// all tokens x weight rows [32 w, +32) of the tile as up to four 32 x 32
+// MFMA tiles.  Within a 64-wide K stage, MFMA step j uses on lanes 0-31
+// inputs 8 j .. 8 j + 7 and on lanes 32-63 inputs 32 + 8 j .., for both
+// operands, so each lane reads 32 contiguous bytes of its weight row per
+// stage.  GS = G / 64 stages make up one scale group.
+template <int GS>
+__global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g)
+{
+    __shared__ __align__(16) _Float16 s_a[2][kGmM * kGmLds];
+
+    // ---- tile (XCD-aware: each XCD takes a contiguous range of tiles, the
+    // weight-row tiles of one token tile and K split back to back, so the
+    // token tile is re-read from that XCD's L2) ----
+    const int per = gridDim.x >> 3;
+    const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (tile >= g.mtiles * g.ntiles * g.ksplit) return;
+    const int nt_i = tile % g.ntiles, rest = tile / g.ntiles;
+    const int mt_i = rest % g.mtiles, split = rest / g.mtiles;
+    const int m0 = mt_i * kGmM, n0 = nt_i * kGmN;
+    const int rows = min(kGmM, g.T - m0);
+    const int k0 = split * g.kslice, len = min(g.kslice, g.K - k0);
+    const int nsteps = len / kGmKS;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+
+    // ---- activation staging: thread -> 16-byte chunk c8 of rows r8 + 32 o;
+    // rows past T read row 0 of the tile (never stored) ----
+    const int c8 = tid & 7, r8 = tid >> 3;
+    const uint16_t *asrc[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        const int row = r8 + 32 * o;
+        asrc[o] = g.x + (size_t)(m0 + (row < rows ? row : 0)) * g.K + k0 + 8 * c8;
+    }
+    u32x4_t ra[2][4];
+
+    // ---- weights: lane -> row n0 + 32 wave + lane % 32 (clamped to N - 1),
+    // bytes [32 half, +32) of each stage ----
+    const int n = n0 + 32 * wave + (lane & 31);
+    const int nrow = min(n, g.N - 1);
+    const u32x4_t *bsrc = reinterpret_cast<const u32x4_t *>(g.wq + (size_t)nrow * (g.K / 4) + k0 / 4) + 2 * half;
+    const uint16_t *ssrc = g.ws + (size_t)nrow * (g.K >> g.gshift) + (k0 >> g.gshift);
+    u32x4_t rb[2][2];
+    uint16_t rs[2];
+
+    f32x16_t acc[4], tmp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+    const int mtiles = (rows + 31) / 32;
+
+    auto kloop = [&](auto ma_c) {
+        constexpr int MA = decltype(ma_c)::value;
+        auto load_a = [&](int s, int p) {
+#pragma unroll
+            for (int o = 0; o < MA; ++o) ra[p][o] = *reinterpret_cast<const u32x4_t *>(asrc[o] + s * kGmKS);
+        };
+        auto store_a = [&](int buf, int p) {
+#pragma unroll
+            for (int o = 0; o < MA; ++o)
+                *reinterpret_cast<u32x4_t *>(s_a[buf] + (r8 + 32 * o) * kGmLds + 8 * c8) = bf16x8_to_f16x8(ra[p][o]);
+        };
+        auto load_b = [&](int s, int p) {
+            rb[p][0] = bsrc[4 * s];
+            rb[p][1] = bsrc[4 * s + 1];
+            rs[p] = ssrc[(s * kGmKS) >> g.gshift];
+        };
+
+        // stage s (register set q = s % 2, LDS buffer q): stage s+1's
+        // activations are stored, stages s+3 (activations) and s+2
+        // (weights) are loaded
+        auto stage = [&](int s, int q) {
+            if (s + 1 < nsteps) store_a(q ^ 1, q ^ 1);
+            const u32x4_t w0 = rb[q][0], w1 = rb[q][1];
+            const float sf = bf16_to_f32(rs[q]);
+            load_a(min(s + 3, nsteps - 1), q ^ 1);
+            load_b(min(s + 2, nsteps - 1), q);
+            const bool gfirst = (q % GS) == 0, glast = (q % GS) == GS - 1;
+            const _Float16 *A = s_a[q] + (lane & 31) * kGmLds + 32 * half;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t wa = j < 2 ? w0[2 * j] : w1[2 * j - 4];
+                const uint32_t wb = j < 2 ? w0[2 * j + 1] : w1[2 * j - 3];
+                const h2_t p0 = code_pair<0>(wa), p1 = code_pair<1>(wa);
+                const h2_t p2 = code_pair<0>(wb), p3 = code_pair<1>(wb);
+                const f16x8_t bf = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt) {
+                    const f16x8_t af = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kGmLds + 8 * j);
+                    if (gfirst && j == 0) {
+                        const f32x16_t z = {};
+                        tmp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, z, 0, 0, 0);
+                    } else {
+                        tmp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, tmp[mt], 0, 0, 0);
+                    }
+                }
+            }
+            if (glast) {
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mt][v] = fmaf(sf, tmp[mt][v], acc[mt][v]);
+            }
+            __syncthreads();
+        };
+
+        // prologue: stage 0's activations in LDS, stages 1 and 2 in
+        // registers, weights of stages 0 and 1 in flight
+        load_a(0, 0);
+        load_b(0, 0);
+        load_b(min(1, nsteps - 1), 1);
+        load_a(min(1, nsteps - 1), 1);
+        store_a(0, 0);
+        load_a(min(2, nsteps - 1), 0);
+        __syncthreads();
+        int s = 0;
+        for (; s + 1 < nsteps; s += 2) {
+            stage(s, 0);
+            stage(s + 1, 1);
+        }
+        if (s < nsteps) stage(s, 0);
+    };
+    switch (mtiles) {
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    default: kloop(std::integral_constant<int, 4>{}); break;
+    }
+
+    // ---- epilogue: lane holds column n for 16 rows of each row tile ----
+    if (n >= g.N) return;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= mtiles) continue;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int m = 32 * mt + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (m >= rows) continue;
+            const size_t o = (size_t)(m0 + m) * g.N + n;
+            if (g.ksplit == 1) g.out[o] = (uint16_t)f32_to_bf16(acc[mt][j]);
+            else g.part[(size_t)split * g.pstride + o] = acc[mt][j];
+        }
+    }
+}
+
+// out[i] = bf16( sum_s part[s][i] ), splits in order; 4 outputs per thread
+// (pstride is a multiple of 4, so every 16-byte load is aligned).
+__global__ __launch_bounds__(256) void int8_splitk_sum_kernel(const float *__restrict__ part, size_t count,
+                                                              size_t pstride, int ksplit,
+                                                              uint16_t *__restrict__ out)
+{
+    const size_t i = (blockIdx.x * (size_t)blockDim.x + threadIdx.x) * 4;
+    if (i >= count) return;
+    if (i + 4 <= count) {
+        float4 a = *reinterpret_cast<const float4 *>(part + i);
+        for (int s = 1; s < ksplit; ++s) {
+            const float4 b = *reinterpret_cast<const float4 *>(part + (size_t)s * pstride + i);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        const uint32_t lo = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
+        const uint32_t hi = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+        if ((reinterpret_cast<uintptr_t>(out + i) & 7) == 0) {
+            *reinterpret_cast<uint2 *>(out + i) = make_uint2(lo, hi);
+        } else {
+            out[i] = (uint16_t)lo;
+            out[i + 1] = (uint16_t)(lo >> 16);
+            out[i + 2] = (uint16_t)hi;
+            out[i + 3] = (uint16_t)(hi >> 16);
+        }
+        return;
+    }
+    for (size_t e = i; e < count; ++e) {
+        float a = part[e];
+        for (int s = 1; s < ksplit; ++s) a += part[(size_t)s * pstride + e];
+        out[e] = (uint16_t)f32_to_bf16(a);
+    }
+}
+
+}  // namespace
+
+// Launch plan of one call (shared by the workspace query and the launch).
+Int8Plan int8_plan(int T, int N, int K, int G)
+{
+    Int8Plan p{};
+    p.gemv = T <= kInt8GemvMaxTokens && (size_t)T * K * 2 <= kInt8GemvMaxLds;
+    if (p.gemv || T == 0) return p;
+    p.mtiles = (T + kGmM - 1) / kGmM;
+    p.ntiles = (N + kGmN - 1) / kGmN;
+    const int unit = G > kGmKS ? G : kGmKS;   // a K split is whole groups and whole stages
+    const int units = K / unit;
+    const long tiles = (long)p.mtiles * p.ntiles;
+    int ks = 1;
+    if (tiles < kInt8GemmTargetTiles) {
+        ks = (int)((kInt8GemmTargetTiles + tiles - 1) / tiles);
+        const int max_split = units / (kInt8MinSplitK / unit > 0 ? kInt8MinSplitK / unit : 1);
+        ks = ks < max_split ? ks : max_split;
+        ks = ks < kInt8MaxSplitK ? ks : kInt8MaxSplitK;
+        ks = ks > 1 ? ks : 1;
+    }
+    const int per = (units + ks - 1) / ks;
+    p.kslice = per * unit;
+    p.ksplit = (K + p.kslice - 1) / p.kslice;
+    p.pstride = ((size_t)T * N + 3) / 4 * 4;
+    p.part_bytes = p.ksplit > 1 ? (size_t)p.ksplit * p.pstride * 4 : 0;
+    return p;
+}
+
+hipError_t launch_int8_linear(const uint16_t *x, const int32_t *wq, const uint16_t *ws, int T, int N,
+                              int K, int G, uint16_t *out, void *workspace, hipStream_t st)
+{
+    const Int8Plan p = int8_plan(T, N, K, G);
+    const int gshift = G == 64 ? 6 : 7;
+    if (p.gemv) {
+        const int nrb = (N + kGvRows - 1) / kGvRows;
+        const int wpb = kGvThreads / 64;
+        int grid = (nrb + wpb - 1) / wpb;
+        grid = grid < kInt8GemvMaxBlocks ? grid : kInt8GemvMaxBlocks;
+        const size_t lds = (size_t)T * K * 2;
+        switch (T) {
+        case 1: int8_gemv_kernel<1><<<grid, kGvThreads, lds, st>>>(x, wq, ws, N, K, gshift, out); break;
+        case 2: int8_gemv_kernel<2><<<grid, kGvThreads, lds, st>>>(x, wq, ws, N, K, gshift, out); break;
+        case 3: int8_gemv_kernel<3><<<grid, kGvThreads, lds, st>>>(x, wq, ws, N, K, gshift, out); break;
+        default: int8_gemv_kernel<4><<<grid, kGvThreads, lds, st>>>(x, wq, ws, N, K, gshift, out); break;
+        }
+        return hipGetLastError();
+    }
+    Int8GemmArgs a{};
+    a.x = x;
+    a.wq = wq;
+    a.ws = ws;
+    a.out = out;
+    a.part = static_cast<float *>(workspace);
+    a.T = T;
+    a.N = N;
+    a.K = K;
+    a.gshift = gshift;
+    a.mtiles = p.mtiles;
+    a.ntiles = p.ntiles;
+    a.ksplit = p.ksplit;
+    a.kslice = p.kslice;
+    a.pstride = p.pstride;
+    const long tiles = (long)p.mtiles * p.ntiles * p.ksplit;
+    const int grid = (int)((tiles + 7) / 8 * 8);
+    if (G == 64) int8_gemm_kernel<1><<<grid, kGmThreads, 0, st>>>(a);
+    else int8_gemm_kernel<2><<<grid, kGmThreads, 0, st>>>(a);
+    if (p.ksplit > 1) {
+        const size_t count = (size_t)T * N;
+        const size_t threads = (count + 3) / 4;
+        int8_splitk_sum_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a.part, count, p.pstride,
+                                                                                 p.ksplit, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

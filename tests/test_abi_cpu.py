@@ -15,14 +15,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     with open(os.path.join(ROOT, "include", "moe_int4.h")) as f:
         src = f.read()
-    return sorted(set(re.findall(r"\b(moe_int4_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_int[48]_\w+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared()
     assert set(names) >= {"moe_int4_forward", "moe_int4_route", "moe_int4_experts",
-                          "moe_int4_workspace_bytes", "moe_int4_last_error"}
+                          "moe_int4_workspace_bytes", "moe_int4_last_error", "moe_int8_linear",
+                          "moe_int8_linear_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(B.EXPORTED) <= set(names)
@@ -123,3 +124,56 @@ def test_quantize_zero_rows_is_a_no_op_and_null_buffers_rejected():
     assert B.lib().moe_int4_quantize(None, 0, 256, 128, None, None, None) == 0
     rc = B.lib().moe_int4_quantize(None, 2, 256, 128, None, None, None)
     assert rc == B.EINVAL and "w" in B.lib().moe_int4_last_error().decode()
+
+
+# ---- INT8 W8A16 linear ----
+
+def _i8_ws(tokens, n, k, group):
+    b = ctypes.c_size_t(0)
+    rc = B.lib().moe_int8_linear_workspace_bytes(tokens, n, k, group, ctypes.byref(b))
+    return rc, b.value
+
+
+@pytest.mark.parametrize("tokens,n,k,group,msg", [
+    (1, 320, 10240, 32, "group"),
+    (1, 320, 10240, 256, "group"),
+    (1, 320, 10200, 64, "k="),
+    (1, 320, 0, 64, "k="),
+    (1, 320, 131072, 64, "k="),
+    (1, 0, 2560, 128, "n="),
+    (-1, 320, 2560, 128, "tokens"),
+    (1 << 20, 1 << 12, 2560, 128, "2^31"),
+])
+def test_int8_bad_arguments_rejected(tokens, n, k, group, msg):
+    rc, _ = _i8_ws(tokens, n, k, group)
+    assert rc == B.EINVAL and msg in B.lib().moe_int4_last_error().decode()
+    rc = B.lib().moe_int8_linear(None, None, None, tokens, n, k, group, None, None, 0, None)
+    assert rc == B.EINVAL and msg in B.lib().moe_int4_last_error().decode()
+
+
+def test_int8_workspace_plan():
+    # few tokens: GEMV, no workspace; lm_head-like many rows: no K split;
+    # the narrow hyper-connection down projection splits K (fp32 partials)
+    assert _i8_ws(1, 248320, 2560, 128) == (0, 0)
+    assert _i8_ws(4, 320, 2560, 64) == (0, 0)
+    assert _i8_ws(512, 10240, 320, 64) == (0, 0)
+    rc, b = _i8_ws(512, 320, 10240, 64)
+    assert rc == 0 and b > 0 and b % (512 * 320 * 4) == 0 and 2 <= b // (512 * 320 * 4) <= 16
+
+
+def test_int8_zero_tokens_no_op_and_checks_before_device():
+    assert B.lib().moe_int8_linear(None, None, None, 0, 320, 10240, 64, None, None, 0, None) == 0
+    rc = B.lib().moe_int8_linear(None, None, None, 2, 320, 10240, 64, None, None, 0, None)
+    assert rc == B.EINVAL and "x" in B.lib().moe_int4_last_error().decode()
+    fake = 1 << 20   # aligned, never dereferenced: every check runs on the host first
+    rc = B.lib().moe_int8_linear(fake + 8, fake, fake, 2, 320, 2560, 64, fake, None, 0, None)
+    assert rc == B.EALIGN and "x" in B.lib().moe_int4_last_error().decode()
+    rc, need = _i8_ws(512, 320, 10240, 64)
+    rc = B.lib().moe_int8_linear(fake, fake, fake, 512, 320, 10240, 64, fake, None, 0, None)
+    assert rc == B.EINVAL and "workspace" in B.lib().moe_int4_last_error().decode()
+    rc = B.lib().moe_int8_linear(fake, fake, fake, 512, 320, 10240, 64, fake, fake, need - 16, None)
+    assert rc == B.EWORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        rc = B.lib().moe_int8_linear(fake, fake, fake, 512, 320, 10240, 64, fake, fake, need, None)
+        assert rc == B.EDEVICE

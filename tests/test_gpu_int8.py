@@ -1,0 +1,174 @@
+"""GPU parity of the INT8 W8A16 linear layer ("Running 125B MoE on Three
+3090s - vLLM Optimization Edition", section 3.3, "Hyper-connection
+(decode-04)": four codes per int32 word, least significant byte first, each
+stored as code + 128; model card "What is quantized", groups C and D:
+symmetric groups of 64 and 128): the HIP path, through the C ABI, against
+the CPU oracle on the same bytes.
+
+Tolerance, from the arithmetic: the output is one bf16 rounding (relative
+error <= 2^-9) of an fp32 sum of exact code * x products (fp16 activations
+are exact for the N(0, 1) inputs used here, apart from magnitudes below 2^-14
+whose contribution is below 2^-25 each); the fp32 sum order differs from the
+oracle's, an error far below 1e-3 of the output's rms for K <= 65536.  So
+every element must satisfy |gpu - o| <= 2^-8 |o| + 1e-3 rms(o), and the
+aggregate bar of the MoE layer (max error <= 2e-2 rms, sum |err| / sum |o|
+<= 5e-3) holds with room to spare."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_router_amd import _binding as B
+from quantized_moe_router_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    yield
+
+
+def to_dev(layer):
+    x = torch.from_numpy(layer["x"].view(np.int16)).cuda()
+    p = torch.from_numpy(layer["packed"]).cuda()
+    s = torch.from_numpy(layer["scales"].view(np.int16)).cuda()
+    return x, p, s
+
+
+def run(x, p, s, T, N, K, G, out=None):
+    need = B.moe_int8_linear_workspace_bytes(T, N, K, G)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    B.moe_int8_linear(x, p, s, T, N, K, G, out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def as_f64(bits: torch.Tensor) -> np.ndarray:
+    return bits.cpu().view(torch.bfloat16).double().numpy()
+
+
+def compare(g: np.ndarray, o: np.ndarray, label: str):
+    rms = float(np.sqrt(np.mean(o * o)))
+    err = np.abs(g - o)
+    bound = 2.0 ** -8 * np.abs(o) + 1e-3 * rms
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{label}: {len(bad)} outputs off, first {bad[:3].tolist()} "
+                           f"gpu {g[tuple(bad[0])]} oracle {o[tuple(bad[0])]}")
+    assert err.max() <= 2e-2 * rms, label
+    assert err.sum() <= 5e-3 * np.abs(o).sum(), label
+
+
+SMALL = [
+    # (T, N, K, G): GEMV cases (T <= 4, T * K <= 32768)
+    (1, 37, 128, 64),      # ragged row block, one partial column pass
+    (1, 300, 2560, 128),   # lm_head row length: 2.5 passes of 64 chunks
+    (2, 130, 320, 64),     # hyper-connection up row length: 20 of 64 lanes
+    (3, 77, 1152, 128),    # two passes, the second ragged
+    (4, 320, 4096, 64),
+    (4, 64, 8192, 128),    # T * K at the GEMV's LDS limit
+    (1, 9, 64, 64),        # single group
+    # GEMM cases
+    (1, 5, 65536, 64),     # one token past the GEMV's LDS limit: split K, one row tile
+    (5, 200, 640, 64),     # the smallest GEMM token count
+    (33, 129, 1024, 128),  # ragged row and weight-row tiles
+    (130, 333, 1024, 64),
+    (300, 256, 256, 128),
+    (64, 1000, 2560, 128),
+    (200, 96, 4096, 64),   # narrow: split K
+]
+
+
+@pytest.mark.parametrize("T,N,K,G", SMALL)
+def test_int8_linear_small(T, N, K, G):
+    label = f"int8 T={T} N={N} K={K} G={G}"
+    say(label)
+    layer = synth.make_int8_linear(T, N, K, G, seed=T * 1000 + N)
+    g = as_f64(run(*to_dev(layer), T, N, K, G))
+    o = oracle.int8_linear(layer["x"], layer["packed"], layer["scales"], G)
+    compare(g, o, label)
+
+
+@pytest.mark.parametrize("T", [1, 4, 512])
+@pytest.mark.parametrize("which", ["down", "up"])
+def test_int8_hyper_connection_shapes(which, T):
+    # the hyper-connection low-rank mixers: down [320, 10240], up [10240, 320]
+    N, K = (320, 10240) if which == "down" else (10240, 320)
+    label = f"hc {which} T={T}"
+    say(label)
+    layer = synth.make_int8_linear(T, N, K, 64, seed=17 + T)
+    g = as_f64(run(*to_dev(layer), T, N, K, 64))
+    # the oracle on a seeded sample of tokens (all of them below 64)
+    rng = np.random.default_rng(T)
+    toks = np.arange(T) if T <= 64 else np.unique(np.concatenate([[0, T - 1], rng.choice(T, 48, replace=False)]))
+    o = oracle.int8_linear(layer["x"][toks], layer["packed"], layer["scales"], 64)
+    compare(g[toks], o, label)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_int8_lm_head_full_size(T):
+    # lm_head [248320, 2560], group 128: every output against the oracle on
+    # a seeded sample of rows (plus the first and last)
+    N, K, G = 248320, 2560, 128
+    label = f"lm_head T={T}"
+    say(label)
+    layer = synth.make_int8_linear(T, N, K, G, seed=5)
+    g = as_f64(run(*to_dev(layer), T, N, K, G))
+    rng = np.random.default_rng(T)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 4096, replace=False)]))
+    o = oracle.int8_linear(layer["x"], layer["packed"][rows], layer["scales"][rows], G)
+    compare(g[:, rows], o, label)
+    assert np.isfinite(g).all()
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_int8_edge_codes_and_scales(T):
+    # all-(-128) and all-127 rows, zero scales, a zero token, powers of two,
+    # through the GEMV (3 tokens) and the GEMM (40 tokens)
+    N, K, G = 8, 256, 64
+    x = np.zeros((T, K), np.float32)
+    x[0::3] = 1.0
+    x[1::3] = np.tile([1.0, -2.0, 0.5, 4.0], K // 4)
+    layer = {"x": synth.bf16_bits(x)}
+    packed = np.zeros((N, K // 4), np.uint32)
+    packed[1] = 0xFFFFFFFF
+    packed[2] = 0x80808080
+    packed[3] = 0x00FF7F80
+    packed[4:] = np.random.default_rng(1).integers(0, 2**32, size=(N - 4, K // 4), dtype=np.uint32)
+    layer["packed"] = packed.view(np.int32)
+    sc = np.full((N, K // G), 2.0 ** -7, np.float32)
+    sc[5] = 0.0
+    sc[6, 1] = 0.0
+    layer["scales"] = synth.bf16_bits(sc)
+    g = as_f64(run(*to_dev(layer), T, N, K, G))
+    o = oracle.int8_linear(layer["x"], layer["packed"], layer["scales"], G)
+    # every product is a multiple of 2^-8 and every partial sum stays far
+    # below 2^24 of those, so the fp32 sum is exact in any order: the GPU
+    # output must be the oracle value rounded once to bf16
+    assert np.all(np.abs(o) * 2.0 ** 8 < 2.0 ** 24)
+    expect = torch.from_numpy(o).float().to(torch.bfloat16).double().numpy()
+    assert np.array_equal(g, expect), np.argwhere(g != expect)[:5]
+    assert g[0, 1] == 127 * K * 2.0 ** -7 and g[0, 2] == 0.0 and g[0, 5] == 0.0
+
+
+def test_int8_zero_tokens_leaves_output_and_repeat_is_deterministic():
+    T, N, K, G = 512, 320, 10240, 64
+    layer = synth.make_int8_linear(T, N, K, G, seed=3)
+    x, p, s = to_dev(layer)
+    out = torch.full((T, N), 0x1234, dtype=torch.int16, device="cuda")
+    B.moe_int8_linear(x, p, s, 0, N, K, G, out, None)
+    torch.cuda.synchronize()
+    assert bool((out == 0x1234).all())
+    a = run(x, p, s, T, N, K, G)
+    b = run(x, p, s, T, N, K, G)
+    assert torch.equal(a, b)
