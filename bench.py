@@ -1,6 +1,7 @@
 """Benchmark of the INT4 routed-expert MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode1|decode4|decode64|prefill512|prefill8192|quantize64]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config decode1|decode4|decode64|prefill512|prefill8192|quantize64|lmhead1|hc1|hc512]
 
 A step is one forward of the whole layer (router, top-k, permutation, gate/up
 projection with SiLU-gate, down projection with the weighted combine) over one
@@ -46,6 +47,14 @@ CONFIGS = {
     # the load-time quantizer (not the layer): 64 experts' bf16 gate/up and
     # down weights at the real shape per step
     "quantize64": dict(experts=64),
+    # INT8 W8A16 linear layers (not the MoE layer): lm_head [248320, 2560]
+    # group 128 at decode, two resident copies used alternately; the
+    # hyper-connection mixers down [320, 10240] + up [10240, 320] group 64,
+    # rotating over `pairs` resident pairs (96 per token in the model: two
+    # per decoder layer, 48 layers)
+    "lmhead1": dict(kind="int8", tokens=1, n=248320, k=2560, group=128, copies=2),
+    "hc1": dict(kind="int8hc", tokens=1, pairs=96),
+    "hc512": dict(kind="int8hc", tokens=512, pairs=16),
 }
 VALU_PEAK_TOPS = 39.3        # MI355X vector ALU, non-packed fp32 lane operations per second (T)
 
@@ -129,6 +138,8 @@ def main():
     B.lib()
     if args.config == "quantize64":
         return bench_quantize(args)
+    if CONFIGS[args.config].get("kind", "").startswith("int8"):
+        return bench_int8(args)
     cfg = dict(CONFIGS[args.config])
     if args.layers:
         cfg["layers"] = args.layers
@@ -429,6 +440,189 @@ def bench_quantize(args):
                                   "cores": oracle.max_threads(), "kind": "oracle",
                                   "sample": f"{n // (rows * H)} calls on {rows}x{H} weights of the same "
                                             f"distribution (host-generated), {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_int8(args):
+    """INT8 W8A16 linear layers.  A step is one lm_head projection (lmhead1)
+    or one hyper-connection mixer pair, down then up, the down output being
+    the up input (hc1, hc512), over T tokens.  Weights are generated on the
+    device (uniform random words: uniform codes; bf16 scales |N(0,1)|*0.0004),
+    activations bf16 N(0, 1).  Timed region: K steps replayed from a captured
+    HIP graph; per-launch times from a second, eager pass with timing-only
+    events between the launches.  The roofline is the larger launch's:
+    algorithmic bytes (codes + scales + activations in + outputs) against
+    HBM, and for many tokens also its flops against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_router_amd import _binding as B
+
+    cfg = dict(CONFIGS[args.config])
+    if args.tokens:
+        cfg["tokens"] = args.tokens
+    T = cfg["tokens"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev).manual_seed(90001)
+
+    def make(n, k, group):
+        w = torch.randint(-2**31, 2**31 - 1, (n, k // 4), dtype=torch.int32, device=dev, generator=gen)
+        s = (torch.randn(n, k // group, device=dev, generator=gen).abs() * 4e-4).to(torch.bfloat16)
+        return w, s.view(torch.int16)
+
+    if cfg["kind"] == "int8":
+        N, Kd, G = cfg["n"], cfg["k"], cfg["group"]
+        mats = [make(N, Kd, G) for _ in range(cfg["copies"])]
+        launches = [("lm_head", N, Kd, G)]
+        x0 = torch.randn(T, Kd, device=dev, generator=gen).to(torch.bfloat16).view(torch.int16)
+    else:
+        mats = []
+        for _ in range(cfg["pairs"]):
+            mats.append(make(320, 10240, 64) + make(10240, 320, 64))
+        launches = [("down", 320, 10240, 64), ("up", 10240, 320, 64)]
+        x0 = torch.randn(T, 10240, device=dev, generator=gen).to(torch.bfloat16).view(torch.int16)
+    outs = [torch.empty(T, n, dtype=torch.int16, device=dev) for _, n, _, _ in launches]
+    wss = []
+    for _, n, kk, g in launches:
+        need = B.moe_int8_linear_workspace_bytes(T, n, kk, g)
+        wss.append(torch.empty(need, dtype=torch.uint8, device=dev) if need else None)
+    nrot = len(mats)
+
+    def launch(i, j):
+        m = mats[i % nrot]
+        _, n, kk, g = launches[j]
+        xin = x0 if j == 0 else outs[0]
+        B.moe_int8_linear(xin, m[2 * j], m[2 * j + 1], T, n, kk, g, outs[j], wss[j])
+
+    def step(i):
+        for j in range(len(launches)):
+            launch(i, j)
+
+    K, W = args.steps, min(args.warmup, 20)
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    Gn = min(nrot, K)
+    graphs = []
+    for start, n in [(W, Gn), (W + (K // Gn) * Gn, K % Gn)]:
+        if n == 0:
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(start + i)
+        graphs.append((g, n))
+    torch.cuda.synchronize()
+    plan = [graphs[0]] * (K // Gn) + ([graphs[1]] if K % Gn else [])
+    assert sum(n for _, n in plan) == K
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ga.record()
+    for g, _ in plan:
+        g.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ga.elapsed_time(gb)
+    ms_per_step = gpu_ms / K
+
+    # per-launch times: eager pass behind a spin kernel, events on the stream
+    TE = TimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    nl = len(launches)
+    evs = [[TE.create() for _ in range(nl + 1)] for _ in range(K)]
+    sa, sb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sa.record(); torch.cuda._sleep(1_000_000); sb.record(); torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(sa.elapsed_time(sb), 1e-3)
+    torch.cuda._sleep(int(cycles_per_ms * (K * nl * 0.03 + 5.0)))
+    for i in range(K):
+        TE.record(evs[i][0], stream)
+        for j in range(nl):
+            launch(W + i, j)
+            TE.record(evs[i][j + 1], stream)
+    torch.cuda.synchronize()
+    per = np.array([[TE.ms(evs[i][j], evs[i][j + 1]) for j in range(nl)] for i in range(K)]) * 1e3
+    launch_us = per.mean(axis=0)
+
+    def alg_bytes(n, kk, g):
+        return n * kk + n * (kk // g) * 2 + T * kk * 2 + T * n * 2
+
+    dom = int(np.argmax(launch_us))
+    name, n, kk, g = launches[dom]
+    plan_gemv = T <= 4 and T * kk <= 32768
+    kname = ("int8_gemv_kernel<%d> (x in LDS, fp16 dot2 on byte-permuted codes)" % T if plan_gemv else
+             "int8_gemm_kernel (fp16 MFMA, exact per-group scaling) + split-K sum")
+    byt = alg_bytes(n, kk, g)
+    fl = 2.0 * T * n * kk
+    hbm = byt / (launch_us[dom] * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": f"{name}: {kname}", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": byt, "launch_us": round(float(launch_us[dom]), 3)}
+    if not plan_gemv:
+        tf = fl / (launch_us[dom] * 1e-6) / 1e12
+        roof["mfma_tflops"] = round(tf, 2)
+        roof["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+    trf = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+    if os.path.exists(trf):
+        with open(trf) as f:
+            t = json.load(f)
+        if t.get("source_hash") == kernel_source_hash() and t.get("tokens", T) == T:
+            roof["traffic"] = t.get("bytes_per_launch")
+    step_bytes = sum(alg_bytes(n_, k_, g_) for _, n_, k_, g_ in launches)
+    if cfg["kind"] == "int8":
+        metric = "INT8 W8A16 lm_head tokens/s"
+        workload = (f"{args.config}: lm_head [{N}x{Kd}] INT8 group {G}, T={T} tokens per step, "
+                    f"{nrot} resident copies used alternately")
+    else:
+        metric = "INT8 W8A16 hyper-connection mixer (down+up) tokens/s"
+        workload = (f"{args.config}: hyper-connection down [320x10240] then up [10240x320], INT8 group 64, "
+                    f"T={T} tokens per step, rotating over {nrot} resident pairs")
+    result = {
+        "metric": metric, "value": round(T * K / (gpu_ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 codes x fp16 activations, fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded, device-generated)",
+        "config": {"workload": workload, "tokens": T,
+                   "launch_us": {nm: round(float(u), 3) for (nm, _, _, _), u in zip(launches, launch_us)},
+                   "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roof, "wall_s": round(wall, 4), "source_hash": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from quantized_moe_router_amd import synth
+        if cfg["kind"] == "int8":
+            rows = 2048
+            lay = synth.make_int8_linear(T, rows, Kd, G, seed=11)
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.int8_linear(lay["x"], lay["packed"], lay["scales"], G)
+                done += rows
+                if time.perf_counter() - t0 >= args.cpu_seconds:
+                    break
+            el = time.perf_counter() - t0
+            sample = (f"{done // rows} oracle calls on {rows} of the {N} rows (same shape and "
+                      f"distribution, host-generated), {el:.1f} s; scaled by rows")
+            tok_s = T * (done / N) / el
+        else:
+            ntok = min(T, 8)
+            dn = synth.make_int8_linear(ntok, 320, 10240, 64, seed=11)
+            up = synth.make_int8_linear(ntok, 10240, 320, 64, seed=12)
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.int8_linear(dn["x"], dn["packed"], dn["scales"], 64)
+                oracle.int8_linear(up["x"], up["packed"], up["scales"], 64)
+                done += ntok
+                if time.perf_counter() - t0 >= args.cpu_seconds:
+                    break
+            el = time.perf_counter() - t0
+            sample = f"{done // ntok} oracle down+up pairs on {ntok} tokens, {el:.1f} s"
+            tok_s = done / el
+        result["cpu_baseline"] = {"value": round(tok_s, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
+                                  "kind": "oracle", "sample": sample}
     print(json.dumps(result), flush=True)
 
 

@@ -183,11 +183,11 @@ int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t
  * out[t][r] = bf16(sum_i x[t][i] * (byte[r][i] - 128) * scale[r][i / group]),
  * accumulated in fp32 and rounded once (to nearest even).  Activations are
  * taken as fp16 (exact for finite bf16 values of magnitude 2^-14 .. 65504;
- * smaller ones lose low bits, larger ones saturate).  At most 4 tokens with
- * tokens * k <= 32768 run as a GEMV; more run as a matrix-core GEMM whose
- * K may be split over workgroups, the fp32 partials then living in the
- * caller's workspace and being summed in a fixed order (the result does not
- * depend on the split schedule's timing).  group is 64 or 128, k a multiple
+ * smaller ones lose low bits, larger ones saturate).  Up to 16 tokens run
+ * as GEMVs (while the fp16 activations fit 64 KB of LDS); more run as a
+ * matrix-core GEMM whose K may be split over workgroups, the fp32 partials
+ * then living in the caller's workspace and being summed in a fixed order
+ * (the result does not depend on the split schedule's timing).  group is 64 or 128, k a multiple
  * of it (at most 65536), n in [1, 2^24], tokens in [0, 2^20] with tokens * n
  * and tokens * k below 2^31; tokens = 0 is a no-op.  Pointers must be
  * 16-byte aligned; the workspace may be NULL when

@@ -417,7 +417,8 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
 // ---------------------------------------------------------------------------
 // INT8 W8A16 linear layer (int8_linear.hip)
 // ---------------------------------------------------------------------------
-constexpr int kInt8GemvMaxTokens = 4;          // GEMV up to this many tokens, GEMM above
+constexpr int kInt8GemvMaxTokens = 4;          // dot-product GEMV up to this many tokens
+constexpr int kInt8MfmaGemvMaxTokens = 16;     // matrix-core GEMV (wide matrices) up to this many
 constexpr size_t kInt8GemvMaxLds = 65536;      // GEMV keeps T x K fp16 activations in LDS
 constexpr int kInt8GemvMaxBlocks = 2048;       // persistent GEMV grid (8 per CU)
 constexpr long kInt8GemmTargetTiles = 256;     // K is split until about this many workgroups
@@ -426,6 +427,8 @@ constexpr int kInt8MaxSplitK = 16;
 
 struct Int8Plan {
     bool gemv;
+    bool rowsplit;       // GEMV with one row per workgroup (narrow matrices)
+    bool mfma;           // matrix-core GEMV (5..16 tokens, wide matrices)
     int mtiles, ntiles, ksplit, kslice;
     size_t pstride;      // floats per split in the partials (T * N rounded up to 4)
     size_t part_bytes;   // fp32 split-K partials (workspace)

@@ -222,6 +222,243 @@ __global__ __launch_bounds__(kGvThreads) void int8_gemv_kernel(const uint16_t *_
     if (u < U) compute(u, r0);
 }
 
+// Narrow matrices (few rows, long rows: the hyper-connection down projection
+// [320, 10240]): four row blocks per wave would leave most of the chip idle,
+// so a workgroup takes one row and its four waves split the row's chunks.
+// Activations come straight from global memory (a few KB, read by every
+// workgroup, so L2 hits) with the weights, converted in registers: no LDS
+// staging and no barrier before the first product.  The four wave sums
+// meet in LDS (added in wave order).
+template <int T>
+__global__ __launch_bounds__(kGvThreads) void int8_gemv_rowsplit_kernel(const uint16_t *__restrict__ x,
+                                                                        const int32_t *__restrict__ wq,
+                                                                        const uint16_t *__restrict__ wscale,
+                                                                        int N, int K, int gshift,
+                                                                        uint16_t *__restrict__ out)
+{
+    __shared__ float s_red[kGvThreads / 64][4];
+    const int CPR = K >> 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x;
+    const int CPW = (CPR + 3) / 4;                  // chunks per wave
+    const int cbeg = wave * CPW, cend = min(CPR, cbeg + CPW);
+    const int NI = (CPW + 63) >> 6;
+    const u32x4_t *wrow = reinterpret_cast<const u32x4_t *>(wq + (size_t)row * (K / 4));
+    const uint16_t *srow = wscale + (size_t)row * (K >> gshift);
+    auto chunk = [&](int i) { return min(cbeg + i * 64 + lane, CPR - 1); };
+    struct Raw {
+        u32x4_t w;
+        u32x4_t xb[T][2];   // bf16 activations of the chunk
+        uint16_t s;
+    };
+    auto load = [&](int i, Raw &r) {
+        const int c = chunk(i);
+        r.w = __builtin_nontemporal_load(wrow + c);
+        r.s = srow[(16 * c) >> gshift];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (size_t)t * K) + 2 * c;
+            r.xb[t][0] = xp[0];
+            r.xb[t][1] = xp[1];
+        }
+    };
+
+    constexpr int M = T == 1 ? 1 : T == 2 ? 2 : 4;   // T, padded to a power of two
+    float acc[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) acc[t] = 0.f;
+    auto compute = [&](int i, const Raw &r) {
+        const bool valid = cbeg + i * 64 + lane < cend;
+        h2_t cp[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            cp[2 * q] = code_pair<0>(r.w[q]);
+            cp[2 * q + 1] = code_pair<1>(r.w[q]);
+        }
+        const float sf = valid ? bf16_to_f32(r.s) : 0.f;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float p = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4_t v = bf16x8_to_f16x8(r.xb[t][h]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t e = v[q];   // element copied out before the bit cast
+                    p = __builtin_amdgcn_fdot2(cp[4 * h + q], __builtin_bit_cast(h2_t, e), p, false);
+                }
+            }
+            acc[t] = fmaf(sf, p, acc[t]);
+        }
+    };
+    Raw r0, r1;
+    load(0, r0);
+    int i = 0;
+    for (; i + 1 < NI; i += 2) {
+        load(i + 1, r1);
+        compute(i, r0);
+        if (i + 2 < NI) load(i + 2, r0);
+        compute(i + 1, r1);
+    }
+    if (i < NI) compute(i, r0);
+
+    const float sum = wave_transpose_sum<M>(acc, lane);
+    constexpr int shift = M == 1 ? 6 : M == 2 ? 5 : 4;
+    const int t = lane >> shift;
+    if ((lane & ((1 << shift) - 1)) == 0 && t < T) s_red[wave][t] = sum;
+    __syncthreads();
+    if (threadIdx.x < T) {
+        const float v = ((s_red[0][threadIdx.x] + s_red[1][threadIdx.x]) + s_red[2][threadIdx.x]) +
+                        s_red[3][threadIdx.x];
+        out[(size_t)threadIdx.x * N + row] = (uint16_t)f32_to_bf16(v);
+    }
+}
+
+// 5..16 tokens on wide matrices: the dot products go to the matrix cores,
+// so the vector ALU work per weight byte (one permute and one packed add per
+// two codes) no longer grows with the token count.  (Up to 4 tokens the
+// dot-product GEMV is faster: its 1 KB-per-row loads keep DRAM pages open,
+// while the matrix-core operand layout spreads a load over 16 rows.)  A wave owns 16 weight
+// rows; per 64-input step each lane loads 16 codes (16 bytes) of row
+// lane % 16 at offset 16 (lane / 16), and two v_mfma_f32_16x16x32_f16 take
+// them as the B operand (column = weight row) against fp16 activations from
+// LDS as the A operand (row = token, lane % 16; rows past T repeat the last
+// token and are never stored).  Each lane's output column is its own weight
+// row, so the group scale is applied per lane: a group's MFMA sums start
+// from zero and are folded in with one FMA per output.  Weight loads run
+// in two batches of four steps (named register sets), each batch's loads
+// issued back to back so a row's 256 consecutive bytes are requested
+// together.
+constexpr int kMfRows = 16;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kGvThreads) void int8_gemv_mfma_kernel(const uint16_t *__restrict__ x,
+                                                                   const int32_t *__restrict__ wq,
+                                                                   const uint16_t *__restrict__ wscale,
+                                                                   int T, int N, int K, int gshift,
+                                                                   uint16_t *__restrict__ out)
+{
+    // x as fp16 [T][K / 8 + 1] 16-byte units (one unit of padding per row so
+    // the 16 token rows of a read fall in different banks)
+    extern __shared__ u32x4_t s_x[];
+    const int K8 = K >> 3, xs = K8 + 1;
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (kGvThreads / 64) + (threadIdx.x >> 6);
+    const int W = gridDim.x * (kGvThreads / 64);
+    const int nrb = (N + kMfRows - 1) / kMfRows;
+    const int steps = K >> 6;
+    const int my_blocks = gw < nrb ? (nrb - gw + W - 1) / W : 0;
+    const int U = my_blocks * steps;
+    const int n = lane & 15, kq = lane >> 4;
+    const size_t rstride = (size_t)K / 4;
+    const int nsc = K >> gshift;
+
+    // wave-uniform cursors (block b, step st) for the loads, which run up to
+    // eight units ahead of the compute; past the last unit the loads repeat
+    // it (a cache hit, never used)
+    int lb = 0, lst = 0;
+    auto lrow_of = [&](int b) { return min((gw + b * W) * kMfRows + n, N - 1); };
+    int lrow = lrow_of(0);
+    struct Raw {
+        u32x4_t w;
+        uint16_t s;
+    };
+    auto load_next = [&](Raw &r) {
+        r.w = *(reinterpret_cast<const u32x4_t *>(wq + lrow * rstride) + 4 * lst + kq);
+        r.s = wscale[(size_t)lrow * nsc + ((lst << 6) >> gshift)];
+        if (lst + 1 < steps) {
+            ++lst;
+        } else if (lb + 1 < my_blocks) {
+            lst = 0;
+            lrow = lrow_of(++lb);
+        }
+    };
+    Raw a0, a1, a2, a3, b0, b1, b2, b3;
+    if (U > 0) {
+        load_next(a0);
+        load_next(a1);
+        load_next(a2);
+        load_next(a3);
+        load_next(b0);
+        load_next(b1);
+        load_next(b2);
+        load_next(b3);
+    }
+    for (int i = threadIdx.x; i < T * K8; i += kGvThreads) {
+        const int t = i / K8, c = i - t * K8;
+        s_x[t * xs + c] = bf16x8_to_f16x8(*reinterpret_cast<const u32x4_t *>(x + (size_t)t * K + 8 * c));
+    }
+    __syncthreads();
+    if (U == 0) return;
+
+    const int tr = min(n, T - 1);
+    const u32x4_t *xrow = s_x + tr * xs + 2 * kq;
+    const int gmask = (1 << (gshift - 6)) - 1;   // steps per scale group, minus one
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, tmp = {0.f, 0.f, 0.f, 0.f};
+    int cb = 0, cst = 0;   // compute cursor
+
+    auto compute = [&](const Raw &r) {
+        f16x8_t bq[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const h2_t p0 = code_pair<0>(r.w[2 * h]), p1 = code_pair<1>(r.w[2 * h]);
+            const h2_t p2 = code_pair<0>(r.w[2 * h + 1]), p3 = code_pair<1>(r.w[2 * h + 1]);
+            bq[h] = f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+        const f16x8_t a0f = __builtin_bit_cast(f16x8_t, xrow[8 * cst]);
+        const f16x8_t a1f = __builtin_bit_cast(f16x8_t, xrow[8 * cst + 1]);
+        if ((cst & gmask) == 0) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0f, bq[0], z, 0, 0, 0);
+        } else {
+            tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0f, bq[0], tmp, 0, 0, 0);
+        }
+        tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1f, bq[1], tmp, 0, 0, 0);
+        if ((cst & gmask) == gmask) {
+            const float sf = bf16_to_f32(r.s);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(sf, tmp[j], acc[j]);
+        }
+        if (cst + 1 < steps) {
+            ++cst;
+        } else {
+            // row block done: lane holds tokens 4 (lane / 16) + j of row n
+            const int row = (gw + cb * W) * kMfRows + n;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * kq + j;
+                if (t < T && row < N) out[(size_t)t * N + row] = (uint16_t)f32_to_bf16(acc[j]);
+                acc[j] = 0.f;
+            }
+            cst = 0;
+            ++cb;
+        }
+    };
+
+    // two batches of four units: a batch is computed while the other is in
+    // flight, and its refill issues four consecutive steps of the same rows
+    // back to back (256 contiguous bytes per row)
+    for (int u = 0; u < U; u += 8) {
+        compute(a0);
+        if (u + 1 < U) compute(a1);
+        if (u + 2 < U) compute(a2);
+        if (u + 3 < U) compute(a3);
+        load_next(a0);
+        load_next(a1);
+        load_next(a2);
+        load_next(a3);
+        if (u + 4 < U) compute(b0);
+        if (u + 5 < U) compute(b1);
+        if (u + 6 < U) compute(b2);
+        if (u + 7 < U) compute(b3);
+        load_next(b0);
+        load_next(b1);
+        load_next(b2);
+        load_next(b3);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // GEMM (MFMA)
 // ---------------------------------------------------------------------------
@@ -431,7 +668,16 @@ __global__ __launch_bounds__(256) void int8_splitk_sum_kernel(const float *__res
 Int8Plan int8_plan(int T, int N, int K, int G)
 {
     Int8Plan p{};
-    p.gemv = T <= kInt8GemvMaxTokens && (size_t)T * K * 2 <= kInt8GemvMaxLds;
+    // narrow: fewer row blocks of four than waves of the persistent grid
+    const bool narrow = (N + 3) / 4 < kInt8GemvMaxBlocks && K >= 1024;
+    if (T >= 1 && T <= kInt8GemvMaxTokens && narrow) {
+        p.gemv = p.rowsplit = true;   // one row per workgroup, K split over its waves
+    } else if (T >= 1 && T <= kInt8GemvMaxTokens && (size_t)T * K * 2 <= kInt8GemvMaxLds) {
+        p.gemv = true;                // dot-product GEMV, four rows per wave
+    } else if (T > kInt8GemvMaxTokens && T <= kInt8MfmaGemvMaxTokens && !narrow &&
+               (size_t)T * (K / 8 + 1) * 16 <= kInt8GemvMaxLds) {
+        p.gemv = p.mfma = true;       // matrix-core GEMV, 16 rows per wave
+    }
     if (p.gemv || T == 0) return p;
     p.mtiles = (T + kGmM - 1) / kGmM;
     p.ntiles = (N + kGmN - 1) / kGmN;
@@ -459,6 +705,24 @@ hipError_t launch_int8_linear(const uint16_t *x, const int32_t *wq, const uint16
 {
     const Int8Plan p = int8_plan(T, N, K, G);
     const int gshift = G == 64 ? 6 : 7;
+    if (p.gemv && p.rowsplit) {
+        switch (T) {
+        case 1: int8_gemv_rowsplit_kernel<1><<<N, kGvThreads, 0, st>>>(x, wq, ws, N, K, gshift, out); break;
+        case 2: int8_gemv_rowsplit_kernel<2><<<N, kGvThreads, 0, st>>>(x, wq, ws, N, K, gshift, out); break;
+        case 3: int8_gemv_rowsplit_kernel<3><<<N, kGvThreads, 0, st>>>(x, wq, ws, N, K, gshift, out); break;
+        default: int8_gemv_rowsplit_kernel<4><<<N, kGvThreads, 0, st>>>(x, wq, ws, N, K, gshift, out); break;
+        }
+        return hipGetLastError();
+    }
+    if (p.gemv && p.mfma) {
+        const int nrb = (N + kMfRows - 1) / kMfRows;
+        const int wpb = kGvThreads / 64;
+        int grid = (nrb + wpb - 1) / wpb;
+        grid = grid < kInt8GemvMaxBlocks ? grid : kInt8GemvMaxBlocks;
+        const size_t lds = (size_t)T * (K / 8 + 1) * 16;
+        int8_gemv_mfma_kernel<<<grid, kGvThreads, lds, st>>>(x, wq, ws, T, N, K, gshift, out);
+        return hipGetLastError();
+    }
     if (p.gemv) {
         const int nrb = (N + kGvRows - 1) / kGvRows;
         const int wpb = kGvThreads / 64;

@@ -70,22 +70,33 @@ def compare(g: np.ndarray, o: np.ndarray, label: str):
 
 
 SMALL = [
-    # (T, N, K, G): GEMV cases (T <= 4, T * K <= 32768)
-    (1, 37, 128, 64),      # ragged row block, one partial column pass
-    (1, 300, 2560, 128),   # lm_head row length: 2.5 passes of 64 chunks
-    (2, 130, 320, 64),     # hyper-connection up row length: 20 of 64 lanes
-    (3, 77, 1152, 128),    # two passes, the second ragged
-    (4, 320, 4096, 64),
-    (4, 64, 8192, 128),    # T * K at the GEMV's LDS limit
-    (1, 9, 64, 64),        # single group
-    # GEMM cases
-    (1, 5, 65536, 64),     # one token past the GEMV's LDS limit: split K, one row tile
-    (5, 200, 640, 64),     # the smallest GEMM token count
-    (33, 129, 1024, 128),  # ragged row and weight-row tiles
+    # (T, N, K, G).  Plan: narrow matrices (N < 8189 and K >= 1024) with at
+    # most 4 tokens take one row per workgroup; other matrices with at most 4
+    # tokens the dot-product GEMV; 5..16 tokens on wide matrices the
+    # matrix-core GEMV (while T * (K + 8) fp16 fit 64 KB of LDS); everything
+    # else the GEMM.
+    (1, 37, 128, 64),      # dot GEMV: ragged row block, one partial column pass
+    (1, 9, 64, 64),        # dot GEMV: single group
+    (2, 130, 320, 64),     # dot GEMV: hyper-connection up row length
+    (2, 9000, 1152, 128),  # dot GEMV: several row blocks per wave, two passes
+    (3, 8193, 2048, 64),   # dot GEMV: ragged last row block
+    (1, 300, 2560, 128),   # row split: lm_head row length
+    (3, 77, 1152, 128),    # row split: ragged wave slices
+    (4, 320, 4096, 64),    # row split
+    (4, 64, 8192, 128),    # row split at the LDS limit
+    (5, 777, 448, 64),     # matrix-core GEMV: odd step count, ragged rows
+    (7, 9001, 1152, 128),  # matrix-core GEMV: several row blocks per wave
+    (8, 3000, 640, 64),
+    (12, 8200, 2560, 128), # matrix-core GEMV at the LDS limit for K = 2560
+    (16, 2001, 320, 64),   # matrix-core GEMV: all 16 token rows
+    (5, 200, 640, 64),     # matrix-core GEMV
+    (6, 320, 2048, 64),    # GEMM: narrow matrix, split K, one row tile
+    (1, 5, 65536, 64),     # GEMM: one token past every GEMV's LDS limit
+    (33, 129, 1024, 128),  # GEMM: ragged row and weight-row tiles
     (130, 333, 1024, 64),
     (300, 256, 256, 128),
     (64, 1000, 2560, 128),
-    (200, 96, 4096, 64),   # narrow: split K
+    (200, 96, 4096, 64),   # GEMM: narrow, split K
 ]
 
 
@@ -115,7 +126,7 @@ def test_int8_hyper_connection_shapes(which, T):
     compare(g[toks], o, label)
 
 
-@pytest.mark.parametrize("T", [1, 2, 4])
+@pytest.mark.parametrize("T", [1, 2, 4, 12, 16])
 def test_int8_lm_head_full_size(T):
     # lm_head [248320, 2560], group 128: every output against the oracle on
     # a seeded sample of rows (plus the first and last)
@@ -131,11 +142,12 @@ def test_int8_lm_head_full_size(T):
     assert np.isfinite(g).all()
 
 
-@pytest.mark.parametrize("T", [3, 40])
-def test_int8_edge_codes_and_scales(T):
+@pytest.mark.parametrize("T,K", [(1, 256), (3, 256), (2, 1024), (6, 256), (40, 256)])
+def test_int8_edge_codes_and_scales(T, K):
     # all-(-128) and all-127 rows, zero scales, a zero token, powers of two,
-    # through the GEMV (3 tokens) and the GEMM (40 tokens)
-    N, K, G = 8, 256, 64
+    # through the dot GEMV (1 and 3 tokens), the one-row-per-workgroup GEMV
+    # (K = 1024), the matrix-core GEMV (6 tokens) and the GEMM (40 tokens)
+    N, G = 8, 64
     x = np.zeros((T, K), np.float32)
     x[0::3] = 1.0
     x[1::3] = np.tile([1.0, -2.0, 0.5, 4.0], K // 4)
