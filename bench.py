@@ -488,6 +488,15 @@ def bench_int8(args):
         need = B.moe_int8_linear_workspace_bytes(T, n, kk, g)
         wss.append(torch.empty(need, dtype=torch.uint8, device=dev) if need else None)
     nrot = len(mats)
+    if args.copy_calibration:
+        # a plain copy of known size: each launch reads and writes exactly n bytes
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def launch(i, j):
         m = mats[i % nrot]
