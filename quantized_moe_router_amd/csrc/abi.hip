@@ -105,7 +105,8 @@ int32_t check_shape(const moe_int4_shape *s, const moe_shared_int6 *sh, Dims *d)
     if (!s) return fail(MOE_INT4_EINVAL, "shape is NULL");
     if (s->tokens < 0 || s->tokens > (1 << 20))
         return fail(MOE_INT4_EINVAL, "tokens=%d outside [0, 1048576]", s->tokens);
-    if (s->group != kGroup) return fail(MOE_INT4_EINVAL, "group=%d, only 128 is supported", s->group);
+    if (s->group != 128 && s->group != 64)
+        return fail(MOE_INT4_EINVAL, "group=%d, INT4 supports 128 and 64", s->group);
     if (s->hidden <= 0 || s->hidden % 256 || s->hidden > 4096)
         return fail(MOE_INT4_EINVAL, "hidden=%d must be a positive multiple of 256, at most 4096",
                     s->hidden);
@@ -123,6 +124,7 @@ int32_t check_shape(const moe_int4_shape *s, const moe_shared_int6 *sh, Dims *d)
     d->I = s->inter;
     d->k = s->top_k;
     d->S = s->tokens * s->top_k;
+    d->gsh = s->group == 64 ? 1 : 2;
     d->sh_I = 0;
     if (sh) {
         if (sh->group != kShGroup)

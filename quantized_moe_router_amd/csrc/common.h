@@ -12,7 +12,7 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxHidden = 4096;
-constexpr int kGroup = 128;      // INT4 group along the input dimension
+constexpr int kGroup = 128;      // INT4 group along the input dimension (64 also accepted)
 constexpr int kShGroup = 64;     // INT6 group (shared expert)
 // Decode (GEMV) path for T <= kDecodeMaxTokens, grouped-GEMM path above.
 constexpr int kDecodeMaxTokens = 16;
@@ -332,6 +332,7 @@ struct Workspace {
 struct Dims {
     int T, H, E, I, k, S;
     int sh_I;  // 0 = no shared expert
+    int gsh;   // INT4 group = 32 << gsh (2: group 128, 1: group 64)
 };
 
 constexpr int kPermChunk = 1024;  // most slots per chunk of the large permutation

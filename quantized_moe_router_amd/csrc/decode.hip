@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
     const int t = s / d.k;
     const uint32_t e_raw = load_coherent(reinterpret_cast<const uint32_t *>(ids) + s);
     const int grp = lane >> 4, q = lane & 15;
-    const int nck = d.H / 32, words = d.H / 8, nsc = d.H / kGroup;
+    const int nck = d.H / 32, words = d.H / 8, nsc = d.H >> (d.gsh + 5);
     // the token's activations first, then the weights: loads complete in
     // issue order, so the LDS store of x then waits for x alone.  Every load
     // and store here is unconditional (clamped indices; copies past the row end
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
         for (int c = 0; c < CPL; ++c) {
             const int kc = q + 16 * c, ok = kc < nck, kcl = ok ? kc : 0;
             w[qd][c] = load_stream(wrow + kcl);
-            const float sv = bf16_to_f32(a.w13s[r * nsc + kcl / 4]);
+            const float sv = bf16_to_f32(a.w13s[r * nsc + (kcl >> d.gsh)]);
             sc[qd][c] = ok ? sv : 0.f;
         }
     }
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int grp = wave * 2 + (lane >> 5), rl = (lane >> 2) & 7, q = lane & 3;
     const int row = blockIdx.x * kDnRows + rl;
-    const int nck = d.I / 32, words = d.I / 8, nsc = d.I / kGroup;
+    const int nck = d.I / 32, words = d.I / 8, nsc = d.I >> (d.gsh + 5);
     const int slots_per_group = kDnHBytes / (2 * d.I);
     int tg = slots_per_group / d.k;
     tg = tg < 1 ? 1 : (tg > kDnMaxGroup ? kDnMaxGroup : tg);
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) 
             for (int c = 0; c < CPL; ++c) {
                 const int kc = q + 4 * c, ok = kc < nck, kcl = ok ? kc : 0;
                 w[c] = load_stream(wrow + kcl);
-                const float sv = bf16_to_f32(a.w2s[r * nsc + kcl / 4]);
+                const float sv = bf16_to_f32(a.w2s[r * nsc + (kcl >> d.gsh)]);
                 sc[c] = ok ? sv : 0.f;
             }
         };

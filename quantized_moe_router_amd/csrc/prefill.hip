@@ -175,14 +175,17 @@ __device__ __forceinline__ h2_t scale_pair(uint16_t bf)
 // workgroups per CU), or 2 for routed tiles of at most 64 rows, which then
 // fit three workgroups per CU (fewer accumulators, half the activation LDS):
 // with few slots per expert the tiles are small and the extra workgroup per
-// CU hides more of the weights' memory latency.
-template <int MODE, int MAXMA = 4>
+// CU hides more of the weights' memory latency.  QG is the number of INT4
+// scale groups per 128 inputs: 1 (group 128) or 2 (group 64, one scale per
+// 64-wide K stage).
+template <int MODE, int MAXMA = 4, int QG = 1>
 __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_kernel(GemmArgs g, int nblocks)
 {
     constexpr bool kW13 = (MODE == kRoutedW13 || MODE == kSharedW13);
     constexpr bool kRouted = (MODE == kRoutedW13 || MODE == kRoutedW2);
     constexpr bool kInt6 = !kRouted;
     static_assert(MAXMA == 4 || (MAXMA == 2 && kRouted), "small tiles are a routed-GEMM variant");
+    static_assert(QG == 1 || (QG == 2 && kRouted), "group 64 is an INT4 (routed) variant");
     __shared__ __align__(16) _Float16 s_a[2][32 * MAXMA * kLdsRow];
     __shared__ int s_tok[kMT];     // token of each tile row (-1: none)
     __shared__ int s_yrow[kMT];    // down modes: row of y that each tile row writes
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
     // MFMA column l of its weight tile nt.
     constexpr int QB = kInt6 ? 1 : 2;
     __shared__ u32x4_t s_bq[QB][kInt6 ? 1 : kNT * 4];
-    __shared__ uint16_t s_bqs[QB][kInt6 ? 1 : kNT];
+    __shared__ uint16_t s_bqs[QB][kInt6 ? 1 : QG * kNT];
     auto tile_row = [&](int r) {
         const int w = r >> 6, nt = (r >> 5) & 1, l = r & 31;
         if constexpr (kW13) return nt == 0 ? 128 * nb + 32 * w + l : g.I + 128 * nb + 32 * w + l;
@@ -296,13 +299,14 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
     uint32_t qoff[4];      // byte offsets of this thread's four rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) qoff[i] = (uint32_t)(tile_row((tid >> 2) + 64 * i) * bstride * 4);
-    const uint16_t *qs = bs + (size_t)tile_row(tid) * (K / kGroup);
+    const uint16_t *qs = bs + (size_t)tile_row(tid) * (K / kGroup * QG);
     u32x4_t rq[4];         // vector type: stored to LDS by value
-    uint16_t rqs = 0;
+    uint16_t rqs[QG];
     auto load_q = [&](int grp) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) rq[i] = *reinterpret_cast<const u32x4_t *>(bq + qoff[i] + 64 * grp);
-        rqs = qs[grp];
+#pragma unroll
+        for (int j = 0; j < QG; ++j) rqs[j] = qs[QG * grp + j];
     };
     auto store_q = [&](int buf) {
 #pragma unroll
@@ -310,7 +314,8 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
             const int r = (tid >> 2) + 64 * i;
             s_bq[buf][r * 4 + (c4 ^ ((r >> 1) & 3))] = rq[i];
         }
-        s_bqs[buf][tid] = rqs;
+#pragma unroll
+        for (int j = 0; j < QG; ++j) s_bqs[buf][j * kNT + tid] = rqs[j];
     };
 
     f32x16_t acc[MAXMA][2];
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
                     const int r = 64 * wave + 32 * nt + (lane & 31);
                     const u32x4_t v = s_bq[buf][r * 4 + ((2 * q + half) ^ ((r >> 1) & 3))];
                     w4[nt] = make_uint4(v[0], v[1], v[2], v[3]);
-                    if (q == 0) s2[nt] = scale_pair(s_bqs[buf][r]);
+                    if (QG == 2 || q == 0) s2[nt] = scale_pair(s_bqs[buf][(QG == 2 ? q : 0) * kNT + r]);
                 }
             }
             // activation fragments of the active row tiles are read one MFMA
@@ -690,12 +695,18 @@ hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const
 
 
 template <int MODE>
-static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st)
+static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st, bool g64 = false)
 {
     const int groups = (ntiles_max + 7) / 8;
     if constexpr (MODE == kRoutedW13 || MODE == kRoutedW2) {
+        const unsigned grid = groups * 8 * nblocks;
         if (g.small_rows > 0) {
-            moe_gemm_kernel<MODE, 2><<<groups * 8 * nblocks, kGemmThreads, 0, st>>>(g, nblocks);
+            if (g64) moe_gemm_kernel<MODE, 2, 2><<<grid, kGemmThreads, 0, st>>>(g, nblocks);
+            else moe_gemm_kernel<MODE, 2><<<grid, kGemmThreads, 0, st>>>(g, nblocks);
+            return hipGetLastError();
+        }
+        if (g64) {
+            moe_gemm_kernel<MODE, 4, 2><<<grid, kGemmThreads, 0, st>>>(g, nblocks);
             return hipGetLastError();
         }
     }
@@ -724,15 +735,15 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     // three-workgroups-per-CU kernel, so the few busy experts of a skewed
     // routing are spread over twice as many workgroups
     g.small_rows = small ? 64 : 0;
-    g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H / kGroup);
-    if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st)) != hipSuccess) return e;
+    g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H >> (d.gsh + 5));
+    if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st, d.gsh == 1)) != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
     // routed down -> y[t][j] = w * (W2 h)
     GemmArgs g2 = g;
     g2.a16 = ws.h; g2.bp = a.w2p; g2.bs = a.w2s; g2.weights = a.weights; g2.y_out = y;
     g2.K = d.I;
-    g2.b_words = (size_t)d.H * d.I / 8; g2.b_scales = (size_t)d.H * (d.I / kGroup);
-    if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st)) != hipSuccess) return e;
+    g2.b_words = (size_t)d.H * d.I / 8; g2.b_scales = (size_t)d.H * (d.I >> (d.gsh + 5));
+    if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st, d.gsh == 1)) != hipSuccess) return e;
     if (d.sh_I > 0) {
         // shared expert: gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
         if ((e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;

@@ -37,7 +37,8 @@ def _shape(**kw):
 
 
 @pytest.mark.parametrize("kw,msg", [
-    (dict(group=64), "group"),
+    (dict(group=32), "group"),
+    (dict(group=256), "group"),
     (dict(hidden=2500), "hidden"),
     (dict(hidden=8192), "hidden"),
     (dict(inter=100), "inter"),

@@ -59,7 +59,7 @@ def run_and_check(host, tokens=None, real_dev=None, label=""):
     say(f"case {label}: T={shape.tokens} H={shape.hidden} E={shape.experts} k={shape.top_k} "
         f"I={shape.inter} shared={'shared' in host}")
     dev = _device_layer(host, real_dev)
-    L = MoeInt4Layer(dev, shape.top_k, shared=dev.get("shared"))
+    L = MoeInt4Layer(dev, shape.top_k, group=host["group"], shared=dev.get("shared"))
     out = L.forward(dev["x"])
     r = L.route(dev["x"])
     torch.cuda.synchronize()
@@ -329,3 +329,22 @@ def test_graph_replay_matches_eager(T):
         assert torch.equal(out, eager)
         assert torch.equal(Lb.forward(b["x"]), other)
         torch.cuda.synchronize()
+
+
+# ---- INT4 group 64 on the same kernels ("Running 125B MoE on Three 3090s -
+# vLLM Edition", section 2: the group-64 alternative to group 128) ----
+
+@pytest.mark.parametrize("T", [1, 4, 16, 17, 70, 600])
+def test_group64_ragged(T):
+    shape = synth.LayerShape(tokens=T, hidden=768, experts=40, top_k=6, inter=384, group=64)
+    run_and_check(synth.make_layer(shape, seed=500 + T), label=f"group64 T={T}")
+
+
+@pytest.mark.parametrize("T,shared", [(1, False), (4, True), (512, True)])
+def test_group64_real_width(T, shared):
+    # hidden 2560, intermediate 640, top-10 over 64 experts (one GPU's share
+    # under 8-way expert parallelism)
+    shape = synth.LayerShape(tokens=T, experts=64, group=64)
+    host = synth.make_layer(shape, seed=600 + T, shared=shared)
+    toks = None if T <= 64 else np.arange(0, T, 7)
+    run_and_check(host, tokens=toks, label=f"group64 real-width T={T}")

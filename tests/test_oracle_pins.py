@@ -293,10 +293,12 @@ def _bf16_vals(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
 
 
-def test_dense_single_expert_matches_torch():
-    """E = 1, k = 1: the layer is a dense SwiGLU MLP."""
+@pytest.mark.parametrize("G", [128, 64])
+def test_dense_single_expert_matches_torch(G):
+    """E = 1, k = 1: the layer is a dense SwiGLU MLP (groups of 128, and of
+    64 for the group-64 variant of the same machinery)."""
     rng = np.random.default_rng(7)
-    H, I, G = 256, 128, 128
+    H, I = 256, 128
     xb = torch.randn(5, H, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
     x = xb.view(torch.int16).numpy().view(np.uint16)
     c13 = rng.integers(-8, 8, size=(2 * I, H))
