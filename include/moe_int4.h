@@ -24,7 +24,9 @@
  *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream)
  *     and is complete when the stream is.  Calls are capturable into a HIP
  *     graph (no host synchronisation, no memset nodes).
- *   - Weight format (INT4, group G = 128, symmetric, no zero point):
+ *   - Weight format (INT4, group G = 128 -- or 64, the finer grouping
+ *     weighed in "Running 125B MoE on Three 3090s - vLLM Edition", section 2
+ *     -- symmetric, no zero point):
  *       w13_packed int32 [E][2I][H/8]  rows 0..I-1 = gate, rows I..2I-1 = up;
  *       w13_scales bf16  [E][2I][H/G]
  *       w2_packed  int32 [E][H][I/8];   w2_scales bf16 [E][H][I/G]
@@ -60,7 +62,7 @@ extern "C" {
 #define MOE_INT4_EDEVICE (-5)    /* no usable gfx950 device */
 
 /* Layer dimensions.  Limits: tokens >= 0 (0 is a no-op); 1 <= top_k <=
- * min(experts, 32); experts <= 1024; group == 128; hidden a multiple of 256,
+ * min(experts, 32); experts <= 1024; group 128 or 64; hidden a multiple of 256,
  * at most 4096; inter a multiple of 128, at most 1024; tokens * hidden and
  * tokens * top_k * inter (and tokens * shared inter) below 2^31. */
 typedef struct moe_int4_shape {
