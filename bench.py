@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="resident layers (0: config default)")
     p.add_argument("--tokens", type=int, default=0,
                    help="tokens per step (0: config default); for sweeps over the batch size")
+    p.add_argument("--group", type=int, default=128, choices=(64, 128),
+                   help="INT4 group of the routed experts (MoE configs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -146,7 +148,7 @@ def main():
     if args.tokens:
         cfg["tokens"] = args.tokens
     T, L = cfg["tokens"], cfg["layers"]
-    shape = synth.LayerShape(tokens=T)
+    shape = synth.LayerShape(tokens=T, group=args.group)
     H, E, I, k = shape.hidden, shape.experts, shape.inter, shape.top_k
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -167,7 +169,7 @@ def main():
             rank = torch.randperm(E, generator=g).double() + 1.0
             w["router_w"][:, H - 1] = (-cfg["zipf"] * torch.log(rank)).to(torch.bfloat16).view(torch.int16).to(dev)
             x[:, H - 1] = torch.tensor(1.0, dtype=torch.bfloat16).view(torch.int16)
-        layers.append(MoeInt4Layer(w, k, shared=shared))
+        layers.append(MoeInt4Layer(w, k, group=args.group, shared=shared))
         xs.append(x)
     ws = layers[0].workspace(T)
     for lay in layers:
@@ -272,10 +274,10 @@ def main():
     dist = np.array([distinct[l] for l in visited], dtype=np.float64)
     d_mean = float(np.mean(dist))
     sh_bytes = acc.shared_int6_bytes() if cfg["shared"] else 0
-    layer_bytes = np.mean([acc.layer_bytes(T, d, shared_bytes=sh_bytes) for d in dist])
+    layer_bytes = np.mean([acc.layer_bytes(T, d, group=args.group, shared_bytes=sh_bytes) for d in dist])
     S = T * k
-    expert_w13 = 2 * I * H // 2 + 2 * I * (H // 128) * 2
-    expert_w2 = H * I // 2 + H * (I // 128) * 2
+    expert_w13 = 2 * I * H // 2 + 2 * I * (H // args.group) * 2
+    expert_w2 = H * I // 2 + H * (I // args.group) * 2
     stage_bytes = {"route": acc.router_bytes() + T * H * 2,
                    "gate_up": d_mean * expert_w13 + T * H * 2 + S * I * 2,
                    "down_combine": d_mean * expert_w2 + S * I * 2 + T * H * 2 + sh_bytes}
@@ -327,7 +329,7 @@ def main():
         "dtype": "w4a16 (int4 weights, bf16 activations, fp32 accumulation)",
         "data": "synthetic (seeded, device-generated weights and activations)",
         "config": {"workload": f"{args.config}: one MoE layer forward per step, T={T} tokens, "
-                               f"hidden {H}, {E} experts, top-{k}, intermediate {I}, INT4 group 128"
+                               f"hidden {H}, {E} experts, top-{k}, intermediate {I}, INT4 group {args.group}"
                                + (", Zipf(1.1) routing skew" if cfg["zipf"] else "")
                                + (", INT6 shared expert" if cfg["shared"] else "")
                                + f"; {L} resident layers rotated",
@@ -644,7 +646,7 @@ def cpu_baseline(layer, xs, T, k, budget_s, synth):
     w = layer.w
     host = {"router_w": synth.to_host(w["router_w"]), "w13_packed": synth.to_host(w["w13_packed"]),
             "w13_scales": synth.to_host(w["w13_scales"]), "w2_packed": synth.to_host(w["w2_packed"]),
-            "w2_scales": synth.to_host(w["w2_scales"]), "top_k": k, "group": 128}
+            "w2_scales": synth.to_host(w["w2_scales"]), "top_k": k, "group": layer.group}
     if layer.shared is not None:
         host["shared"] = {kk: (synth.to_host(v) if hasattr(v, "cpu") else v) for kk, v in layer.shared.items()}
     n_tok = 0
