@@ -166,7 +166,8 @@ int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
  * clamped to [-8, 7], and its error is the sum of (w - code * s_j)^2 in fp32
  * in input order.  The first candidate with the smallest error is written.
  * Scales below 2^-126 are not candidates; a group without any (all zeros)
- * gets scale 0 and codes 0.  group must be 128, cols a multiple of it and
+ * gets scale 0 and codes 0.  group is 128 or 64 (the same search over groups
+ * of 64 inputs, for the group-64 weights), cols a multiple of it and
  * rows * cols below 2^31; rows = 0 is a no-op.  Needs no workspace. */
 int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t group,
                           int32_t *packed, uint16_t *scales, void *hip_stream);

@@ -17,8 +17,8 @@ hipError_t launch_decode_forward(const uint16_t *x, const uint16_t *router_w, co
                                  hipEvent_t ev_mid, hipStream_t st);
 hipError_t launch_decode_experts(const ExpertArgs &a, const int32_t *ids, const float *wts,
                                  const Dims &d, const Workspace &ws, hipStream_t st);
-hipError_t launch_quantize_int4(const uint16_t *w, int rows, int K, int32_t *packed, uint16_t *scales,
-                                hipStream_t st);
+hipError_t launch_quantize_int4(const uint16_t *w, int rows, int K, int group, int32_t *packed,
+                                uint16_t *scales, hipStream_t st);
 
 namespace {
 
@@ -368,7 +368,7 @@ int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t
                           int32_t *packed, uint16_t *scales, void *hip_stream)
 {
     g_error.clear();
-    if (group != kGroup) return fail(MOE_INT4_EINVAL, "group=%d, only 128 is supported", group);
+    if (group != 128 && group != 64) return fail(MOE_INT4_EINVAL, "group=%d, INT4 supports 128 and 64", group);
     if (rows < 0 || cols <= 0 || cols % group)
         return fail(MOE_INT4_EINVAL, "rows=%d cols=%d: rows >= 0 and cols a positive multiple of %d",
                     rows, cols, group);
@@ -378,7 +378,7 @@ int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t
     int32_t rc = check_ptrs({{"w", w}, {"packed", packed}, {"scales", scales}});
     if (rc) return rc;
     if ((rc = check_device())) return rc;
-    return launched(launch_quantize_int4(w, rows, cols, packed, scales, (hipStream_t)hip_stream),
+    return launched(launch_quantize_int4(w, rows, cols, group, packed, scales, (hipStream_t)hip_stream),
                     "quantize");
 }
 

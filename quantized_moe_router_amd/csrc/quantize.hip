@@ -3,7 +3,8 @@
 // Edition", section 7): round to nearest, group 128, symmetric, with a
 // per-group search for the clip that gives the smallest squared error.
 //
-// Per group of 128 inputs of one row:
+// Per group of G inputs of one row (G = 128, the pages' choice, or 64 for the
+// group-64 variant of the experts):
 //   amax = max |w|;  for j = 0..19: c_j = 1 - j/40 (1 down to 0.525),
 //   s_j = bf16(fp32(amax * fp32(c_j / 7))) (the clipped magnitude maps to the
 //   largest positive code 7), q = nearest integer to w / s_j with ties to
@@ -23,7 +24,6 @@
 
 namespace moe {
 
-constexpr int kQGroup = 128;
 constexpr int kQClips = 20;
 constexpr int kQThreads = 256;
 
@@ -42,6 +42,7 @@ __device__ __forceinline__ float code_even(float x, float s, float rs)
     return __builtin_amdgcn_fmed3f(q, -8.f, 7.f);
 }
 
+template <int kQGroup>
 __global__ __launch_bounds__(kQThreads, 2) void quantize_int4_kernel(const uint16_t *__restrict__ w,
                                                                   int rows, int K,
                                                                   int32_t *__restrict__ packed,
@@ -113,13 +114,14 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_int4_kernel(const uint1
     scales[gid] = (uint16_t)best_s;
 }
 
-hipError_t launch_quantize_int4(const uint16_t *w, int rows, int K, int32_t *packed, uint16_t *scales,
-                                hipStream_t st)
+hipError_t launch_quantize_int4(const uint16_t *w, int rows, int K, int group, int32_t *packed,
+                                uint16_t *scales, hipStream_t st)
 {
-    const long groups = (long)rows * (K / kQGroup);
+    const long groups = (long)rows * (K / group);
     if (groups == 0) return hipSuccess;
-    quantize_int4_kernel<<<(unsigned)((groups + kQThreads - 1) / kQThreads), kQThreads, 0, st>>>(
-        w, rows, K, packed, scales);
+    const unsigned grid = (unsigned)((groups + kQThreads - 1) / kQThreads);
+    if (group == 64) quantize_int4_kernel<64><<<grid, kQThreads, 0, st>>>(w, rows, K, packed, scales);
+    else quantize_int4_kernel<128><<<grid, kQThreads, 0, st>>>(w, rows, K, packed, scales);
     return hipGetLastError();
 }
 

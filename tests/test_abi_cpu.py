@@ -109,7 +109,7 @@ def test_no_device_is_reported_not_crashed():
 
 
 @pytest.mark.parametrize("rows,cols,group,msg", [
-    (4, 256, 64, "group"),
+    (4, 256, 32, "group"),
     (4, 200, 128, "cols"),
     (-1, 256, 128, "rows"),
     (4, 0, 128, "cols"),

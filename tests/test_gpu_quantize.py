@@ -30,32 +30,34 @@ def gpu():
     yield
 
 
-def gpu_quantize(w: np.ndarray):
+def gpu_quantize(w: np.ndarray, group: int = 128):
     rows, cols = w.shape
     wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).cuda()
     packed = torch.empty((rows, cols // 8), dtype=torch.int32, device="cuda")
-    scales = torch.empty((rows, cols // 128), dtype=torch.int16, device="cuda")
-    B.moe_int4_quantize(wd, rows, cols, packed, scales)
+    scales = torch.empty((rows, cols // group), dtype=torch.int16, device="cuda")
+    B.moe_int4_quantize(wd, rows, cols, packed, scales, group=group)
     torch.cuda.synchronize()
     return packed.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
 
 
-def check(w: np.ndarray, label: str):
-    say(f"quantize case {label}: {w.shape}")
-    gp, gs = gpu_quantize(w)
-    op, os_, _, _ = oracle.quantize_int4(w)
+def check(w: np.ndarray, label: str, group: int = 128):
+    say(f"quantize case {label}: {w.shape} group {group}")
+    gp, gs = gpu_quantize(w, group)
+    op, os_, _, _ = oracle.quantize_int4(w, group)
     bad_s = np.argwhere(gs != os_)
     assert bad_s.size == 0, f"{label}: {len(bad_s)} scales differ, first {bad_s[:3].tolist()}"
     bad_w = np.argwhere(gp != op)
     assert bad_w.size == 0, f"{label}: {len(bad_w)} packed words differ, first {bad_w[:3].tolist()}"
 
 
+@pytest.mark.parametrize("group", [128, 64])
 @pytest.mark.parametrize("rows,cols,seed", [(7, 128, 1), (300, 2560, 2), (64, 640, 3), (1, 4096, 4)])
-def test_quantize_random(rows, cols, seed):
-    check(synth.make_dense_weights(rows, cols, seed), f"random {rows}x{cols}")
+def test_quantize_random(rows, cols, seed, group):
+    check(synth.make_dense_weights(rows, cols, seed), f"random {rows}x{cols}", group)
 
 
-def test_quantize_special_groups():
+@pytest.mark.parametrize("group", [128, 64])
+def test_quantize_special_groups(group):
     f = (np.random.default_rng(9).standard_normal((12, 256)) * 0.02).astype(np.float32)
     f[0] = 0.0                                                  # zero groups
     f[1, :128] = 0.25                                           # constant group
@@ -74,7 +76,7 @@ def test_quantize_special_groups():
     f[9] = -np.abs(f[9])                                        # one-signed
     f[10, :128] = -8 * 2.0 ** -4                                # the code -8 level
     f[10, 1] = 7 * 2.0 ** -4
-    check(synth.bf16_bits(f), "special groups")
+    check(synth.bf16_bits(f), "special groups", group)
 
 
 def test_quantize_real_expert_shapes():

@@ -412,16 +412,18 @@ def _unpack_codes(packed):
     return nib.reshape(u.shape[0], -1) - 8
 
 
-def test_quantizer_reproduces_exact_groups():
-    # values n * 2^-6 with |n| <= 7 and 7 present: the unclipped candidate
-    # has scale exactly 2^-6 and zero error; any clip would saturate the 7s
+@pytest.mark.parametrize("group", [128, 64])
+def test_quantizer_reproduces_exact_groups(group):
+    # values n * 2^-6 with |n| <= 7 and 7 present in every group: the
+    # unclipped candidate has scale exactly 2^-6 and zero error; any clip
+    # would saturate the 7s
     rng = np.random.default_rng(3)
     n = rng.integers(-7, 8, (6, 256))
-    n[:, 0] = 7
+    n[:, ::group] = 7
     n[:, 128] = -7
     n[3, 128] = 7
     w = _to_bf16_bits(n * 2.0 ** -6)
-    packed, scales, e1, _ = oracle.quantize_int4(w)
+    packed, scales, e1, _ = oracle.quantize_int4(w, group)
     assert np.all(_bits_to_float(scales) == 2.0 ** -6)
     assert np.all(e1 == 0)
     assert np.array_equal(_unpack_codes(packed), n)
