@@ -184,3 +184,30 @@ def test_int8_zero_tokens_leaves_output_and_repeat_is_deterministic():
     a = run(x, p, s, T, N, K, G)
     b = run(x, p, s, T, N, K, G)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T,N,K,G", [(1, 4100, 2560, 128), (3, 320, 10240, 64), (8, 9001, 1152, 128),
+                                     (512, 320, 10240, 64)])
+def test_int8_graph_replay_matches_eager(T, N, K, G):
+    # every kernel of the chosen plan captured in a HIP graph: replays, with
+    # eager work and synchronisation between them, equal the eager result
+    # (the split-K partials are fully rewritten by every call: no clearing)
+    layer = synth.make_int8_linear(T, N, K, G, seed=77)
+    x, p, s = to_dev(layer)
+    need = B.moe_int8_linear_workspace_bytes(T, N, K, G)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    eager = torch.empty((T, N), dtype=torch.int16, device="cuda")
+    B.moe_int8_linear(x, p, s, T, N, K, G, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.zeros((T, N), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.moe_int8_linear(x, p, s, T, N, K, G, out, ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.zero_()
+        junk = torch.randn(1024, device="cuda") * (i + 1)   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs"
+        del junk
