@@ -211,3 +211,29 @@ def test_int8_graph_replay_matches_eager(T, N, K, G):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i} differs"
         del junk
+
+
+@pytest.mark.parametrize("T,N,K,G", [(1, 1 << 24, 64, 64), (1 << 20, 64, 64, 64), (2, 3, 65536, 128)])
+def test_int8_maximum_sizes(T, N, K, G):
+    # the largest row count (2^24 rows: the dot GEMV's persistent grid loops
+    # over 4M row blocks), the largest token count (2^20: a GEMM with 8192
+    # token tiles) and the longest rows (K = 65536); the oracle on a seeded
+    # sample of outputs
+    label = f"int8 max T={T} N={N} K={K}"
+    say(label)
+    rng = np.random.default_rng(T + N)
+    gen = torch.Generator(device="cuda").manual_seed(T + N + K)
+    p = torch.randint(-2**31, 2**31 - 1, (N, K // 4), dtype=torch.int32, device="cuda", generator=gen)
+    s = (torch.randn(N, K // G, device="cuda", generator=gen).abs() * 4e-4).to(torch.bfloat16).view(torch.int16)
+    x = torch.randn(T, K, device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+    out = run(x, p, s, T, N, K, G)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 24)]))
+    rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 512)]))
+    xs = x[torch.from_numpy(toks).cuda()].cpu().numpy().view(np.uint16)
+    ps = p[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ss = s[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)
+    o = oracle.int8_linear(xs, ps, ss, G)
+    g = as_f64(out[torch.from_numpy(toks).cuda()][:, torch.from_numpy(rows).cuda()])
+    compare(g, o, label)
+    del p, s, x, out
+    torch.cuda.empty_cache()
