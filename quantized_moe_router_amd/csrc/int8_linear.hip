@@ -21,6 +21,10 @@
 //   * the scale is applied in fp32 to a partial sum that covers one group
 //     only, so code * x products are exact and nothing is rounded before the
 //     fp32 accumulator: no dequantized weight is ever formed;
+//   * the dot-product GEMV skips the bias removal per code pair: it sums the
+//     exact products (1024 + q) x of a 16-input chunk and subtracts 1152
+//     times the chunk's activation sum (staged in LDS with x) once per row
+//     and token;
 //   * few tokens (GEMV): x sits in LDS; a wave streams four weight rows at a
 //     time, every lane on the same 16-byte column chunk of the four rows, so
 //     one LDS read of x serves four rows; rows are spread over the waves of
@@ -52,6 +56,15 @@ __device__ __forceinline__ h2_t code_pair(uint32_t w)
     constexpr uint32_t sel = I == 0 ? 0x04010400u : 0x04030402u;
     const uint32_t p = __builtin_amdgcn_perm(0x64646464u, w, sel);
     return __builtin_bit_cast(h2_t, p) + h2_t{(_Float16)-1152.f, (_Float16)-1152.f};
+}
+
+// Stored bytes 2i and 2i+1 -> fp16 pair (1024 + q), exact; the caller
+// removes the bias (1152 per unit of the activation sum) once per chunk.
+template <int I>
+__device__ __forceinline__ h2_t code_pair_biased(uint32_t w)
+{
+    constexpr uint32_t sel = I == 0 ? 0x04010400u : 0x04030402u;
+    return __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, w, sel));
 }
 
 // 8 bf16 (natural order) -> 8 fp16 (natural order); exact in fp16's normal
@@ -118,10 +131,25 @@ __global__ __launch_bounds__(kGvThreads) void int8_gemv_kernel(const uint16_t *_
     // lanes are consecutive (no bank conflicts)
     extern __shared__ u32x4_t s_x[];
     const int CPR = K >> 4;   // 16-input chunks per row
-    for (int i = threadIdx.x; i < T * CPR * 2; i += kGvThreads) {
-        const int t = i / (2 * CPR), r = i - t * 2 * CPR, c = r >> 1, p = r & 1;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(x + (size_t)t * K + 16 * c + 8 * p);
-        s_x[(t * 2 + p) * CPR + c] = bf16x8_to_f16x8(v);
+    // after the T x 2 x CPR units of x: the fp32 sum of each chunk's 16 fp16
+    // activations, [T][CPR]
+    float *s_xsum = reinterpret_cast<float *>(s_x + T * 2 * CPR);
+    for (int i = threadIdx.x; i < T * CPR; i += kGvThreads) {
+        const int t = i / CPR, c = i - t * CPR;
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + (size_t)t * K + 16 * c);
+        const h2_t one = {(_Float16)1.f, (_Float16)1.f};
+        float sum = 0.f;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const u32x4_t v = bf16x8_to_f16x8(src[p]);
+            s_x[(t * 2 + p) * CPR + c] = v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t e = v[q];
+                sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, e), one, sum, false);
+            }
+        }
+        s_xsum[t * CPR + c] = sum;
     }
     __syncthreads();
 
@@ -163,8 +191,10 @@ __global__ __launch_bounds__(kGvThreads) void int8_gemv_kernel(const uint16_t *_
         const int c0 = i * 64 + lane, c = min(c0, CPR - 1);
         const bool valid = c0 < CPR;
         h2_t xv[T][8];
+        float xsum[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
+            xsum[t] = s_xsum[t * CPR + c];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const u32x4_t v = s_x[(t * 2 + p) * CPR + c];
@@ -182,8 +212,8 @@ __global__ __launch_bounds__(kGvThreads) void int8_gemv_kernel(const uint16_t *_
             h2_t cp[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                cp[2 * q] = code_pair<0>(r.w[j][q]);
-                cp[2 * q + 1] = code_pair<1>(r.w[j][q]);
+                cp[2 * q] = code_pair_biased<0>(r.w[j][q]);
+                cp[2 * q + 1] = code_pair_biased<1>(r.w[j][q]);
             }
             const float sf = valid ? bf16_to_f32(r.s[j]) : 0.f;
 #pragma unroll
@@ -191,7 +221,8 @@ __global__ __launch_bounds__(kGvThreads) void int8_gemv_kernel(const uint16_t *_
                 float p = 0.f;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) p = __builtin_amdgcn_fdot2(cp[q], xv[t][q], p, false);
-                acc[j * T + t] = fmaf(sf, p, acc[j * T + t]);
+                // sum (1024 + q) x - 1152 sum x = sum (q - 128) x
+                acc[j * T + t] = fmaf(sf, fmaf(-1152.f, xsum[t], p), acc[j * T + t]);
             }
         }
         if (i == NI - 1) {
@@ -672,7 +703,8 @@ Int8Plan int8_plan(int T, int N, int K, int G)
     const bool narrow = (N + 3) / 4 < kInt8GemvMaxBlocks && K >= 1024;
     if (T >= 1 && T <= kInt8GemvMaxTokens && narrow) {
         p.gemv = p.rowsplit = true;   // one row per workgroup, K split over its waves
-    } else if (T >= 1 && T <= kInt8GemvMaxTokens && (size_t)T * K * 2 <= kInt8GemvMaxLds) {
+    } else if (T >= 1 && T <= kInt8GemvMaxTokens &&
+               (size_t)T * K * 2 + (size_t)T * (K / 16) * 4 <= kInt8GemvMaxLds) {
         p.gemv = true;                // dot-product GEMV, four rows per wave
     } else if (T > kInt8GemvMaxTokens && T <= kInt8MfmaGemvMaxTokens && !narrow &&
                (size_t)T * (K / 8 + 1) * 16 <= kInt8GemvMaxLds) {
@@ -728,7 +760,7 @@ hipError_t launch_int8_linear(const uint16_t *x, const int32_t *wq, const uint16
         const int wpb = kGvThreads / 64;
         int grid = (nrb + wpb - 1) / wpb;
         grid = grid < kInt8GemvMaxBlocks ? grid : kInt8GemvMaxBlocks;
-        const size_t lds = (size_t)T * K * 2;
+        const size_t lds = (size_t)T * K * 2 + (size_t)T * (K / 16) * 4;
         switch (T) {
         case 1: int8_gemv_kernel<1><<<grid, kGvThreads, lds, st>>>(x, wq, ws, N, K, gshift, out); break;
         case 2: int8_gemv_kernel<2><<<grid, kGvThreads, lds, st>>>(x, wq, ws, N, K, gshift, out); break;
