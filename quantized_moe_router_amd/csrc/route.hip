@@ -50,6 +50,64 @@ __global__ __launch_bounds__(kWave) void permute_small_kernel(const int32_t *__r
                  ws.slot_pos, ws.active);
 }
 
+// Mid-size permutation (kPermChunk < S <= kPermMidWaves * kPermChunk): one
+// workgroup of 16 waves runs the three passes of the large path without a
+// kernel boundary.  Wave w counts the slots [w * chunk, + chunk) into its own
+// LDS histogram; thread e then sums expert e over the chunks, the workgroup
+// scans the totals, and expert e's base in each chunk replaces the count;
+// each wave finally scatters its chunk from those bases (in slot order:
+// stable).
+constexpr int kPermMidWaves = 16;
+static_assert(kPermMidWaves * kWave >= kMaxExperts, "one thread per expert in the scan");
+
+__global__ __launch_bounds__(kPermMidWaves * kWave) void permute_mid_kernel(const int32_t *__restrict__ ids,
+                                                                            Dims d, Workspace ws, RouteOut ro)
+{
+    __shared__ int32_t s_run[kPermMidWaves][kMaxExperts];
+    __shared__ int s_sum[kPermMidWaves], s_nz[kPermMidWaves];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int E = d.E, S = d.S;
+    const int chunk = (S + kPermMidWaves - 1) / kPermMidWaves;   // <= kPermChunk
+    const int beg = min(S, wave * chunk), end = min(S, beg + chunk);
+    for (int e = lane; e < E; e += kWave) s_run[wave][e] = 0;
+    wave_count(ids, beg, end, E, lane, s_run[wave]);
+    __syncthreads();
+    const int e = tid;   // kPermMidWaves * kWave = 1024 = kMaxExperts threads
+    int total = 0;
+    if (e < E)
+        for (int w = 0; w < kPermMidWaves; ++w) total += s_run[w][e];
+    const int nz = (e < E && total > 0) ? 1 : 0;
+    const int incl = wave_incl_scan(total, lane), nz_incl = wave_incl_scan(nz, lane);
+    if (lane == kWave - 1) {
+        s_sum[wave] = incl;
+        s_nz[wave] = nz_incl;
+    }
+    __syncthreads();
+    int base = 0, nz_base = 0;
+    for (int w = 0; w < wave; ++w) {
+        base += s_sum[w];
+        nz_base += s_nz[w];
+    }
+    const int off = base + incl - total, nz_pos = nz_base + nz_incl - nz;
+    if (e < E) {
+        ro.counts[e] = total;
+        ro.offsets[e] = off;
+        if (nz) ws.active[1 + nz_pos] = e;
+        int run = off;
+        for (int w = 0; w < kPermMidWaves; ++w) {
+            const int c = s_run[w][e];
+            s_run[w][e] = run;
+            run += c;
+        }
+    }
+    if (e == E - 1) {
+        ro.offsets[E] = S;
+        ws.active[0] = nz_pos + nz;
+    }
+    __syncthreads();
+    wave_scatter(ids, beg, end, E, lane, s_run[wave], ro.sorted_slots, ws.slot_pos);
+}
+
 // Large permutation, pass 1: per-chunk histograms (one wave per chunk).
 __global__ __launch_bounds__(kWave) void perm_hist_kernel(const int32_t *__restrict__ ids, Dims d,
                                                           Workspace ws)
@@ -131,6 +189,10 @@ hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro
 {
     if (d.S <= kPermChunk) {
         permute_small_kernel<<<1, kWave, 0, st>>>(ro.ids, d, ws, ro);
+        return hipGetLastError();
+    }
+    if (d.S <= kPermMidWaves * kPermChunk) {
+        permute_mid_kernel<<<1, kPermMidWaves * kWave, 0, st>>>(ro.ids, d, ws, ro);
         return hipGetLastError();
     }
     const int chunk = perm_chunk(d.S), nchunks = (d.S + chunk - 1) / chunk;
