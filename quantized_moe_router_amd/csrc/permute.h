@@ -75,14 +75,12 @@ __device__ inline void wave_count(const int32_t *ids, int beg, int end, int E, i
 }
 
 // Place slots [beg, end) at run[id] + (rank among equal ids), advancing run[].
-// One wave; end - beg <= kPermChunk.
-__device__ inline void wave_scatter(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run,
-                             int32_t *sorted_slots, int32_t *slot_pos)
+// One wave; end - beg <= kPermChunk; idv as loaded by load_chunk_ids.
+__device__ inline void wave_scatter_ids(const int (&idv)[kPermPer], int beg, int end, int E, int lane,
+                                        int32_t *run, int32_t *sorted_slots, int32_t *slot_pos)
 {
     if (end <= beg) return;
     const int nbits = id_bits(E);
-    int idv[kPermPer];
-    load_chunk_ids(ids, beg, end, E, lane, idv);
 #pragma unroll
     for (int j = 0; j < kPermPer; ++j) {
         const int base = beg + kWave * j;
@@ -99,6 +97,15 @@ __device__ inline void wave_scatter(const int32_t *ids, int beg, int end, int E,
         }
         if (valid && below == 0) run[id] += __popcll(m);
     }
+}
+
+__device__ inline void wave_scatter(const int32_t *ids, int beg, int end, int E, int lane, int32_t *run,
+                             int32_t *sorted_slots, int32_t *slot_pos)
+{
+    if (end <= beg) return;
+    int idv[kPermPer];
+    load_chunk_ids(ids, beg, end, E, lane, idv);
+    wave_scatter_ids(idv, beg, end, E, lane, run, sorted_slots, slot_pos);
 }
 
 // counts -> offsets (exclusive) and the active-expert list; turns run[] into

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kWave) void permute_small_kernel(const int32_t *__r
 // Mid-size permutation (kPermChunk < S <= kPermMidWaves * kPermChunk): one
 // workgroup of 16 waves runs the three passes of the large path without a
 // kernel boundary.  Wave w counts the slots [w * chunk, + chunk) into its own
-// LDS histogram; thread e then sums expert e over the chunks, the workgroup
+// LDS histogram (LDS atomics: a count needs no ranking); thread e then sums expert e over the chunks, the workgroup
 // scans the totals, and expert e's base in each chunk replaces the count;
 // each wave finally scatters its chunk from those bases (in slot order:
 // stable).
@@ -69,8 +69,16 @@ __global__ __launch_bounds__(kPermMidWaves * kWave) void permute_mid_kernel(cons
     const int E = d.E, S = d.S;
     const int chunk = (S + kPermMidWaves - 1) / kPermMidWaves;   // <= kPermChunk
     const int beg = min(S, wave * chunk), end = min(S, beg + chunk);
+    // the chunk's ids stay in registers for the scatter; the count needs no
+    // ranking, so it is one LDS atomic per slot
+    int idv[kPermPer];
+    load_chunk_ids(ids, beg, end, E, lane, idv);
     for (int e = lane; e < E; e += kWave) s_run[wave][e] = 0;
-    wave_count(ids, beg, end, E, lane, s_run[wave]);
+#pragma unroll
+    for (int j = 0; j < kPermPer; ++j) {
+        if (beg + kWave * j >= end) break;   // uniform
+        if (beg + kWave * j + lane < end) atomicAdd(&s_run[wave][idv[j]], 1);
+    }
     __syncthreads();
     const int e = tid;   // kPermMidWaves * kWave = 1024 = kMaxExperts threads
     int total = 0;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(kPermMidWaves * kWave) void permute_mid_kernel(cons
         ws.active[0] = nz_pos + nz;
     }
     __syncthreads();
-    wave_scatter(ids, beg, end, E, lane, s_run[wave], ro.sorted_slots, ws.slot_pos);
+    wave_scatter_ids(idv, beg, end, E, lane, s_run[wave], ro.sorted_slots, ws.slot_pos);
 }
 
 // Large permutation, pass 1: per-chunk histograms (one wave per chunk).
