@@ -125,7 +125,14 @@ __global__ __launch_bounds__(kWave) void perm_hist_kernel(const int32_t *__restr
     for (int e = lane; e < d.E; e += kWave) s_run[e] = 0;
     const int chunk = perm_chunk(d.S);
     int beg = c * chunk, end = min(d.S, beg + chunk);
-    wave_count(ids, beg, end, d.E, lane, s_run);
+    // a count needs no ranking: one LDS atomic per slot
+    int idv[kPermPer];
+    load_chunk_ids(ids, beg, end, d.E, lane, idv);
+#pragma unroll
+    for (int j = 0; j < kPermPer; ++j) {
+        if (beg + kWave * j >= end) break;   // uniform
+        if (beg + kWave * j + lane < end) atomicAdd(&s_run[idv[j]], 1);
+    }
     for (int e = lane; e < d.E; e += kWave) ws.chunk_hist[(size_t)c * d.E + e] = s_run[e];
 }
 
@@ -137,14 +144,16 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
     __shared__ int s_sum[16], s_nz[16];
     const int e = threadIdx.x, lane = e & (kWave - 1), wave = e >> 6;
     const int ec = e < d.E ? e : 0;
-    // eight chunks' loads in flight per pass (clamped addresses), summed in order
+    // kScanBatch chunks' loads in flight per pass (clamped addresses), summed
+    // in order
+    constexpr int kScanBatch = 32;
     int total = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {
-        int v[8];
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+        int v[kScanBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + ec];
+        for (int u = 0; u < kScanBatch; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + ec];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) total += c0 + u < nchunks ? v[u] : 0;
+        for (int u = 0; u < kScanBatch; ++u) total += c0 + u < nchunks ? v[u] : 0;
     }
     if (e >= d.E) total = 0;
     int nz = (e < d.E && total > 0) ? 1 : 0;
@@ -160,12 +169,12 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
         ro.offsets[e] = off;
         if (nz) ws.active[1 + nz_pos] = e;
         int run = off;
-        for (int c0 = 0; c0 < nchunks; c0 += 8) {
-            int v[8];
+        for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+            int v[kScanBatch];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + e];
+            for (int u = 0; u < kScanBatch; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < kScanBatch; ++u)
                 if (c0 + u < nchunks) {
                     ws.chunk_hist[(size_t)(c0 + u) * d.E + e] = run;
                     run += v[u];

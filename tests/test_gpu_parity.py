@@ -348,3 +348,11 @@ def test_group64_real_width(T, shared):
     host = synth.make_layer(shape, seed=600 + T, shared=shared)
     toks = None if T <= 64 else np.arange(0, T, 7)
     run_and_check(host, tokens=toks, label=f"group64 real-width T={T}")
+
+
+def test_large_permutation_many_experts():
+    # 700 tokens x top-32 over 1000 experts: 22400 slots, past the
+    # one-workgroup permutation (16384), so the three-pass path runs with
+    # nearly the largest expert count
+    shape = synth.LayerShape(tokens=700, hidden=256, experts=1000, top_k=32, inter=128)
+    run_and_check(synth.make_layer(shape, seed=4242), label="large permutation, E=1000, k=32")
