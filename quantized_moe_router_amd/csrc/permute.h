@@ -148,9 +148,19 @@ __device__ inline void wave_permute(const int32_t *ids, int S, int E, int lane, 
                              int32_t *slot_pos, int32_t *active)
 {
     for (int e = lane; e < E; e += kWave) run[e] = 0;
-    wave_count(ids, 0, S, E, lane, run);
+    // the ids are loaded once, counted with one LDS atomic each (a count
+    // needs no ranking) and kept in registers for the scatter
+    int idv[kPermPer];
+    if (S > 0) {
+        load_chunk_ids(ids, 0, S, E, lane, idv);
+#pragma unroll
+        for (int j = 0; j < kPermPer; ++j) {
+            if (kWave * j >= S) break;   // uniform
+            if (kWave * j + lane < S) atomicAdd(&run[idv[j]], 1);
+        }
+    }
     wave_offsets(E, S, lane, run, counts, offsets, active);
-    wave_scatter(ids, 0, S, E, lane, run, sorted_slots, slot_pos);
+    if (S > 0) wave_scatter_ids(idv, 0, S, E, lane, run, sorted_slots, slot_pos);
 }
 
 }  // namespace moe
