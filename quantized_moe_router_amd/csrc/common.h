@@ -368,6 +368,17 @@ inline int router_ksplit(const Dims &d)
 // slots per expert are few) in pairs, pairs dealt round-robin to the 8 XCDs,
 // 16 slots per round.  At most S / 64 + 2 E tile positions are used (each
 // expert's tiles rounded up to a pair), which this bound covers.
+// Rows per routed GEMM tile: 64 when the slots per expert are few.
+inline int routed_tile_rows(const Dims &d) { return (long)d.S < 32L * d.E ? 64 : 128; }
+
+// Permutations of kPermChunk < S <= kPermMidWaves * kPermChunk run in one
+// workgroup of kPermMidWaves waves, which also builds the GEMM tile list.
+constexpr int kPermMidWaves = 16;
+inline bool permute_builds_tiles(const Dims &d)
+{
+    return d.S > kPermChunk && d.S <= kPermMidWaves * kPermChunk;
+}
+
 inline size_t routed_tile_slots(const Dims &d)
 {
     const size_t pairs = ((size_t)d.S + 63) / 64 / 2 + (size_t)d.E + 1;

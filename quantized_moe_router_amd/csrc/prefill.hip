@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "int6.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -619,64 +620,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint1
         }
 }
 
-// Tile list of the grouped GEMMs.  Expert e has ceil(count_e / 128) row
-// tiles (e | mblock << 16).  The list is a sequence of pairs of tiles: first
-// the experts with two or more tiles, each rounded up to whole pairs (an odd
-// count leaves one empty slot, -1), then the one-tile experts, two to a pair.
-// Pair q goes to XCD q % 8 as list slots (2 (q / 8) + j) * 8 + q % 8, j = 0, 1.
-// The GEMM gives list slot t to workgroups on XCD t % 8, in order, so the row
-// tiles of a pair run on one XCD at about the same time and share that
-// expert's weights through its L2; a large expert still spreads over the
-// XCDs two tiles at a time.  One workgroup of 1024.
-__device__ __forceinline__ int tile_slot(int pos)   // list slot of tile position pos
-{
-    const int q = pos >> 1;
-    return (2 * (q >> 3) + (pos & 1)) * 8 + (q & 7);
-}
-
-__device__ __forceinline__ int block_excl_sum(int v, int *s_sum, int &total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    __syncthreads();
-    if (lane == 63) s_sum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    total = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-        base += w < wave ? s_sum[w] : 0;
-        total += s_sum[w];
-    }
-    return base + incl - v;
-}
-
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ counts,
                                                            const int32_t *__restrict__ offsets, int E,
                                                            int nslots, int mt, int4 *__restrict__ tiles)
 {
     __shared__ int s_sum[16];
     const int e = threadIdx.x;
-    const int cnt = e < E ? counts[e] : 0;
-    const int nt = (cnt + mt - 1) / mt;
-    const int multi = nt >= 2 ? (nt + 1) & ~1 : 0;   // positions of a multi-tile expert
-    int nmulti, nsingle;
-    const int pm = block_excl_sum(multi, s_sum, nmulti);
-    const int ps = block_excl_sum(nt == 1 ? 1 : 0, s_sum, nsingle);
-    const int off = e < E ? offsets[e] : 0;
-    auto entry = [&](int i) { return make_int4(e | (i << 16), off + i * mt, min(mt, cnt - i * mt), 0); };
-    if (nt >= 2) {
-        for (int i = 0; i < multi; ++i) tiles[tile_slot(pm + i)] = i < nt ? entry(i) : make_int4(-1, 0, 0, 0);
-    } else if (nt == 1) {
-        tiles[tile_slot(nmulti + ps)] = entry(0);
-    }
-    // every other slot the GEMM grid covers is empty
-    const int used = nmulti + nsingle;
-    for (int pos = used + (int)threadIdx.x; pos < nslots; pos += blockDim.x) tiles[tile_slot(pos)] = make_int4(-1, 0, 0, 0);
+    build_tile_list(e < E ? counts[e] : 0, e < E ? offsets[e] : 0, nslots, mt, tiles, s_sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -720,10 +670,13 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     hipError_t e;
     const size_t xn8 = (size_t)d.T * d.H / 8;
     convert_x_kernel<<<(unsigned)((xn8 + 255) / 256), 256, 0, st>>>(a.x, ws.xh, xn8);
-    const bool small = (long)d.S < 32L * d.E;
-    build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, ro.offsets, d.E, (int)routed_tile_slots(d),
-                                           small ? 64 : kMT, ws.tiles);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const bool small = routed_tile_rows(d) < kMT;
+    // the one-workgroup permutation builds the list itself
+    if (!permute_builds_tiles(d)) {
+        build_tiles_kernel<<<1, 1024, 0, st>>>(ro.counts, ro.offsets, d.E, (int)routed_tile_slots(d),
+                                               routed_tile_rows(d), ws.tiles);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     uint16_t *y = ws.y;
     // routed gate/up -> h (sorted slot order)
     const int tmax = (int)routed_tile_slots(d);

@@ -15,6 +15,7 @@
 // Logits stay fp32 (the page keys on bf16 logits; fp32 avoids manufacturing
 // ties).  Everything here is integer-exact except the fp32 sums and exp.
 #include "permute.h"
+#include "tiles.h"
 #include "topk.h"
 
 namespace moe {
@@ -57,11 +58,11 @@ __global__ __launch_bounds__(kWave) void permute_small_kernel(const int32_t *__r
 // scans the totals, and expert e's base in each chunk replaces the count;
 // each wave finally scatters its chunk from those bases (in slot order:
 // stable).
-constexpr int kPermMidWaves = 16;
 static_assert(kPermMidWaves * kWave >= kMaxExperts, "one thread per expert in the scan");
 
 __global__ __launch_bounds__(kPermMidWaves * kWave) void permute_mid_kernel(const int32_t *__restrict__ ids,
-                                                                            Dims d, Workspace ws, RouteOut ro)
+                                                                            Dims d, Workspace ws, RouteOut ro,
+                                                                            int nslots, int mt)
 {
     __shared__ int32_t s_run[kPermMidWaves][kMaxExperts];
     __shared__ int s_sum[kPermMidWaves], s_nz[kPermMidWaves];
@@ -114,6 +115,9 @@ __global__ __launch_bounds__(kPermMidWaves * kWave) void permute_mid_kernel(cons
     }
     __syncthreads();
     wave_scatter_ids(idv, beg, end, E, lane, s_run[wave], ro.sorted_slots, ws.slot_pos);
+    // the grouped GEMMs' tile list from this thread's (expert e's) count and
+    // offset
+    build_tile_list(e < E ? total : 0, e < E ? off : 0, nslots, mt, ws.tiles, s_sum);
 }
 
 // Large permutation, pass 1: per-chunk histograms (one wave per chunk).
@@ -208,8 +212,9 @@ hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro
         permute_small_kernel<<<1, kWave, 0, st>>>(ro.ids, d, ws, ro);
         return hipGetLastError();
     }
-    if (d.S <= kPermMidWaves * kPermChunk) {
-        permute_mid_kernel<<<1, kPermMidWaves * kWave, 0, st>>>(ro.ids, d, ws, ro);
+    if (permute_builds_tiles(d)) {
+        permute_mid_kernel<<<1, kPermMidWaves * kWave, 0, st>>>(ro.ids, d, ws, ro, (int)routed_tile_slots(d),
+                                                                routed_tile_rows(d));
         return hipGetLastError();
     }
     const int chunk = perm_chunk(d.S), nchunks = (d.S + chunk - 1) / chunk;

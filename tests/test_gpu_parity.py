@@ -144,7 +144,7 @@ def test_zero_tokens_is_a_no_op():
     assert (out == 7).all()
 
 
-@pytest.mark.parametrize("T", [6, 50])
+@pytest.mark.parametrize("T", [6, 50, 600])
 def test_caller_routing_entry(T):
     """moe_int4_experts under arbitrary caller routing (distinct ids per token)."""
     shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=3, inter=128)
