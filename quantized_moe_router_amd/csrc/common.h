@@ -399,8 +399,10 @@ struct RouteOut {
     int32_t *sorted_slots;
 };
 
+// convert_x (many-token routing only): the top-k kernel also writes x in the
+// gate/up GEMMs' fp16 pair order to ws.xh
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
-                        const Workspace &ws, const RouteOut &ro, hipStream_t st);
+                        const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x = false);
 hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro,
                           hipStream_t st);
 
@@ -423,8 +425,26 @@ struct ExpertArgs {
 // Many-token experts: grouped GEMMs (gate/up, then down + combine), with the
 // shared expert when present.  `ev_mid` (may be null) is recorded between the
 // gate/up and down projections.
+// x_converted: ws.xh already holds x in fp16 pair order (from the routing)
 hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid);
+                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid,
+                                  bool x_converted = false);
+
+// bf16 octet (natural order) -> fp16 octet in pair order.
+__device__ __forceinline__ uint4 bf16_octet_to_f16_pairs(uint4 v)
+{
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // element j is in dword j/2, element j+4 in dword 2 + j/2
+        const uint32_t a = in[j >> 1], b = in[2 + (j >> 1)];
+        const float fa = __uint_as_float((j & 1) ? (a & 0xFFFF0000u) : (a << 16));
+        const float fb = __uint_as_float((j & 1) ? (b & 0xFFFF0000u) : (b << 16));
+        out[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
 
 // ---------------------------------------------------------------------------
 // INT8 W8A16 linear layer (int8_linear.hip)

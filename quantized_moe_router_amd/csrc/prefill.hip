@@ -130,22 +130,6 @@ __device__ __forceinline__ f16x8_t dequant_int6_octet(const uint32_t w[7], h2_t 
     return out;
 }
 
-// bf16 octet (natural order) -> fp16 octet in pair order.
-__device__ __forceinline__ uint4 bf16_octet_to_f16_pairs(uint4 v)
-{
-    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-    uint32_t out[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // element j is in dword j/2, element j+4 in dword 2 + j/2
-        const uint32_t a = in[j >> 1], b = in[2 + (j >> 1)];
-        const float fa = __uint_as_float((j & 1) ? (a & 0xFFFF0000u) : (a << 16));
-        const float fb = __uint_as_float((j & 1) ? (b & 0xFFFF0000u) : (b << 16));
-        out[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa, fb));
-    }
-    return make_uint4(out[0], out[1], out[2], out[3]);
-}
-
 // xh[t][:] = x[t][:] as fp16 in nibble-pair order, once per forward: the
 // gate/up GEMMs read each token row once per weight block, so converting here
 // saves that many conversions.
@@ -665,11 +649,11 @@ static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hi
 }
 
 hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid)
+                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid, bool x_converted)
 {
     hipError_t e;
     const size_t xn8 = (size_t)d.T * d.H / 8;
-    convert_x_kernel<<<(unsigned)((xn8 + 255) / 256), 256, 0, st>>>(a.x, ws.xh, xn8);
+    if (!x_converted) convert_x_kernel<<<(unsigned)((xn8 + 255) / 256), 256, 0, st>>>(a.x, ws.xh, xn8);
     const bool small = routed_tile_rows(d) < kMT;
     // the one-workgroup permutation builds the list itself
     if (!permute_builds_tiles(d)) {

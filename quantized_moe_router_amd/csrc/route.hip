@@ -27,18 +27,37 @@ namespace moe {
 // One wave per token.
 // The logits arrive as nsplit partial sums over H ([split][T][E]), added here
 // in split order.
+// With xh given, the wave also writes its token's x row to xh in the gate/up
+// GEMMs' fp16 pair order: the row's loads are issued before the selection
+// and stored after it, so the conversion rides on the selection's latency
+// instead of taking a kernel of its own.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int nsplit, Dims d,
-                                                   int32_t *ids, float *weights)
+                                                   int32_t *ids, float *weights,
+                                                   const uint16_t *__restrict__ x, uint16_t *__restrict__ xh)
 {
     __shared__ uint32_t s_topk[4][kTopkLds];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= d.T) return;
+    constexpr int kXo = kMaxHidden / 8 / kWave;   // octets of a row per lane
+    const int n8 = d.H / 8;
+    uint4 xo[kXo];
+    if (xh) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d.H);
+#pragma unroll
+        for (int j = 0; j < kXo; ++j) xo[j] = src[min(lane + kWave * j, n8 - 1)];
+    }
     const TopkLane r = topk_any(logits + (size_t)t * d.E, nsplit, (size_t)d.T * d.E, d.E, d.k, lane,
                                 s_topk[wave]);
     if (lane < d.k) {
         ids[(size_t)t * d.k + lane] = r.id;
         weights[(size_t)t * d.k + lane] = r.w;
+    }
+    if (xh) {
+        uint4 *dst = reinterpret_cast<uint4 *>(xh + (size_t)t * d.H);
+#pragma unroll
+        for (int j = 0; j < kXo; ++j)
+            if (lane + kWave * j < n8) dst[lane + kWave * j] = bf16_octet_to_f16_pairs(xo[j]);
     }
 }
 
@@ -230,12 +249,13 @@ hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const
                               float *logits, hipStream_t st);
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
-                        const Workspace &ws, const RouteOut &ro, hipStream_t st)
+                        const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x)
 {
     if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
     hipError_t e = launch_router_mfma(x, router_w, d, ws.logits, st);
     if (e != hipSuccess) return e;
-    topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, router_ksplit(d), d, ro.ids, ro.weights);
+    topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, router_ksplit(d), d, ro.ids, ro.weights, x,
+                                               convert_x ? ws.xh : nullptr);
     return launch_permute(d, ws, ro, st);
 }
 
