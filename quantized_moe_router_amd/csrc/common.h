@@ -372,12 +372,10 @@ inline int router_ksplit(const Dims &d)
 inline int routed_tile_rows(const Dims &d) { return (long)d.S < 32L * d.E ? 64 : 128; }
 
 // Permutations of kPermChunk < S <= kPermMidWaves * kPermChunk run in one
-// workgroup of kPermMidWaves waves, which also builds the GEMM tile list.
+// workgroup of kPermMidWaves waves; larger ones scan in one workgroup.  Both
+// of those workgroups also build the GEMM tile list.
 constexpr int kPermMidWaves = 16;
-inline bool permute_builds_tiles(const Dims &d)
-{
-    return d.S > kPermChunk && d.S <= kPermMidWaves * kPermChunk;
-}
+inline bool permute_builds_tiles(const Dims &d) { return d.S > kPermChunk; }
 
 inline size_t routed_tile_slots(const Dims &d)
 {

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kWave) void perm_hist_kernel(const int32_t *__restr
 // Pass 2: per-expert totals, offsets, active list, and each chunk's base.
 // One workgroup of 1024 threads, thread e owns expert e.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, RouteOut ro,
-                                                         int nchunks)
+                                                         int nchunks, int nslots, int mt)
 {
     __shared__ int s_sum[16], s_nz[16];
     const int e = threadIdx.x, lane = e & (kWave - 1), wave = e >> 6;
@@ -208,6 +208,9 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
         ro.offsets[d.E] = d.S;
         ws.active[0] = nz_pos + nz;
     }
+    // the grouped GEMMs' tile list from this thread's (expert e's) count and
+    // offset
+    build_tile_list(e < d.E ? total : 0, e < d.E ? off : 0, nslots, mt, ws.tiles, s_sum);
 }
 
 // Pass 3: scatter each chunk's slots from its per-expert bases.
@@ -231,14 +234,14 @@ hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro
         permute_small_kernel<<<1, kWave, 0, st>>>(ro.ids, d, ws, ro);
         return hipGetLastError();
     }
-    if (permute_builds_tiles(d)) {
+    if (d.S <= kPermMidWaves * kPermChunk) {
         permute_mid_kernel<<<1, kPermMidWaves * kWave, 0, st>>>(ro.ids, d, ws, ro, (int)routed_tile_slots(d),
                                                                 routed_tile_rows(d));
         return hipGetLastError();
     }
     const int chunk = perm_chunk(d.S), nchunks = (d.S + chunk - 1) / chunk;
     perm_hist_kernel<<<nchunks, kWave, 0, st>>>(ro.ids, d, ws);
-    perm_scan_kernel<<<1, 1024, 0, st>>>(d, ws, ro, nchunks);
+    perm_scan_kernel<<<1, 1024, 0, st>>>(d, ws, ro, nchunks, (int)routed_tile_slots(d), routed_tile_rows(d));
     perm_scatter_kernel<<<nchunks, kWave, 0, st>>>(ro.ids, d, ws, ro);
     return hipGetLastError();
 }
