@@ -334,7 +334,7 @@ static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
             return rc;
     } else {
         RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
-        if ((rc = launched(launch_route(x, router_w, d, ws, ro, st, true), "route"))) return rc;
+        if ((rc = launched(launch_route(x, router_w, d, ws, ro, st, true, a.sh_gate), "route"))) return rc;
         if (ev[1] && (rc = launched(hipEventRecord(ev[1], st), "event"))) return rc;
         if ((rc = launched(launch_prefill_experts(a, d, ws, ro, st, ev[2], true), "experts"))) return rc;
     }

@@ -398,9 +398,11 @@ struct RouteOut {
 };
 
 // convert_x (many-token routing only): the top-k kernel also writes x in the
-// gate/up GEMMs' fp16 pair order to ws.xh
+// gate/up GEMMs' fp16 pair order to ws.xh and, given gate_w, the shared
+// expert's gate logits to ws.shared_gate
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
-                        const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x = false);
+                        const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x = false,
+                        const uint16_t *gate_w = nullptr);
 hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro,
                           hipStream_t st);
 
@@ -423,7 +425,8 @@ struct ExpertArgs {
 // Many-token experts: grouped GEMMs (gate/up, then down + combine), with the
 // shared expert when present.  `ev_mid` (may be null) is recorded between the
 // gate/up and down projections.
-// x_converted: ws.xh already holds x in fp16 pair order (from the routing)
+// x_converted: ws.xh already holds x in fp16 pair order (from the routing),
+// and ws.shared_gate the shared expert's gate logits when it has one
 hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
                                   const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid,
                                   bool x_converted = false);

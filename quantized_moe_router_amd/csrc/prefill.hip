@@ -683,7 +683,8 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st, d.gsh == 1)) != hipSuccess) return e;
     if (d.sh_I > 0) {
         // shared expert: gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
-        if ((e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;
+        if (!x_converted && (e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess)
+            return e;
         GemmArgs gs{};
         gs.x = ws.xh; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
         gs.T = d.T; gs.H = d.H; gs.I = d.sh_I; gs.k = d.k; gs.K = d.H;

@@ -30,10 +30,14 @@ namespace moe {
 // With xh given, the wave also writes its token's x row to xh in the gate/up
 // GEMMs' fp16 pair order: the row's loads are issued before the selection
 // and stored after it, so the conversion rides on the selection's latency
-// instead of taking a kernel of its own.
+// instead of taking a kernel of its own.  With gate_w given as well, it also
+// forms the shared expert's gate logit x . gate_w from the same registers
+// (bf16 products, fp32 sums in the order of the stand-alone gate kernel).
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int nsplit, Dims d,
                                                    int32_t *ids, float *weights,
-                                                   const uint16_t *__restrict__ x, uint16_t *__restrict__ xh)
+                                                   const uint16_t *__restrict__ x, uint16_t *__restrict__ xh,
+                                                   const uint16_t *__restrict__ gate_w,
+                                                   float *__restrict__ gate_out)
 {
     __shared__ uint32_t s_topk[4][kTopkLds];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
@@ -58,6 +62,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 #pragma unroll
         for (int j = 0; j < kXo; ++j)
             if (lane + kWave * j < n8) dst[lane + kWave * j] = bf16_octet_to_f16_pairs(xo[j]);
+        if (gate_w) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < kXo; ++j) {
+                if (lane + kWave * j < n8) {
+                    const uint4 gv = reinterpret_cast<const uint4 *>(gate_w)[lane + kWave * j];
+                    acc = dot2(gv.x, xo[j].x, acc);
+                    acc = dot2(gv.y, xo[j].y, acc);
+                    acc = dot2(gv.z, xo[j].z, acc);
+                    acc = dot2(gv.w, xo[j].w, acc);
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) gate_out[t] = acc;
+        }
     }
 }
 
@@ -252,13 +271,15 @@ hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const
                               float *logits, hipStream_t st);
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
-                        const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x)
+                        const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x,
+                        const uint16_t *gate_w)
 {
     if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
     hipError_t e = launch_router_mfma(x, router_w, d, ws.logits, st);
     if (e != hipSuccess) return e;
     topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, router_ksplit(d), d, ro.ids, ro.weights, x,
-                                               convert_x ? ws.xh : nullptr);
+                                               convert_x ? ws.xh : nullptr, convert_x ? gate_w : nullptr,
+                                               ws.shared_gate);
     return launch_permute(d, ws, ro, st);
 }
 
