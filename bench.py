@@ -1,15 +1,24 @@
 """Benchmark of the INT4 routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config decode1|decode4|decode64|prefill512|prefill8192|quantize64|lmhead1|hc1|hc512]
+                    [--config prefill8192|prefill512|decode1|decode4|decode64|quantize64|lmhead1|hc1|hc512]
 
 A step is one forward of the whole layer (router, top-k, permutation, gate/up
-projection with SiLU-gate, down projection with the weighted combine) over one
-batch of synthetic tokens.  Decode configs rotate over 48 resident layers
-(hidden 2560, 512 experts, top-10, intermediate 640, INT4 group 128; 62 GB),
-each with its own seeded weights and activations, so every step streams its
+projection with SiLU-gate, down projection with the weighted combine, and the
+INT6 shared expert where the workload has one) over one batch of synthetic
+tokens.  The default workload is the largest single-GPU one: 8192 tokens
+through the real-shape layer (hidden 2560, 512 experts, top-10, intermediate
+640, INT4 group 128) plus the always-on INT6 shared expert, rotating over 4
+resident layers.  Decode configs rotate over 48 resident layers (62 GB), each
+with its own seeded weights and activations, so every step streams its
 weights from HBM rather than from the 256 MB last-level cache.  Inputs are
 resident in HBM before timing starts.
+
+The default run also measures, as the extra key `decode48x4`, one decode step
+of the whole 48-layer stack: 4 tokens through all 48 resident layers in
+sequence, fresh activations per layer, reported as sustained HBM GB/s over
+the bytes the method must read (router rows, every touched expert once,
+activations, outputs).
 
 Timed region: exactly K steps replayed from captured HIP graphs, bracketed by
 events.  Per-stage times come from a second pass over the same K steps, run
@@ -64,7 +73,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode1", choices=sorted(CONFIGS))
+    p.add_argument("--config", default="prefill8192", choices=sorted(CONFIGS))
+    p.add_argument("--no-decode48", action="store_true",
+                   help="skip the 48-layer decode step measured beside the default workload")
+    p.add_argument("--decode48-steps", type=int, default=20)
     p.add_argument("--layers", type=int, default=0, help="resident layers (0: config default)")
     p.add_argument("--tokens", type=int, default=0,
                    help="tokens per step (0: config default); for sweeps over the batch size")
@@ -326,7 +338,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "w4a16 (int4 weights, bf16 activations, fp32 accumulation)",
+        "dtype": ("w4a16: int4 weights, bf16 router and activations, fp32 accumulation (GEMV path)"
+                  if decode else
+                  "w4a16 on fp16 MFMA: int4 weights dequantised exactly to fp16, activations converted "
+                  "to fp16, bf16 router MFMA, fp32 accumulation"),
         "data": "synthetic (seeded, device-generated weights and activations)",
         "config": {"workload": f"{args.config}: one MoE layer forward per step, T={T} tokens, "
                                f"hidden {H}, {E} experts, top-{k}, intermediate {I}, INT4 group {args.group}"
@@ -352,7 +367,78 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers[0], xs, T, k, args.cpu_seconds, synth)
+    if args.config == "prefill8192" and not args.no_decode48 and not args.layers and not args.tokens:
+        del layers, xs, ws, out
+        torch.cuda.empty_cache()
+        result["decode48x4"] = bench_decode48(args)
     print(json.dumps(result), flush=True)
+
+
+def bench_decode48(args, T=4, L=48):
+    """One decode step of a 48-layer stack: T tokens through all L resident
+    layers in sequence (each layer its own seeded weights and fresh
+    activations), replayed from one captured HIP graph per step.  Returns
+    the time per step and the sustained HBM rate over the algorithmic bytes
+    (router rows, each touched expert once, activations in and out)."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_router_amd import _binding as B
+    from quantized_moe_router_amd import accounting as acc
+    from quantized_moe_router_amd import synth
+    from quantized_moe_router_amd.layer import MoeInt4Layer
+
+    dev = torch.device("cuda:0")
+    shape = synth.LayerShape(tokens=T)
+    k = shape.top_k
+    layers, xs = [], []
+    for l in range(L):
+        layers.append(MoeInt4Layer(synth.device_weights(shape, seed=l, device=dev), k))
+        xs.append(synth.device_activations(shape, seed=1000 + l, device=dev))
+    ws = layers[0].workspace(T)
+    out = torch.empty(T, shape.hidden, dtype=torch.int16, device=dev)
+    distinct = []
+    for l in range(L):
+        r = layers[l].route(xs[l])
+        distinct.append(int((r["counts"] > 0).sum().item()))
+    step_bytes = sum(acc.layer_bytes(T, d) for d in distinct)
+
+    def step():
+        for l in range(L):
+            lay = layers[l]
+            w = lay.w
+            B.moe_int4_forward(xs[l], w["router_w"], w["w13_packed"], w["w13_scales"], w["w2_packed"],
+                               w["w2_scales"], k, out, lay.shape(T), None, ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    K = max(1, args.decode48_steps)
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    for _ in range(K):
+        g.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    ms = ga.elapsed_time(gb) / K
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    status = B.workspace_status(ws)
+    del g, layers, xs, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"decode step over {L} resident layers in sequence, T={T} tokens per layer, "
+                        "hidden 2560, 512 experts, top-10, intermediate 640, INT4 group 128, "
+                        "fresh activations per layer",
+            "steps": K, "us_per_step": round(ms * 1e3, 2), "us_per_layer": round(ms * 1e3 / L, 3),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "algorithmic_bytes_per_step": int(step_bytes),
+            "distinct_experts_per_layer": round(float(np.mean(distinct)), 2),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": "HIP-graph replay of the 48-layer step, events around the replays",
+            "workspace_status": status}
 
 
 def bench_quantize(args):

@@ -34,15 +34,40 @@
  *     holding code+8 for a code in [-8, 7]; weight = code * scale[row][k/G].
  *   - Workspace: a caller-owned device buffer of at least
  *     moe_int4_workspace_bytes() bytes.  It must be ZERO-FILLED before its
- *     first use; its first 64 KiB (the few-token router's hand-off area,
- *     whatever the shape) are zero again whenever a call completes, so a
+ *     first use.  Its first MOE_INT4_WS_PREFIX_BYTES bytes (the hand-off area
+ *     between workgroups of one launch, the same for every shape) are zero
+ *     again whenever a call completes, except the sticky status word, so a
  *     workspace can be reused without clearing, also across shapes.  Two
- *     calls in flight at the same time need two workspaces.
+ *     calls in flight at the same time need two workspaces.  A call that did
+ *     not complete (a device error, an aborted stream) can leave the area
+ *     non-zero: zero the prefix again before reusing such a workspace.
+ *   - Status word: the uint32 at byte offset MOE_INT4_WS_STATUS_OFFSET of the
+ *     workspace.  The few-token path (T <= 16) hands work between workgroups
+ *     of one launch through bounded waits: a workgroup polls data that
+ *     workgroups with lower block indices publish.  This relies on the
+ *     hardware dispatching a launch's workgroups in increasing block order
+ *     (every earlier workgroup is then resident or finished when a later one
+ *     waits), which AMD GPUs do but the HIP programming model does not
+ *     promise.  A wait that still runs out ORs a MOE_INT4_STATUS_* bit into
+ *     the status word; that call's output is then unreliable.  The library
+ *     never clears the word: a caller that checks it (after the stream
+ *     completes) clears it itself.
+ *   - Numerics.  Products are formed exactly and summed in fp32; the output
+ *     is rounded once, to nearest even, to bf16.  The SwiGLU activation
+ *     a = silu(g) * u is kept in fp16 (round to nearest even, saturating at
+ *     +-65504).  For more than 16 tokens (the matrix-core path) x is also
+ *     converted to fp16, by rounding toward zero: exact for finite bf16
+ *     values of magnitude 2^-17 .. 65504, smaller ones lose low bits (zero
+ *     below 2^-24), larger ones saturate at +-65504; and each slot's weighted
+ *     down-projection row w * (W2_e a) is rounded to fp16 (saturating) before
+ *     a token's rows are added in fp32 in a fixed order.  Up to 16 tokens, x
+ *     is used as bf16 unchanged and the weighted slot rows stay in fp32.
  *
  * Errors: every entry point returns 0 on success or a negative code.  All
  * checks run on the host before anything is enqueued, so a failing call has
  * done no work.  moe_int4_last_error() returns a message for the calling
- * thread's last failure.  No C++ exception crosses this boundary.
+ * thread's last failure.  No C++ exception crosses this boundary.  Failures
+ * on the device are reported in the workspace's status word (above).
  */
 #ifndef MOE_INT4_H
 #define MOE_INT4_H
@@ -60,6 +85,13 @@ extern "C" {
 #define MOE_INT4_EWORKSPACE (-3) /* workspace smaller than required */
 #define MOE_INT4_ELAUNCH (-4)    /* the HIP runtime refused a launch */
 #define MOE_INT4_EDEVICE (-5)    /* no usable gfx950 device */
+
+/* Workspace control prefix and status word (see "Workspace" above). */
+#define MOE_INT4_WS_PREFIX_BYTES 65792u   /* zero between calls, except the status word */
+#define MOE_INT4_WS_STATUS_OFFSET 65536u  /* uint32 sticky status word */
+#define MOE_INT4_STATUS_KEY_WAIT 1u       /* routing gave up waiting for router logits */
+#define MOE_INT4_STATUS_ROUTE_WAIT 2u     /* an expert workgroup gave up waiting for the routing */
+#define MOE_INT4_STATUS_H_WAIT 4u         /* a down-projection workgroup gave up waiting for a */
 
 /* Layer dimensions.  Limits: tokens >= 0 (0 is a no-op); 1 <= top_k <=
  * min(experts, 32); experts <= 1024; group 128 or 64; hidden a multiple of 256,
@@ -154,8 +186,9 @@ int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
                                 void *const *events);
 
 /* Load-time INT4 quantizer ("Running 125B MoE on Three 3090s - vLLM
- * Optimization Edition", section 7: round to nearest, group 128, symmetric,
- * with a per-group search for the clip that minimizes the squared error):
+ * Optimization Edition", section 7, which quantizes the draft head's experts
+ * to symmetric INT4 in groups of 128 by rounding to nearest, choosing each
+ * group's clipping range as the one with the least squared error):
  *   w       bf16  [rows][cols]        in   weights (finite values)
  *   packed  int32 [rows][cols/8]      out  codes in the layout above
  *   scales  bf16  [rows][cols/group]  out

@@ -398,9 +398,9 @@ void oracle_forward(const uint16_t *x, const uint16_t *router_w,
 }
 
 /* ---------------------------------------------------------------------
- * Load-time INT4 quantizer ([VO] section 7: the experts are quantized
- * round-to-nearest, group 128, symmetric, with a per-group search for the
- * clip that minimizes the squared error).
+ * Load-time INT4 quantizer ([VO] section 7: the draft head's experts are
+ * made symmetric INT4 in groups of 128 by rounding to nearest, each group
+ * taking the clipping range whose squared error is least).
  *
  * Readings (the page names the method only):
  *   - candidate clips: twenty ratios c_j = 1 - j/40, j = 0..19 (1 down to

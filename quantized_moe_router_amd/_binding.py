@@ -107,10 +107,29 @@ def workspace_bytes(shape: MoeShape, shared: MoeSharedInt6 | None = None) -> int
     return n.value
 
 
+# Workspace control prefix (include/moe_int4.h): zero between calls, except
+# the sticky status word at WS_STATUS_OFFSET.
+WS_PREFIX_BYTES = 65792
+WS_STATUS_OFFSET = 65536
+STATUS_KEY_WAIT, STATUS_ROUTE_WAIT, STATUS_H_WAIT = 1, 2, 4
+
+
 def new_workspace(shape: MoeShape, shared: MoeSharedInt6 | None = None, device="cuda"):
     """A zero-filled workspace (the library keeps its counters at zero after each call)."""
     import torch
     return torch.zeros(workspace_bytes(shape, shared), dtype=torch.uint8, device=device)
+
+
+def workspace_status(workspace) -> int:
+    """The sticky status word of a workspace (reads device memory: call after
+    the stream has completed)."""
+    w = workspace[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 4].cpu().numpy()
+    return int(w.view("<u4")[0])
+
+
+def workspace_prefix_clean(workspace) -> bool:
+    """Whether the control prefix is back at zero, status word included."""
+    return not bool(workspace[:WS_PREFIX_BYTES].any().item())
 
 
 def moe_int4_route(x, router_w, shape: MoeShape, topk_ids, topk_w, expert_counts,

@@ -39,7 +39,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t dec_keys, logits, ids, weights, counts, offsets, sorted_slots,
+    size_t dec_keys, ctrl, logits, ids, weights, counts, offsets, sorted_slots,
         slot_pos, active, chunk_hist, tiles, h, y, shared_gate, sh_h, xh, xp, xs, total;
 };
 
@@ -54,7 +54,8 @@ Layout layout(const Dims &d)
     };
     const size_t S = (size_t)d.S, T = (size_t)d.T;
     const size_t chunk = (size_t)perm_chunk(d.S), nchunks = (S + chunk - 1) / chunk;
-    L.dec_keys = take(4 * (size_t)kDecodeMaxTokens * kMaxExperts);   // same size for every shape
+    L.dec_keys = take(kKeysBytes);   // the control prefix: same place and size for every shape
+    L.ctrl = take(kCtrlBytes);
     L.logits = take(4 * T * d.E * (size_t)(d.T > kDecodeMaxTokens ? router_ksplit(d) : 1));
     L.ids = take(4 * S);
     L.weights = take(4 * S);
@@ -173,6 +174,7 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
     char *b = static_cast<char *>(ws);
     Workspace w{};
     w.dec_keys = reinterpret_cast<uint32_t *>(b + L.dec_keys);
+    w.ctrl = reinterpret_cast<uint32_t *>(b + L.ctrl);
     w.logits = reinterpret_cast<float *>(b + L.logits);
     w.ids = reinterpret_cast<int32_t *>(b + L.ids);
     w.weights = reinterpret_cast<float *>(b + L.weights);
@@ -220,6 +222,12 @@ int32_t check_int8_shape(int32_t tokens, int32_t n, int32_t k, int32_t group)
 }  // namespace
 
 size_t workspace_size(const Dims &d) { return layout(d).total; }
+
+static_assert(kKeysBytes == MOE_INT4_WS_STATUS_OFFSET, "status word follows the router keys");
+static_assert(kKeysBytes + kCtrlBytes == MOE_INT4_WS_PREFIX_BYTES, "control prefix size");
+static_assert(kStatusKeyWait == MOE_INT4_STATUS_KEY_WAIT && kStatusRouteWait == MOE_INT4_STATUS_ROUTE_WAIT &&
+                  kStatusHWait == MOE_INT4_STATUS_H_WAIT,
+              "status bits");
 
 }  // namespace moe
 

@@ -259,6 +259,11 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v)
 {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Record a failed bounded wait in the sticky status word (a vector atomic).
+__device__ __forceinline__ void set_status(uint32_t *ctrl, uint32_t bit)
+{
+    __hip_atomic_fetch_or(ctrl, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Cross-lane sums with DPP lane moves (VALU only; a shuffle would go through
 // the LDS crossbar with a full wait per step).  Every lane of a quad / row /
@@ -304,9 +309,21 @@ __device__ __forceinline__ float wave_sum(float v)
 // Workspace map.  Every region is 256-byte aligned; counters first so that
 // the zero-state contract covers a fixed prefix.
 // ---------------------------------------------------------------------------
+// The workspace starts with a fixed control prefix, the same for every shape:
+// the few-token router's keys (64 KiB), then 256 bytes of control words.
+// Control word 0 is the sticky status (kStatus* bits, set when a bounded
+// wait gives up; never cleared by the library); the other control words are
+// hand-off counters that are zero between calls.
+constexpr size_t kKeysBytes = 4 * (size_t)kDecodeMaxTokens * kMaxExperts;   // 65536
+constexpr size_t kCtrlBytes = 256;
+constexpr uint32_t kStatusKeyWait = 1u;     // a routing wave gave up waiting for router keys
+constexpr uint32_t kStatusRouteWait = 2u;   // an expert workgroup gave up waiting for the routing
+constexpr uint32_t kStatusHWait = 4u;       // a down-projection workgroup gave up waiting for h
+
 struct Workspace {
     // zero between calls (a fixed prefix of every layout)
     uint32_t *dec_keys;      // [kDecodeMaxTokens * kMaxExperts] decode router keys, 0 = unset
+    uint32_t *ctrl;          // [kCtrlBytes / 4] control words: [0] sticky status, then counters
     // routing
     float *logits;           // [T][E]
     int32_t *ids;            // [T][k]   (forward: internal copy)

@@ -68,21 +68,25 @@ __device__ __forceinline__ uint32_t logit_key(float l)
     return k == 0u ? 1u : k;
 }
 
-// One token's routing from its published keys (one wave).
+// One token's routing from its published keys (one wave).  A wave that gives
+// up waiting sets kStatusKeyWait in the sticky status word and routes on the
+// keys it has (absent keys read as 0, below every logit).
 template <int KPL>
-__device__ TopkLane route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds)
+__device__ TopkLane route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds, uint32_t *ctrl)
 {
     uint32_t val[KPL];
-    for (uint32_t spin = 0; spin < kKeySpinLimit; ++spin) {
-        bool missing = false;
+    bool missing = true;
+    for (uint32_t spin = 0; spin < kKeySpinLimit && missing; ++spin) {
+        bool miss = false;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
             const int e = lane + kWave * i;
             val[i] = e < E ? load_coherent(keys + e) : 0u;
-            missing |= e < E && val[i] == 0u;
+            miss |= e < E && val[i] == 0u;
         }
-        if (!__ballot(missing)) break;
+        missing = __ballot(miss) != 0;
     }
+    if (missing && lane == 0) set_status(ctrl, kStatusKeyWait);
     const TopkLane r = wave_topk_keys<KPL>(val, k, lane, lds);
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
@@ -93,13 +97,13 @@ __device__ TopkLane route_token(uint32_t *keys, int E, int k, int lane, uint32_t
 }
 
 __device__ __forceinline__ TopkLane route_token_any(uint32_t *keys, int E, int k, int lane,
-                                                    uint32_t *lds)
+                                                    uint32_t *lds, uint32_t *ctrl)
 {
-    if (E <= 64) return route_token<1>(keys, E, k, lane, lds);
-    if (E <= 128) return route_token<2>(keys, E, k, lane, lds);
-    if (E <= 256) return route_token<4>(keys, E, k, lane, lds);
-    if (E <= 512) return route_token<8>(keys, E, k, lane, lds);
-    return route_token<16>(keys, E, k, lane, lds);
+    if (E <= 64) return route_token<1>(keys, E, k, lane, lds, ctrl);
+    if (E <= 128) return route_token<2>(keys, E, k, lane, lds, ctrl);
+    if (E <= 256) return route_token<4>(keys, E, k, lane, lds, ctrl);
+    if (E <= 512) return route_token<8>(keys, E, k, lane, lds, ctrl);
+    return route_token<16>(keys, E, k, lane, lds, ctrl);
 }
 
 // x of the T tokens in nibble-pair order (ws.xp) with the sums of its 32-value
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
         if (!publish) return;
         for (int t = wave; t < d.T; t += kRtWaves) {
             const TopkLane tk = route_token_any(r.ws.dec_keys + (size_t)t * d.E, d.E, d.k, lane,
-                                                s_topk[wave]);
+                                                s_topk[wave], r.ws.ctrl);
             if (lane < d.k) {
                 const int id = clamp_expert(tk.id, d.E);
                 r.ro.ids[t * d.k + lane] = id;

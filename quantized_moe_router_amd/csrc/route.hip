@@ -4,9 +4,11 @@
 // Method ("Running 125B MoE on Three 3090s - vLLM Optimization Edition",
 // section 3.3, "MoE block (decode-05)"):
 //   * the router is one GEMV over the bf16 router rows;
-//   * the workgroup that finishes last (found with an acquire-release ticket
-//     taken after its stores) does the top-k, the renormalisation and the
-//     grouping of slots by expert, so no grid-wide barrier kernel is needed;
+//   * the page's router hands its logits to its last CTA, which does the
+//     top-k, the renormalisation and the grouping of slots by expert; here
+//     the few-token router (decode.hip) publishes its logits as keys that a
+//     routing workgroup of the same launch polls, and the many-token path
+//     below runs a top-k kernel and a permutation after the router GEMM;
 //   * top-k keys pack an order-preserving integer image of the logit above
 //     the inverted expert id, so one max yields value and id and equal
 //     logits resolve to the lower id;

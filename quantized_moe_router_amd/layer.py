@@ -35,6 +35,9 @@ class MoeInt4Layer:
                                             device=device or self.w["router_w"].device)
         return self._ws[key]
 
+    def workspaces(self) -> list:
+        return list(self._ws.values())
+
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         T = x.shape[0]
         if out is None:

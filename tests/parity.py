@@ -16,6 +16,9 @@ half-ulp term is the rounding of the exact value to the bf16 output format
 itself: without it the correctly rounded exact result would fail the max
 gate wherever an output exceeds about 5x rms near the bottom of a binade.
 """
+import json
+import os
+
 import numpy as np
 
 import oracle
@@ -80,9 +83,26 @@ def worst(got, ref, n=5):
     return "; ".join(f"{tuple(int(v) for v in r)}: got {got[r]:.6g} ref {ref[r]:.6g}" for r in rows)
 
 
-def check_output(got, ref, max_tol=MAX_TOL, mean_tol=MEAN_TOL):
+def _log_margin(label, mx, mean, raw_mx, max_tol, mean_tol):
+    """Appends one JSON line per comparison to the file named by PARITY_LOG
+    (unset: nothing is written), so the margins of a run can be tabulated."""
+    path = os.environ.get("PARITY_LOG")
+    if not path:
+        return
+    rec = {"case": label or os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0],
+           "max_beyond_half_ulp_over_rms": float(mx), "max_raw_over_rms": float(raw_mx),
+           "mean_rel": float(mean), "max_tol": max_tol, "mean_tol": mean_tol,
+           "max_margin": float(mx / max_tol), "mean_margin": float(mean / mean_tol)}
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
+
+
+def check_output(got, ref, max_tol=MAX_TOL, mean_tol=MEAN_TOL, label=""):
+    """Returns (max beyond half-ulp / rms, mean relative error, raw max / rms)."""
     mx, mean = output_errors(got, ref)
+    raw = np.abs(got - ref).max() / max(np.sqrt(np.mean(ref * ref)), 1e-300)
+    _log_margin(label, mx, mean, raw, max_tol, mean_tol)
     assert mx <= max_tol and mean <= mean_tol, (
         f"max (beyond half-ulp)/rms={mx:.3e} (<= {max_tol}), mean rel={mean:.3e} (<= {mean_tol}); "
         f"rms={np.sqrt(np.mean(ref * ref)):.4g}; worst: {worst(got, ref)}")
-    return mx, mean
+    return mx, mean, raw

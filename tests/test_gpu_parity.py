@@ -78,9 +78,20 @@ def run_and_check(host, tokens=None, real_dev=None, label=""):
         sel = differ[ref["tokens"]]
         got[sel] = got_o[sel]
         say(f"  {sel.sum()} near-tie token(s) compared under oracle routing")
-    mx, mean = check_output(got, ref["out"])
-    say(f"  ok: max/rms={mx:.2e} mean-rel={mean:.2e} exempt-differ={int(differ.sum())}")
+    mx, mean, raw = check_output(got, ref["out"], label=label)
+    say(f"  ok: max(beyond half-ulp)/rms={mx:.2e} raw max/rms={raw:.2e} mean-rel={mean:.2e} "
+        f"exempt-differ={int(differ.sum())}")
+    assert_workspaces_clean(L)
     return out, L, dev
+
+
+def assert_workspaces_clean(L):
+    """After a call completes: the sticky status word is zero (no bounded
+    wait gave up) and the rest of the control prefix is back at zero."""
+    torch.cuda.synchronize()
+    for ws in L.workspaces():
+        assert B.workspace_status(ws) == 0, f"status word {B.workspace_status(ws):#x}"
+        assert B.workspace_prefix_clean(ws), "the workspace control prefix was not returned to zero"
 
 
 # ---------------------------------------------------------------------------
@@ -158,7 +169,8 @@ def test_caller_routing_entry(T):
     torch.cuda.synchronize()
     ref = oracle.experts(host["x"], ids, w.astype(np.float64), host["w13_packed"], host["w13_scales"],
                          host["w2_packed"], host["w2_scales"])
-    check_output(bf16_to_f64(out.cpu().numpy()), ref)
+    check_output(bf16_to_f64(out.cpu().numpy()), ref, label=f"caller routing T={T}")
+    assert_workspaces_clean(L)
 
 
 @pytest.mark.parametrize("T,shared", [(600, False), (1111, False), (700, True)])
@@ -199,7 +211,7 @@ def test_decode_repeated_calls_share_workspace(T):
         got = L.forward(dev["x"] if i % 2 == 0 else x2)
         torch.cuda.synchronize()
         assert torch.equal(got, first[i % 2]), f"call {i}"
-    assert not L.workspace(T)[:65536].any(), "the hand-off area was not returned to zero"
+    assert_workspaces_clean(L)
     fresh = MoeInt4Layer(dev, shape.top_k).forward(dev["x"])   # a new zeroed workspace
     torch.cuda.synchronize()
     assert torch.equal(fresh, first[0])
@@ -208,8 +220,8 @@ def test_decode_repeated_calls_share_workspace(T):
 def test_one_workspace_across_shapes():
     """One workspace buffer serves calls of different token counts (decode and
     many-token paths, forward and routing-only) in any order: each result
-    equals the result on a fresh workspace, and the first 64 KiB are zero
-    after every call."""
+    equals the result on a fresh workspace, and the control prefix is zero
+    after every call (the status word included)."""
     base = dict(hidden=512, experts=64, top_k=4, inter=256)
     host = synth.make_layer(synth.LayerShape(tokens=40, **base), seed=23)
     dev = synth.to_device(host)
@@ -243,7 +255,7 @@ def test_one_workspace_across_shapes():
             torch.cuda.synchronize()
             for key in got:
                 assert torch.equal(got[key], want[key]), f"T={T} route {key}"
-        assert not ws[:65536].any(), f"T={T} {what}: the hand-off area was not returned to zero"
+        assert B.workspace_prefix_clean(ws), f"T={T} {what}: the control prefix was not returned to zero"
 
 
 @pytest.mark.parametrize("H,I,E,k", [(768, 384, 40, 6), (1280, 128, 100, 3)])
@@ -276,6 +288,48 @@ def test_real_decode(real_weights, T):
     shape = synth.LayerShape(tokens=T)
     host = synth.make_layer(shape, seed=0, x_seed=1000 + T, weights=w)
     run_and_check(host, real_dev=dev, label=f"real decode T={T}")
+
+
+@pytest.mark.parametrize("T,shared", [(6, False), (8, False), (16, False), (8, True)])
+def test_real_decode_token_groups(real_weights, T, shared):
+    """Few-token batches of 6 to 16 tokens at the real shape, group 128: more
+    slots than one pass of the down projection's lane groups covers, and
+    (T = 16) the largest batch of the few-token path."""
+    w, dev = real_weights
+    shape = synth.LayerShape(tokens=T)
+    host = synth.make_layer(shape, seed=0, x_seed=5000 + T, weights=w, shared=shared)
+    run_and_check(host, real_dev=dev, label=f"real decode T={T} shared={shared}")
+
+
+def _extreme_layer(T, seed):
+    """Activations whose magnitudes are spread log-uniformly over [1e-4, 6e4]
+    with random signs (bf16, inside fp16's exact range), with the router and
+    gate/up scales taken down by 2^-16 (exact in bf16) so that logits and the
+    SwiGLU activation stay in their usual range."""
+    shape = synth.LayerShape(tokens=T, hidden=1024, experts=32, top_k=4, inter=256)
+    host = synth.make_layer(shape, seed=seed)
+    rng = np.random.default_rng(seed + 99)
+    mag = np.exp(rng.uniform(np.log(1e-4), np.log(6e4), (T, 1024)))
+    x = (mag * rng.choice([-1.0, 1.0], (T, 1024))).astype(np.float32)
+    host["x"] = synth.bf16_bits(x)
+    xf = bf16_to_f64(host["x"])
+    assert np.abs(xf).max() <= 65504 and np.abs(xf).min() >= 2.0 ** -14
+    def down16(b):   # bf16 bits * 2^-16: exponent field - 16 (all values are normal)
+        b = b.astype(np.uint16)
+        e = (b >> 7) & 0xFF
+        assert (e > 16).all()
+        return ((b & 0x807F) | ((e - 16) << 7)).astype(np.uint16)
+    host["router_w"] = down16(host["router_w"])
+    host["w13_scales"] = down16(host["w13_scales"])
+    return host
+
+
+@pytest.mark.parametrize("T", [16, 17])
+def test_extreme_activations_in_range(T):
+    """The largest few-token batch (bf16 activations used as they are) and the
+    smallest matrix-core batch (activations converted to fp16) give the same
+    parity on activations from 1e-4 to 6e4 in magnitude."""
+    run_and_check(_extreme_layer(T, 4100), label=f"extreme activations T={T}")
 
 
 def test_real_decode_batch64(real_weights):

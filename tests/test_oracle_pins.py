@@ -388,8 +388,8 @@ def test_token_subset_equals_full():
 
 
 # ---------------------------------------------------------------------------
-# Load-time INT4 quantizer ([VO] section 7: round to nearest, group 128,
-# symmetric, per-group clip search minimising the squared error)
+# Load-time INT4 quantizer ([VO] section 7: symmetric INT4 in groups of 128,
+# rounded to nearest, each group clipped where its squared error is least)
 # ---------------------------------------------------------------------------
 from fractions import Fraction
 
@@ -509,6 +509,161 @@ def test_quantizer_zero_group_and_packing():
     assert np.all(_unpack_codes(packed)[1, 128:] == 7)
     assert np.all(packed[1, 16:] == -1)
     assert float(_bits_to_float(scales[1, 1])) == float(_bits_to_float(_to_bf16_bits(np.float32(0.25) * np.float32(1.0 / 7.0))))
+
+
+# ---- the clip search's choice, checked candidate by candidate in exact
+# rationals (independent of the oracle's fp32 accumulation) ----
+
+def _candidate_scales(amax_bits):
+    """The twenty candidate scales of a group as the reading defines them:
+    bf16(fp32(amax * fp32((1 - j/40) / 7))), j = 0..19; None below 2^-126."""
+    amax = np.float32(_bits_to_float(amax_bits))
+    out = []
+    for j in range(20):
+        kj = np.float32((1.0 - j / 40.0) / 7.0)
+        sb = _to_bf16_bits(np.float32(amax * kj))
+        s = float(_bits_to_float(sb))
+        out.append(None if s < 2.0 ** -126 else (int(sb), Fraction(s)))
+    return out
+
+
+def _exact_candidate_errors(wbits, cands, absolute=False):
+    """Exact sum of squared (or absolute) residuals per candidate, with the
+    nearest-even code clamped to [-8, 7]."""
+    xs = [Fraction(float(v)) for v in _bits_to_float(wbits)]
+    errs = []
+    for c in cands:
+        if c is None:
+            errs.append(None)
+            continue
+        s = c[1]
+        e = Fraction(0)
+        for x in xs:
+            q = max(-8, min(7, round(x / s)))   # Fraction rounds half to even
+            d = x - q * s
+            e += abs(d) if absolute else d * d
+        errs.append(e)
+    return errs
+
+
+# fp32 sums of 128 fp32-rounded squares: each term and each addition is off by
+# at most 2^-24 relative, so two candidates whose exact errors are closer than
+# this may be ordered either way by an fp32 search
+_QSLACK = 2.0 * 130 * 2.0 ** -24
+
+
+def _choice_ok(wbits, chosen_bits, best_err=None):
+    """Whether a chosen scale is a correct answer of the search for this group:
+    its exact error is the minimum over the candidates (within the fp32 slack
+    of the best), and among exactly tied minima it is the first candidate."""
+    amax_bits = _to_bf16_bits(np.abs(_bits_to_float(wbits)).max())
+    cands = _candidate_scales(amax_bits)
+    errs = _exact_candidate_errors(wbits, cands)
+    valid = [(e, j) for j, e in enumerate(errs) if e is not None]
+    if not valid:
+        return int(chosen_bits) == 0
+    emin = min(e for e, _ in valid)
+    first_min = min(j for e, j in valid if e == emin)
+    allowed = {cands[j][0] for e, j in valid if e == emin or float(e - emin) <= _QSLACK * float(emin)}
+    # exact ties (no fp32 ambiguity) must resolve to the first candidate
+    near = [j for e, j in valid if e != emin and float(e - emin) <= _QSLACK * float(emin)]
+    if not near:
+        allowed = {cands[first_min][0]}
+    if int(chosen_bits) not in allowed:
+        return False
+    if best_err is not None:
+        # the reported fp32 error is the chosen candidate's error to fp32 slack
+        jc = [j for j, c in enumerate(cands) if c is not None and c[0] == int(chosen_bits)][0]
+        ec = float(errs[jc])
+        if abs(float(best_err) - ec) > _QSLACK * max(ec, 2.0 ** -126):
+            return False
+    return True
+
+
+def _quantizer_groups(n_groups=240, group=128, seed=2024):
+    """Seeded groups of three kinds: normal N(0, 0.02); outlier-heavy (a few
+    entries x 8 to x 30); near-constant (0.5 +- 1e-3 with random signs)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(n_groups):
+        kind = i % 3
+        if kind == 0:
+            f = rng.standard_normal(group) * 0.02
+        elif kind == 1:
+            f = rng.standard_normal(group) * 0.02
+            idx = rng.choice(group, rng.integers(1, 6), replace=False)
+            f[idx] *= rng.uniform(8, 30, idx.size)
+        else:
+            f = (0.5 + rng.standard_normal(group) * 1e-3) * rng.choice([-1.0, 1.0], group)
+        rows.append(f)
+    return _to_bf16_bits(np.array(rows, np.float32))
+
+
+def test_quantizer_choice_is_the_exact_minimum_over_all_candidates():
+    # every candidate's squared error recomputed in exact rationals; the
+    # oracle's scale must attain the minimum (within the fp32 accumulation
+    # slack), its codes must be the nearest-even levels of that scale and
+    # its reported error must be that candidate's
+    w = _quantizer_groups()
+    packed, scales, e1, e2 = oracle.quantize_int4(w)
+    codes = _unpack_codes(packed)
+    picked = []
+    for g in range(w.shape[0]):
+        assert _choice_ok(w[g], scales[g, 0], e1[g, 0]), f"group {g}: scale {scales[g, 0]:#06x}"
+        assert e2[g, 0] >= e1[g, 0]
+        s = Fraction(float(_bits_to_float(scales[g, 0])))
+        for k in range(0, 128, 17):
+            x = Fraction(float(_bits_to_float(w[g, k])))
+            assert codes[g, k] == max(-8, min(7, round(x / s)))
+        cands = _candidate_scales(_to_bf16_bits(np.abs(_bits_to_float(w[g])).max()))
+        picked.append([j for j, c in enumerate(cands) if c and c[0] == int(scales[g, 0])][0])
+    # the search really searches: the chosen clips spread over many candidates
+    assert len(set(picked)) >= 6 and max(picked) >= 10
+
+
+def test_quantizer_pin_rejects_plausible_mistakes():
+    # the check above must fail a quantizer with a wrong clip grid (1 - j/20),
+    # an absolute-error criterion, or the scale of a neighbouring candidate
+    w = _quantizer_groups(n_groups=90, seed=77)
+    wrong_grid = wrong_crit = wrong_pick = 0
+    for g in range(w.shape[0]):
+        amax = np.float32(_bits_to_float(_to_bf16_bits(np.abs(_bits_to_float(w[g])).max())))
+        grid20 = []
+        for j in range(20):
+            sb = _to_bf16_bits(np.float32(amax * np.float32((1.0 - j / 20.0) / 7.0)))
+            grid20.append(None if _bits_to_float(sb) < 2.0 ** -126 else (int(sb), Fraction(float(_bits_to_float(sb)))))
+        e20 = _exact_candidate_errors(w[g], grid20)
+        j20 = min((e, j) for j, e in enumerate(e20) if e is not None)[1]
+        wrong_grid += not _choice_ok(w[g], grid20[j20][0])
+        cands = _candidate_scales(_to_bf16_bits(amax))
+        eabs = _exact_candidate_errors(w[g], cands, absolute=True)
+        jabs = min((e, j) for j, e in enumerate(eabs) if e is not None)[1]
+        wrong_crit += not _choice_ok(w[g], cands[jabs][0])
+        esq = _exact_candidate_errors(w[g], cands)
+        jsq = min((e, j) for j, e in enumerate(esq) if e is not None)[1]
+        jn = jsq + 1 if jsq < 19 else jsq - 1
+        if cands[jn][0] != cands[jsq][0]:
+            wrong_pick += not _choice_ok(w[g], cands[jn][0])
+    assert wrong_grid >= 5 and wrong_crit >= 3 and wrong_pick >= 30, (wrong_grid, wrong_crit, wrong_pick)
+
+
+def test_quantizer_exact_tie_goes_to_the_first_candidate():
+    # one group found by an exhaustive search over pairs of bf16 values: with
+    # amax 1, candidates 0 (scale 0.142578125) and 1 (0.1396484375) have
+    # exactly the same squared error, the smallest of all twenty, and every
+    # residual square and partial sum is exact in fp32, so the search sees
+    # the tie too; the rule keeps the first
+    f = np.zeros(128, np.float32)
+    f[0], f[1], f[2] = 1.0, 0.0986328125, -0.09814453125
+    w = _to_bf16_bits(f)
+    cands = _candidate_scales(_to_bf16_bits(np.float32(1.0)))
+    errs = _exact_candidate_errors(w, cands)
+    emin = min(errs)
+    assert errs[0] == errs[1] == emin and cands[0][0] != cands[1][0]
+    assert sum(e == emin for e in errs) == 2
+    _, scales, e1, e2 = oracle.quantize_int4(w[None, :])
+    assert int(scales[0, 0]) == cands[0][0]
+    assert e1[0, 0] == e2[0, 0] == float(emin)
 
 
 # ---- INT8 W8A16 linear ([VO] decode-04 layout; [MC] groups C and D) ----
