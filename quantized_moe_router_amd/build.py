@@ -51,7 +51,9 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("hipcc failed")
     tmp = LIB + ".tmp"
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+                           "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

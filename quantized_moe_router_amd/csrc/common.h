@@ -385,8 +385,23 @@ inline int router_ksplit(const Dims &d)
 // slots per expert are few) in pairs, pairs dealt round-robin to the 8 XCDs,
 // 16 slots per round.  At most S / 64 + 2 E tile positions are used (each
 // expert's tiles rounded up to a pair), which this bound covers.
-// Rows per routed GEMM tile: 64 when the slots per expert are few.
-inline int routed_tile_rows(const Dims &d) { return (long)d.S < 32L * d.E ? 64 : 128; }
+// Routed grouped GEMMs.  With many slots per expert (at least
+// kBigMinRowsPerExpert on average) one workgroup takes a whole chunk of up to
+// kBigRows rows of one expert (every row of it, for balanced routing), so the
+// expert's weights are fetched and dequantised once per weight block
+// (moe_gemm_big_kernel); otherwise row tiles of 128 rows, or 64 when the
+// slots per expert are few (moe_gemm_kernel).
+constexpr int kBigRows = 192;
+constexpr int kBigMinRowsPerExpert = 64;
+inline bool routed_big(const Dims &d)
+{
+    return d.gsh == 2 && (long)d.S >= (long)kBigMinRowsPerExpert * d.E;   // group 128
+}
+// Rows per routed tile list entry.
+inline int routed_tile_rows(const Dims &d)
+{
+    return routed_big(d) ? kBigRows : ((long)d.S < 32L * d.E ? 64 : 128);
+}
 
 // Permutations of kPermChunk < S <= kPermMidWaves * kPermChunk run in one
 // workgroup of kPermMidWaves waves; larger ones scan in one workgroup.  Both
@@ -396,6 +411,11 @@ inline bool permute_builds_tiles(const Dims &d) { return d.S > kPermChunk; }
 
 inline size_t routed_tile_slots(const Dims &d)
 {
+    if (routed_big(d)) {
+        // chunks: at most ceil(S / kBigRows) + E, a multiple of 8
+        const size_t chunks = ((size_t)d.S + kBigRows - 1) / kBigRows + (size_t)d.E;
+        return 8 * ((chunks + 7) / 8);
+    }
     const size_t pairs = ((size_t)d.S + 63) / 64 / 2 + (size_t)d.E + 1;
     return 16 * ((pairs + 7) / 8);
 }

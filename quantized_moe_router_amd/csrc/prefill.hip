@@ -486,6 +486,287 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
     }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-expert grouped GEMM (many slots per expert).  A workgroup takes one
+// chunk of up to 192 sorted rows of one expert (all of an expert's rows for
+// balanced routing) and one block of 256 weight rows, so every weight is
+// fetched from memory once per chunk.  Eight waves, two per SIMD: wave
+// (g, c) takes the weight rows [64 c, 64 c + 64) of the block (two 32-wide
+// column tiles) and row group g of the chunk: the first ceil(T / 2) of its T
+// 32-row tiles for g = 0, the rest for g = 1, as v_mfma_f32_32x32x16_f16
+// tiles.  The two waves of a SIMD convert the same weights (each for its
+// own rows) and keep the matrix core busy while the other waits.
+//   * K advances one 128-wide weight group (one scale per row) per stage, with
+//     one barrier per stage.  The chunk's scales are copied to LDS once.
+//   * Weights: each wave loads its own rows straight into registers, two
+//     groups ahead: per row the two lane halves read the 16-byte pieces at
+//     bytes 16h and 32 + 16h of the group's 64 bytes.  Piece p of half h,
+//     word w, holds K = 64 p + 32 h + 8 w .. + 7, and MFMA step j = 4 p + w
+//     consumes it; the activation tile is read in the same K order.
+//   * Activations: gathered rows (256 bytes per row and stage) are loaded
+//     into registers a stage ahead and written to the other half of a
+//     double-buffered LDS tile during the stage before their use, spread
+//     over its MFMA steps.
+//   * Software pipeline: while the MFMAs of step j run, the activation
+//     fragments and weight operands of step j + 1 are prepared; scheduling
+//     barriers keep that preparation in the shadow of the step's MFMAs.
+// ---------------------------------------------------------------------------
+constexpr int kBigMA = kBigRows / 32;   // row tiles per chunk
+constexpr int kBigWaves = 8;
+constexpr int kBigThreads = kBigWaves * kWave;
+constexpr int kBigKS = 128;             // K per stage (one weight group)
+constexpr int kBigLdsRow = kBigKS + 8;  // padded LDS row (fp16 elements)
+constexpr int kBigMaxGroups = kMaxHidden / kGroup;   // scales per weight row
+constexpr int kBigStageRows = kBigThreads / 8;        // rows one staging pass covers (8 threads per row)
+
+template <int MODE>
+__global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g, int nblocks)
+{
+    static_assert(MODE == kRoutedW13 || MODE == kRoutedW2, "routed modes only");
+    static_assert(kBigKS == kGroup, "one weight group per stage");
+    constexpr bool kW13 = MODE == kRoutedW13;
+    __shared__ __align__(16) _Float16 s_a[2][kBigRows * kBigLdsRow];
+    __shared__ uint16_t s_sc[kBigMaxGroups][kNT];   // [group][tile weight row] bf16 scales
+    __shared__ int s_tok[kBigRows];     // token of each chunk row (-1: none)
+    __shared__ int s_yrow[kBigRows];    // down mode: row of y that each chunk row writes
+    __shared__ float s_wgt[kBigRows];   // down mode: output factor of each chunk row
+
+    // ---- chunk and weight block (XCD-aware: the blocks of one chunk share an XCD) ----
+    const int wid = blockIdx.x;
+    const int xcd = wid & 7, r = wid >> 3;
+    const int nb = r % nblocks, chunk = (r / nblocks) * 8 + xcd;
+    const int4 tv = g.tiles[chunk];
+    if (tv.x < 0) return;   // empty slot
+    const int e = tv.x & 0xFFFF, pbase = tv.y, rows = tv.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int cg = wave & 3, rg = wave >> 2;   // column group, row group
+    const int K = g.K, nstages = K / kBigKS;
+    // weight row of tile column c (0..255): column group c / 64, column tile (c / 32) & 1
+    auto tile_row = [&](int c) {
+        const int w = c >> 6, nt = (c >> 5) & 1, l = c & 31;
+        if constexpr (kW13) return nt == 0 ? 128 * nb + 32 * w + l : g.I + 128 * nb + 32 * w + l;
+        else return kNT * nb + c;
+    };
+    const int32_t *bpe = g.bp + (size_t)e * g.b_words;
+    const uint16_t *bse = g.bs + (size_t)e * g.b_scales;
+    static_assert(kBigThreads >= kNT && kBigThreads >= kBigRows, "one thread per tile column and chunk row");
+    if (tid < kNT) {
+        // this thread's tile column's scales -> LDS
+        const uint16_t *sr = bse + (size_t)tile_row(tid) * nstages;
+        for (int q = 0; q < nstages; ++q) s_sc[q][tid] = sr[q];
+    }
+    float wraw = 0.f;
+    if (tid < kBigRows) {
+        const int i = tid < rows ? tid : 0;
+        const int slot = g.sorted_slots[pbase + i];
+        const int tok = slot / g.k;
+        if constexpr (!kW13) {
+            wraw = g.weights[slot];
+            s_yrow[tid] = tok * (g.k + 1) + (slot - tok * g.k);
+        }
+        s_tok[tid] = tid < rows ? tok : -1;
+    }
+    __syncthreads();
+
+    // activation staging: thread -> 16-byte chunks c8 and c8 + 8 of rows r8 + 64 o
+    const int c8 = tid & 7, r8 = tid >> 3;
+    constexpr int kNO = kBigRows / kBigStageRows;   // staging passes for a full chunk
+    uint32_t aoff[kNO];   // element offsets of this thread's rows (row 0 of the chunk past its end)
+    const uint16_t *abase = kW13 ? g.x : g.a16;
+#pragma unroll
+    for (int o = 0; o < kNO; ++o) {
+        const int row = r8 + kBigStageRows * o, arow = row < rows ? row : 0;
+        aoff[o] = kW13 ? (uint32_t)s_tok[arow] * (uint32_t)g.H + 8 * c8
+                       : (uint32_t)(pbase + arow) * (uint32_t)K + 8 * c8;
+    }
+    const int col = lane & 31;
+    const size_t bstride = (size_t)K / 8;   // words per weight row
+    const u32x4_t *bq[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+        bq[nt] = reinterpret_cast<const u32x4_t *>(bpe + (size_t)tile_row(64 * cg + 32 * nt + col) * bstride) + half;
+    const int mtiles = (rows + 31) / 32;
+    const int t0 = rg == 0 ? 0 : (mtiles + 1) / 2;   // first row tile of this wave's row group
+
+    f32x16_t acc[kBigMA / 2][2];
+#pragma unroll
+    for (int i = 0; i < kBigMA / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    // MA: this wave's row tiles; NO: staging passes of the chunk (every wave
+    // takes part in staging)
+    auto kloop = [&](auto ma_c, auto no_c) {
+        constexpr int MA = decltype(ma_c)::value;
+        constexpr int NO = decltype(no_c)::value;
+        u32x4_t ra[NO][2];          // the next stage's activations
+        u32x4_t rb[3][2][2];        // weight groups in flight: [set][nt][piece]
+        auto load_a_pass = [&](int st, int o) {
+            const uint16_t *src = abase + aoff[o] + st * kBigKS;
+            ra[o][0] = *reinterpret_cast<const u32x4_t *>(src);
+            ra[o][1] = *reinterpret_cast<const u32x4_t *>(src + 64);
+        };
+        auto store_a_pass = [&](int buf, int o) {
+            _Float16 *dst = s_a[buf] + (r8 + kBigStageRows * o) * kBigLdsRow + 8 * c8;
+            *reinterpret_cast<u32x4_t *>(dst) = ra[o][0];
+            *reinterpret_cast<u32x4_t *>(dst + 64) = ra[o][1];
+        };
+        auto load_b_piece = [&](int grp, int set, int nt) {
+            const u32x4_t *q = bq[nt] + 4 * grp;   // 64 bytes per group; + half applied
+            rb[set][nt][0] = q[0];
+            rb[set][nt][1] = q[2];
+        };
+        // fp16 scale pairs of weight group grp for this lane's two rows
+        auto scales_of = [&](int grp, h2_t (&s2)[2]) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) s2[nt] = scale_pair(s_sc[grp][64 * cg + 32 * nt + col]);
+        };
+        // weight operands of MFMA step j (0..7) of the weight group in `set`
+        auto dequant_step = [&](int set, const h2_t (&s2)[2], int j, f16x8_t (&out)[2]) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const u32x4_t v = rb[set][nt][j >> 2];
+                out[nt] = dequant_int4_f16(v[j & 3], s2[nt]);
+            }
+        };
+        f16x8_t bcur[2];   // weight operands of the step about to run
+        // stage st: weight group st in `set` (the next in nset), activations
+        // in LDS buffer st & 1; during it the next stage's activations go to
+        // the other buffer (unconditionally: the last stage writes a buffer no
+        // stage reads any more and reloads the last stage, so no branch leaves
+        // the compiler guessing how many loads are in flight), the stage after
+        // next's are loaded, and the weights of group st + 2 are loaded into
+        // (set + 2) % 3
+        auto stage = [&](int st, int set, int nset) {
+            const int nst = min(st + 2, nstages - 1);
+            h2_t s2c[2];
+            scales_of(st, s2c);
+            const _Float16 *A = s_a[st & 1] + (32 * t0 + col) * kBigLdsRow + 32 * half;
+            f16x8_t af[2][MA > 0 ? MA : 1];
+#pragma unroll
+            for (int mt = 0; mt < MA; ++mt)
+                af[0][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kBigLdsRow);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (j < NO) {
+                    store_a_pass((st + 1) & 1, j);
+                    load_a_pass(nst, j);
+                }
+                if (j == 3) load_b_piece(nst, (set + 2) % 3, 0);
+                if (j == 5) load_b_piece(nst, (set + 2) % 3, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (MA > 0) {
+                    f16x8_t bnext[2];
+                    if (j < 7) {
+                        const int ko = 64 * ((j + 1) >> 2) + 8 * ((j + 1) & 3);
+#pragma unroll
+                        for (int mt = 0; mt < MA; ++mt)
+                            af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kBigLdsRow + ko);
+                        dequant_step(set, s2c, j + 1, bnext);
+                    } else {
+                        h2_t s2n[2];
+                        scales_of(min(st + 1, nstages - 1), s2n);
+                        dequant_step(nset, s2n, 0, bnext);   // the next stage's first step
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MA; ++mt) {
+                        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bcur[0], acc[mt][0], 0, 0, 0);
+                        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bcur[1], acc[mt][1], 0, 0, 0);
+                    }
+                    // interleave: one MFMA, then a share of the step's
+                    // preparation (LDS reads first, then conversions)
+#pragma unroll
+                    for (int i = 0; i < 2 * MA; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        if (j < 7 && i < MA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                        __builtin_amdgcn_sched_group_barrier(0x002, (30 + 2 * MA - 1) / (2 * MA), 0);   // VALU
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    bcur[0] = bnext[0];
+                    bcur[1] = bnext[1];
+                }
+            }
+            __syncthreads();
+        };
+        // prologue: weight groups 0 and 1, activation stage 0 in LDS and
+        // stage 1 in flight
+        load_b_piece(0, 0, 0);
+        load_b_piece(0, 0, 1);
+        load_b_piece(min(1, nstages - 1), 1, 0);
+        load_b_piece(min(1, nstages - 1), 1, 1);
+#pragma unroll
+        for (int o = 0; o < NO; ++o) load_a_pass(0, o);
+#pragma unroll
+        for (int o = 0; o < NO; ++o) store_a_pass(0, o);
+#pragma unroll
+        for (int o = 0; o < NO; ++o) load_a_pass(min(1, nstages - 1), o);
+        if constexpr (MA > 0) {
+            h2_t s20[2];
+            scales_of(0, s20);
+            dequant_step(0, s20, 0, bcur);
+        }
+        __syncthreads();
+        int st = 0;
+        for (; st + 3 <= nstages; st += 3) {
+            stage(st, 0, 1);
+            stage(st + 1, 1, 2);
+            stage(st + 2, 2, 0);
+        }
+        if (st < nstages) stage(st, 0, 1);
+        if (st + 1 < nstages) stage(st + 1, 1, 2);
+    };
+    static_assert(kBigMA == 6 && kNO == 3, "K loop variants below");
+    // row tiles: row group 0 takes ceil(T / 2), row group 1 the rest; the
+    // staging passes cover ceil(T / 2) * 64 rows
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    switch (mtiles * 2 + rg) {
+    case 2: kloop(I1{}, I1{}); break;   // 1 tile: group 0 has it
+    case 3: kloop(I0{}, I1{}); break;
+    case 4: kloop(I1{}, I1{}); break;   // 2 tiles
+    case 5: kloop(I1{}, I1{}); break;
+    case 6: kloop(I2{}, I2{}); break;   // 3 tiles
+    case 7: kloop(I1{}, I2{}); break;
+    case 8: kloop(I2{}, I2{}); break;   // 4 tiles
+    case 9: kloop(I2{}, I2{}); break;
+    case 10: kloop(I3{}, I3{}); break;  // 5 tiles
+    case 11: kloop(I2{}, I3{}); break;
+    default: kloop(I3{}, I3{}); break;  // 6 tiles
+    }
+    const int ma_w = rg == 0 ? (mtiles + 1) / 2 : mtiles / 2;
+
+    // ---- epilogue ----
+    if constexpr (!kW13) {
+        if (tid < kBigRows) s_wgt[tid] = wraw * kScaleDown;   // routing weight times 2^-10
+        __syncthreads();
+    }
+#pragma unroll
+    for (int mt = 0; mt < kBigMA / 2; ++mt) {
+        if (mt >= ma_w) continue;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int m = 32 * (t0 + mt) + 8 * (j >> 2) + 4 * half + (j & 3);
+            if (m >= rows) continue;
+            if constexpr (kW13) {
+                const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
+                const int i = 128 * nb + 32 * cg + col;
+                const int ip = (i & ~7) | pair_pos(i & 7);
+                g.h_out[(size_t)(pbase + m) * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
+            } else {
+                const float wv = s_wgt[m];
+                uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * nb + 64 * cg + col;
+                yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
+                yr[32] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
+            }
+        }
+    }
+}
+
 // out[t][n] = bf16( sum_j y[t][j][n] (+ y[t][k][n] for the shared expert) ),
 // fixed order; one thread per 8 outputs.  The slot rows are loaded four at a
 // time, all four in flight together (clamped, unconditional loads; a clamped
@@ -629,11 +910,16 @@ hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const
 
 
 template <int MODE>
-static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st, bool g64 = false)
+static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hipStream_t st, bool g64 = false,
+                              bool big = false)
 {
     const int groups = (ntiles_max + 7) / 8;
     if constexpr (MODE == kRoutedW13 || MODE == kRoutedW2) {
         const unsigned grid = groups * 8 * nblocks;
+        if (big) {
+            moe_gemm_big_kernel<MODE><<<grid, kBigThreads, 0, st>>>(g, nblocks);
+            return hipGetLastError();
+        }
         if (g.small_rows > 0) {
             if (g64) moe_gemm_kernel<MODE, 2, 2><<<grid, kGemmThreads, 0, st>>>(g, nblocks);
             else moe_gemm_kernel<MODE, 2><<<grid, kGemmThreads, 0, st>>>(g, nblocks);
@@ -673,14 +959,15 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     // routing are spread over twice as many workgroups
     g.small_rows = small ? 64 : 0;
     g.b_words = (size_t)2 * d.I * d.H / 8; g.b_scales = (size_t)2 * d.I * (d.H >> (d.gsh + 5));
-    if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st, d.gsh == 1)) != hipSuccess) return e;
+    const bool big = routed_big(d);
+    if ((e = launch_gemm<kRoutedW13>(g, tmax, d.I / 128, st, d.gsh == 1, big)) != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
     // routed down -> y[t][j] = w * (W2 h)
     GemmArgs g2 = g;
     g2.a16 = ws.h; g2.bp = a.w2p; g2.bs = a.w2s; g2.weights = a.weights; g2.y_out = y;
     g2.K = d.I;
     g2.b_words = (size_t)d.H * d.I / 8; g2.b_scales = (size_t)d.H * (d.I >> (d.gsh + 5));
-    if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st, d.gsh == 1)) != hipSuccess) return e;
+    if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st, d.gsh == 1, big)) != hipSuccess) return e;
     if (d.sh_I > 0) {
         // shared expert: gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
         if (!x_converted && (e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess)

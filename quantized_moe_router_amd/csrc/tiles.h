@@ -42,12 +42,35 @@ __device__ __forceinline__ int block_excl_sum(int v, int *s_sum, int &total)
     return base + incl - v;
 }
 
+// Chunk list of the whole-expert GEMM (mt == kBigRows): expert e's count_e
+// rows are split into ceil(count_e / kBigRows) chunks of nearly equal size
+// (consecutive sorted rows), listed densely in expert order; list slot p goes
+// to XCD p % 8, and every weight block of a chunk runs on that XCD, so the
+// chunk's activation rows are read into one L2.  Slots past the last chunk
+// are empty (-1).
+__device__ inline void build_chunk_list(int cnt, int off, int nslots, int4 *__restrict__ tiles, int *s_sum)
+{
+    const int e = threadIdx.x;
+    const int nc = (cnt + kBigRows - 1) / kBigRows;
+    int total;
+    const int p0 = block_excl_sum(nc, s_sum, total);
+    for (int i = 0; i < nc; ++i) {
+        const int b = (int)((long)cnt * i / nc), en = (int)((long)cnt * (i + 1) / nc);
+        tiles[p0 + i] = make_int4(e, off + b, en - b, 0);
+    }
+    for (int pos = total + (int)threadIdx.x; pos < nslots; pos += blockDim.x) tiles[pos] = make_int4(-1, 0, 0, 0);
+}
+
 // The list from the expert counts and offsets; called by all 1024 threads
 // of one workgroup, thread e passing expert e's count and offset (count 0
 // for e >= E).
 __device__ inline void build_tile_list(int cnt, int off, int nslots, int mt, int4 *__restrict__ tiles,
                                        int *s_sum)
 {
+    if (mt == kBigRows) {
+        build_chunk_list(cnt, off, nslots, tiles, s_sum);
+        return;
+    }
     const int e = threadIdx.x;
     const int nt = (cnt + mt - 1) / mt;
     const int multi = nt >= 2 ? (nt + 1) & ~1 : 0;   // positions of a multi-tile expert

@@ -184,6 +184,34 @@ def test_many_rows_per_expert(T, shared):
     run_and_check(host, label=f"many rows per expert T={T} shared={shared}")
 
 
+@pytest.mark.parametrize("H,I", [(256, 128), (768, 384)])
+def test_whole_expert_gemm_row_counts(H, I):
+    """Caller routing that gives the experts every row count the whole-expert
+    grouped GEMM distinguishes: 0, 1 and 2 to 6 row tiles of 32 (ragged and
+    full), exactly one chunk (192 rows) and counts that split into two or
+    three chunks; ids may repeat within a token.  Every token is checked."""
+    counts = [0, 1, 5, 31, 32, 33, 63, 64, 96, 150, 160, 191, 192, 193, 300, 385]
+    k = 4
+    S = sum(counts)
+    counts[-1] += (-S) % k
+    S = sum(counts)
+    T = S // k
+    assert S >= 64 * 16   # the whole-expert path is the one taken
+    shape = synth.LayerShape(tokens=T, hidden=H, experts=16, top_k=k, inter=I)
+    host = synth.make_layer(shape, seed=77 + H)
+    rng = np.random.default_rng(H)
+    ids = rng.permutation(np.repeat(np.arange(16), counts)).astype(np.int32).reshape(T, k)
+    w = rng.random((T, k)).astype(np.float32)
+    dev = synth.to_device(host)
+    L = MoeInt4Layer(dev, k)
+    out = L.experts(dev["x"], torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.experts(host["x"], ids, w.astype(np.float64), host["w13_packed"], host["w13_scales"],
+                         host["w2_packed"], host["w2_scales"])
+    check_output(bf16_to_f64(out.cpu().numpy()), ref, label=f"whole-expert GEMM row counts H={H} I={I}")
+    assert_workspaces_clean(L)
+
+
 @pytest.mark.parametrize("T", [2, 30])
 def test_deterministic(T):
     shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=2, inter=128)
