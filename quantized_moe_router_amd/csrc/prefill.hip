@@ -520,29 +520,37 @@ constexpr int kBigMaxGroups = kMaxHidden / kGroup;   // scales per weight row
 constexpr int kBigStageRows = kBigThreads / 8;        // rows one staging pass covers (8 threads per row)
 
 template <int MODE>
-__global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g, int nblocks)
+__global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g, int nblocks, int nbg)
 {
     static_assert(MODE == kRoutedW13 || MODE == kRoutedW2, "routed modes only");
     static_assert(kBigKS == kGroup, "one weight group per stage");
     constexpr bool kW13 = MODE == kRoutedW13;
+    // several weight blocks per workgroup only for the down projection (its K
+    // is short, so a block's set-up costs as much as a good part of its loop;
+    // the gate/up projection's 20 groups of scales fill the LDS for one block)
+    constexpr bool kBlockLoop = !kW13;
     __shared__ __align__(16) _Float16 s_a[2][kBigRows * kBigLdsRow];
-    __shared__ uint16_t s_sc[kBigMaxGroups][kNT];   // [group][tile weight row] bf16 scales
+    __shared__ uint16_t s_sc[kBigMaxGroups][kNT];   // [block * groups + group][tile weight row] bf16 scales
     __shared__ int s_tok[kBigRows];     // token of each chunk row (-1: none)
     __shared__ int s_yrow[kBigRows];    // down mode: row of y that each chunk row writes
     __shared__ float s_wgt[kBigRows];   // down mode: output factor of each chunk row
 
-    // ---- chunk and weight block (XCD-aware: the blocks of one chunk share an XCD) ----
+    // ---- chunk and first weight block (XCD-aware: the blocks of one chunk
+    // share an XCD); the workgroup runs weight blocks b0 .. b0 + nbg - 1 ----
     const int wid = blockIdx.x;
     const int xcd = wid & 7, r = wid >> 3;
-    const int nb = r % nblocks, chunk = (r / nblocks) * 8 + xcd;
+    const int ngroups_b = nblocks / nbg;
+    const int b0 = (r % ngroups_b) * nbg, chunk = (r / ngroups_b) * 8 + xcd;
     const int4 tv = g.tiles[chunk];
     if (tv.x < 0) return;   // empty slot
     const int e = tv.x & 0xFFFF, pbase = tv.y, rows = tv.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int cg = wave & 3, rg = wave >> 2;   // column group, row group
     const int K = g.K, nstages = K / kBigKS;
-    // weight row of tile column c (0..255): column group c / 64, column tile (c / 32) & 1
-    auto tile_row = [&](int c) {
+    // weight row of tile column c (0..255) of weight block nb: column group
+    // c / 64, column tile (c / 32) & 1; block nb + 1 is kBlockRows rows on
+    constexpr int kBlockRows = kW13 ? 128 : kNT;
+    auto tile_row = [&](int nb, int c) __attribute__((always_inline)) {
         const int w = c >> 6, nt = (c >> 5) & 1, l = c & 31;
         if constexpr (kW13) return nt == 0 ? 128 * nb + 32 * w + l : g.I + 128 * nb + 32 * w + l;
         else return kNT * nb + c;
@@ -551,17 +559,18 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
     const uint16_t *bse = g.bs + (size_t)e * g.b_scales;
     static_assert(kBigThreads >= kNT && kBigThreads >= kBigRows, "one thread per tile column and chunk row");
     if (tid < kNT) {
-        // this thread's tile column's scales -> LDS
-        const uint16_t *sr = bse + (size_t)tile_row(tid) * nstages;
-        for (int q = 0; q < nstages; ++q) s_sc[q][tid] = sr[q];
+        // this thread's tile column's scales, every block of the workgroup -> LDS
+        for (int bi = 0; bi < nbg; ++bi) {
+            const uint16_t *sr = bse + (size_t)tile_row(b0 + bi, tid) * nstages;
+            for (int q = 0; q < nstages; ++q) s_sc[bi * nstages + q][tid] = sr[q];
+        }
     }
-    float wraw = 0.f;
     if (tid < kBigRows) {
         const int i = tid < rows ? tid : 0;
         const int slot = g.sorted_slots[pbase + i];
         const int tok = slot / g.k;
         if constexpr (!kW13) {
-            wraw = g.weights[slot];
+            s_wgt[tid] = g.weights[slot] * kScaleDown;   // routing weight times the 2^-10 of the scales
             s_yrow[tid] = tok * (g.k + 1) + (slot - tok * g.k);
         }
         s_tok[tid] = tid < rows ? tok : -1;
@@ -581,47 +590,54 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
     }
     const int col = lane & 31;
     const size_t bstride = (size_t)K / 8;   // words per weight row
+    const size_t bblock = (size_t)kBlockRows * bstride / 4;   // 16-byte units from one block to the next
     const u32x4_t *bq[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-        bq[nt] = reinterpret_cast<const u32x4_t *>(bpe + (size_t)tile_row(64 * cg + 32 * nt + col) * bstride) + half;
+        bq[nt] = reinterpret_cast<const u32x4_t *>(bpe + (size_t)tile_row(b0, 64 * cg + 32 * nt + col) * bstride) + half;
     const int mtiles = (rows + 31) / 32;
     const int t0 = rg == 0 ? 0 : (mtiles + 1) / 2;   // first row tile of this wave's row group
+    const int nst_all = nbg * nstages;                // stages over all the workgroup's blocks
 
     f32x16_t acc[kBigMA / 2][2];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kBigMA / 2; ++i)
+        for (int i = 0; i < kBigMA / 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    };
+    zero_acc();
 
     // MA: this wave's row tiles; NO: staging passes of the chunk (every wave
     // takes part in staging)
-    auto kloop = [&](auto ma_c, auto no_c) {
+    auto kloop = [&](auto ma_c, auto no_c) __attribute__((always_inline)) {
         constexpr int MA = decltype(ma_c)::value;
         constexpr int NO = decltype(no_c)::value;
         u32x4_t ra[NO][2];          // the next stage's activations
         u32x4_t rb[3][2][2];        // weight groups in flight: [set][nt][piece]
-        auto load_a_pass = [&](int st, int o) {
-            const uint16_t *src = abase + aoff[o] + st * kBigKS;
+        // global stage gs: block gs / nstages of the workgroup, K stage gs % nstages
+        auto load_a_pass = [&](int gs, int o) __attribute__((always_inline)) {
+            const uint16_t *src = abase + aoff[o] + (gs % nstages) * kBigKS;
             ra[o][0] = *reinterpret_cast<const u32x4_t *>(src);
             ra[o][1] = *reinterpret_cast<const u32x4_t *>(src + 64);
         };
-        auto store_a_pass = [&](int buf, int o) {
+        auto store_a_pass = [&](int buf, int o) __attribute__((always_inline)) {
             _Float16 *dst = s_a[buf] + (r8 + kBigStageRows * o) * kBigLdsRow + 8 * c8;
             *reinterpret_cast<u32x4_t *>(dst) = ra[o][0];
             *reinterpret_cast<u32x4_t *>(dst + 64) = ra[o][1];
         };
-        auto load_b_piece = [&](int grp, int set, int nt) {
-            const u32x4_t *q = bq[nt] + 4 * grp;   // 64 bytes per group; + half applied
+        auto load_b_piece = [&](int gs, int set, int nt) __attribute__((always_inline)) {
+            const int bi = gs / nstages, grp = gs - bi * nstages;
+            const u32x4_t *q = bq[nt] + bi * bblock + 4 * grp;   // 64 bytes per group; + half applied
             rb[set][nt][0] = q[0];
             rb[set][nt][1] = q[2];
         };
-        // fp16 scale pairs of weight group grp for this lane's two rows
-        auto scales_of = [&](int grp, h2_t (&s2)[2]) {
+        // fp16 scale pairs of global stage gs for this lane's two rows
+        auto scales_of = [&](int gs, h2_t (&s2)[2]) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) s2[nt] = scale_pair(s_sc[grp][64 * cg + 32 * nt + col]);
+            for (int nt = 0; nt < 2; ++nt) s2[nt] = scale_pair(s_sc[gs][64 * cg + 32 * nt + col]);
         };
         // weight operands of MFMA step j (0..7) of the weight group in `set`
         auto dequant_step = [&](int set, const h2_t (&s2)[2], int j, f16x8_t (&out)[2]) {
@@ -631,19 +647,42 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
                 out[nt] = dequant_int4_f16(v[j & 3], s2[nt]);
             }
         };
+        // outputs of weight block b from the accumulators
+        auto store_block = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mt = 0; mt < MA; ++mt) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int m = 32 * (t0 + mt) + 8 * (j >> 2) + 4 * half + (j & 3);
+                    if (m >= rows) continue;
+                    if constexpr (kW13) {
+                        const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
+                        const int i = 128 * b + 32 * cg + col;
+                        const int ip = (i & ~7) | pair_pos(i & 7);
+                        g.h_out[(size_t)(pbase + m) * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
+                    } else {
+                        const float wv = s_wgt[m];
+                        uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * b + 64 * cg + col;
+                        yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
+                        yr[32] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
+                    }
+                }
+            }
+        };
         f16x8_t bcur[2];   // weight operands of the step about to run
-        // stage st: weight group st in `set` (the next in nset), activations
-        // in LDS buffer st & 1; during it the next stage's activations go to
-        // the other buffer (unconditionally: the last stage writes a buffer no
-        // stage reads any more and reloads the last stage, so no branch leaves
-        // the compiler guessing how many loads are in flight), the stage after
-        // next's are loaded, and the weights of group st + 2 are loaded into
-        // (set + 2) % 3
-        auto stage = [&](int st, int set, int nset) {
-            const int nst = min(st + 2, nstages - 1);
+        // global stage gs: its weight group in `set` (the next stage's in
+        // nset), activations in LDS buffer gs & 1; during it the next stage's
+        // activations go to the other buffer (unconditionally: the last stage
+        // writes a buffer no stage reads any more and reloads the last stage,
+        // so no branch leaves the compiler guessing how many loads are in
+        // flight), the stage after next's are loaded, and the weights of stage
+        // gs + 2 are loaded into (set + 2) % 3.  The next block's first stages
+        // are loaded during the previous block's last ones.
+        auto stage = [&](int gs, int set, int nset) __attribute__((always_inline)) {
+            const int ngs = min(gs + 2, nst_all - 1);
             h2_t s2c[2];
-            scales_of(st, s2c);
-            const _Float16 *A = s_a[st & 1] + (32 * t0 + col) * kBigLdsRow + 32 * half;
+            scales_of(gs, s2c);
+            const _Float16 *A = s_a[gs & 1] + (32 * t0 + col) * kBigLdsRow + 32 * half;
             f16x8_t af[2][MA > 0 ? MA : 1];
 #pragma unroll
             for (int mt = 0; mt < MA; ++mt)
@@ -652,11 +691,11 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
             for (int j = 0; j < 8; ++j) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (j < NO) {
-                    store_a_pass((st + 1) & 1, j);
-                    load_a_pass(nst, j);
+                    store_a_pass((gs + 1) & 1, j);
+                    load_a_pass(ngs, j);
                 }
-                if (j == 3) load_b_piece(nst, (set + 2) % 3, 0);
-                if (j == 5) load_b_piece(nst, (set + 2) % 3, 1);
+                if (j == 3) load_b_piece(ngs, (set + 2) % 3, 0);
+                if (j == 5) load_b_piece(ngs, (set + 2) % 3, 1);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (MA > 0) {
                     f16x8_t bnext[2];
@@ -668,7 +707,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
                         dequant_step(set, s2c, j + 1, bnext);
                     } else {
                         h2_t s2n[2];
-                        scales_of(min(st + 1, nstages - 1), s2n);
+                        scales_of(min(gs + 1, nst_all - 1), s2n);
                         dequant_step(nset, s2n, 0, bnext);   // the next stage's first step
                     }
 #pragma unroll
@@ -690,33 +729,42 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
                 }
             }
             __syncthreads();
+            if constexpr (kBlockLoop) {
+                // the end of a weight block: its outputs, then fresh accumulators
+                const int bi = gs / nstages;
+                if (gs - bi * nstages == nstages - 1) {
+                    store_block(b0 + bi);
+                    zero_acc();
+                }
+            }
         };
-        // prologue: weight groups 0 and 1, activation stage 0 in LDS and
-        // stage 1 in flight
+        // prologue: the first two stages' weights, stage 0's activations in
+        // LDS and stage 1's in flight
         load_b_piece(0, 0, 0);
         load_b_piece(0, 0, 1);
-        load_b_piece(min(1, nstages - 1), 1, 0);
-        load_b_piece(min(1, nstages - 1), 1, 1);
+        load_b_piece(min(1, nst_all - 1), 1, 0);
+        load_b_piece(min(1, nst_all - 1), 1, 1);
 #pragma unroll
         for (int o = 0; o < NO; ++o) load_a_pass(0, o);
 #pragma unroll
         for (int o = 0; o < NO; ++o) store_a_pass(0, o);
 #pragma unroll
-        for (int o = 0; o < NO; ++o) load_a_pass(min(1, nstages - 1), o);
+        for (int o = 0; o < NO; ++o) load_a_pass(min(1, nst_all - 1), o);
         if constexpr (MA > 0) {
             h2_t s20[2];
             scales_of(0, s20);
             dequant_step(0, s20, 0, bcur);
         }
         __syncthreads();
-        int st = 0;
-        for (; st + 3 <= nstages; st += 3) {
-            stage(st, 0, 1);
-            stage(st + 1, 1, 2);
-            stage(st + 2, 2, 0);
+        int gs = 0;
+        for (; gs + 3 <= nst_all; gs += 3) {
+            stage(gs, 0, 1);
+            stage(gs + 1, 1, 2);
+            stage(gs + 2, 2, 0);
         }
-        if (st < nstages) stage(st, 0, 1);
-        if (st + 1 < nstages) stage(st + 1, 1, 2);
+        if (gs < nst_all) stage(gs, 0, 1);
+        if (gs + 1 < nst_all) stage(gs + 1, 1, 2);
+        if constexpr (!kBlockLoop) store_block(b0);
     };
     static_assert(kBigMA == 6 && kNO == 3, "K loop variants below");
     // row tiles: row group 0 takes ceil(T / 2), row group 1 the rest; the
@@ -738,33 +786,22 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
     case 11: kloop(I2{}, I3{}); break;
     default: kloop(I3{}, I3{}); break;  // 6 tiles
     }
-    const int ma_w = rg == 0 ? (mtiles + 1) / 2 : mtiles / 2;
+}
 
-    // ---- epilogue ----
-    if constexpr (!kW13) {
-        if (tid < kBigRows) s_wgt[tid] = wraw * kScaleDown;   // routing weight times 2^-10
-        __syncthreads();
+// Weight blocks per workgroup of the whole-expert GEMM: the most that divide
+// the block count, keep every block's scales in LDS (kBigMaxGroups) and leave
+// at least kBigMinWgs workgroups for the given chunk count, so the block loop
+// shares one set-up among several blocks where K is short.
+constexpr long kBigMinWgs = 512;
+static int big_blocks_per_wg(int nblocks, int groups_per_block, int chunks)
+{
+    int best = 1;
+    for (int n = 1; n <= nblocks; ++n) {
+        if (nblocks % n || n * groups_per_block > kBigMaxGroups) continue;
+        if ((long)chunks * (nblocks / n) < kBigMinWgs) break;
+        best = n;
     }
-#pragma unroll
-    for (int mt = 0; mt < kBigMA / 2; ++mt) {
-        if (mt >= ma_w) continue;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int m = 32 * (t0 + mt) + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (m >= rows) continue;
-            if constexpr (kW13) {
-                const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
-                const int i = 128 * nb + 32 * cg + col;
-                const int ip = (i & ~7) | pair_pos(i & 7);
-                g.h_out[(size_t)(pbase + m) * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
-            } else {
-                const float wv = s_wgt[m];
-                uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * nb + 64 * cg + col;
-                yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
-                yr[32] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
-            }
-        }
-    }
+    return best;
 }
 
 // out[t][n] = bf16( sum_j y[t][j][n] (+ y[t][k][n] for the shared expert) ),
@@ -917,7 +954,10 @@ static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hi
     if constexpr (MODE == kRoutedW13 || MODE == kRoutedW2) {
         const unsigned grid = groups * 8 * nblocks;
         if (big) {
-            moe_gemm_big_kernel<MODE><<<grid, kBigThreads, 0, st>>>(g, nblocks);
+            // chunks: about one per expert for balanced routing (the list has
+            // room for at most S / kBigRows + E, about twice that)
+            const int nbg = MODE == kRoutedW2 ? big_blocks_per_wg(nblocks, g.K / kBigKS, ntiles_max / 2) : 1;
+            moe_gemm_big_kernel<MODE><<<groups * 8 * (nblocks / nbg), kBigThreads, 0, st>>>(g, nblocks, nbg);
             return hipGetLastError();
         }
         if (g.small_rows > 0) {
