@@ -37,16 +37,21 @@ __device__ __forceinline__ int clamp_expert(int id, int E)
 //    logits of a token with one 32-byte coherent store, as order-preserving
 //    keys, which are never zero; then it is done (no wait, no counter).
 //    The last workgroup, dispatched after every producer, first converts x to
-//    nibble-pair order with its chunk sums (for the gate/up kernel), then,
-//    one wave per token, reads the token's keys until none is zero, selects
-//    the experts, and sets the keys back to zero for the next call; for the
-//    routing-only entry point it then builds the expert permutation.  ("MoE
-//    block (decode-05)": the router's last CTA does the top-k, the
-//    renormalisation and the block alignment, with no separate kernel.)
-//    The keys live in a fixed zeroed region of the workspace that no other
-//    path writes.  The wait for them is bounded, so the kernel always ends;
-//    every producer is resident or done by the time the last workgroup runs,
-//    so the bound is never reached in practice.
+//    nibble-pair order with its chunk sums (for the gate/up kernel), then
+//    reads each token's keys until none is zero, selects the experts, and
+//    sets the keys back to zero for the next call; for the routing-only
+//    entry point it then builds the expert permutation.  With fewer tokens
+//    than waves, several waves watch a token with staggered polls: one
+//    coherent load round trip (about 1.2 us on this part) is the largest
+//    step of the routing, and staggering shortens the wait from the last key
+//    landing to a poll that sees it.  ("MoE block (decode-05)": the router's
+//    last CTA does the top-k, the renormalisation and the block alignment,
+//    with no separate kernel.)  The keys live in a fixed zeroed region of the
+//    workspace that no other path writes.  The wait for them is bounded, so
+//    the kernel always ends; every producer is resident or done by the time
+//    the last workgroup runs (workgroups are dispatched in block order), so
+//    the bound is not reached in practice, and a wait that does reach it sets
+//    kStatusKeyWait.
 // ---------------------------------------------------------------------------
 constexpr int kRtWaves = 8;
 constexpr uint32_t kKeySpinLimit = 1u << 22;   // reads of a token's keys before giving up
@@ -68,42 +73,58 @@ __device__ __forceinline__ uint32_t logit_key(float l)
     return k == 0u ? 1u : k;
 }
 
-// One token's routing from its published keys (one wave).  A wave that gives
-// up waiting sets kStatusKeyWait in the sticky status word and routes on the
-// keys it has (absent keys read as 0, below every logit).
+// One token's routing from its published keys.  Several waves may watch
+// one token: each polls the keys (its first poll delayed by `delay` short
+// sleeps, so that the waves' polls are spread over one load round trip
+// instead of arriving together), the first to see every key claims the token
+// in LDS and routes it, and the others stop at their next poll.  Returns true
+// on the wave that routed (`out` is valid there).  A wave that gives up
+// waiting claims the token as well, sets kStatusKeyWait in the sticky status
+// word and routes on the keys it has (absent keys read as 0, below every
+// logit).
+constexpr int kPollRoundTrip = 48;   // s_sleep(1) periods in about one coherent load round trip
+
 template <int KPL>
-__device__ TopkLane route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds, uint32_t *ctrl)
+__device__ bool route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds, uint32_t *ctrl,
+                            int *claim, int delay, TopkLane &out)
 {
+    for (int i = 0; i < delay; ++i) __builtin_amdgcn_s_sleep(1);
     uint32_t val[KPL];
     bool missing = true;
-    for (uint32_t spin = 0; spin < kKeySpinLimit && missing; ++spin) {
+    for (uint32_t spin = 0; spin < kKeySpinLimit; ++spin) {
+        if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int *>(claim))) return false;
         bool miss = false;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
             const int e = lane + kWave * i;
-            val[i] = e < E ? load_coherent(keys + e) : 0u;
-            miss |= e < E && val[i] == 0u;
+            const uint32_t v = load_coherent(keys + min(e, E - 1));
+            val[i] = e < E ? v : 0u;
+            miss |= e < E && v == 0u;
         }
         missing = __ballot(miss) != 0;
+        if (!missing) break;
     }
+    int won = 0;
+    if (lane == 0) won = atomicCAS(claim, 0, 1) == 0;
+    if (!__builtin_amdgcn_readfirstlane(won)) return false;
     if (missing && lane == 0) set_status(ctrl, kStatusKeyWait);
-    const TopkLane r = wave_topk_keys<KPL>(val, k, lane, lds);
+    out = wave_topk_keys<KPL>(val, k, lane, lds);
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + kWave * i;
         if (e < E) store_coherent(keys + e, 0u);   // ready for the next call
     }
-    return r;
+    return true;
 }
 
-__device__ __forceinline__ TopkLane route_token_any(uint32_t *keys, int E, int k, int lane,
-                                                    uint32_t *lds, uint32_t *ctrl)
+__device__ __forceinline__ bool route_token_any(uint32_t *keys, int E, int k, int lane, uint32_t *lds,
+                                                uint32_t *ctrl, int *claim, int delay, TopkLane &out)
 {
-    if (E <= 64) return route_token<1>(keys, E, k, lane, lds, ctrl);
-    if (E <= 128) return route_token<2>(keys, E, k, lane, lds, ctrl);
-    if (E <= 256) return route_token<4>(keys, E, k, lane, lds, ctrl);
-    if (E <= 512) return route_token<8>(keys, E, k, lane, lds, ctrl);
-    return route_token<16>(keys, E, k, lane, lds, ctrl);
+    if (E <= 64) return route_token<1>(keys, E, k, lane, lds, ctrl, claim, delay, out);
+    if (E <= 128) return route_token<2>(keys, E, k, lane, lds, ctrl, claim, delay, out);
+    if (E <= 256) return route_token<4>(keys, E, k, lane, lds, ctrl, claim, delay, out);
+    if (E <= 512) return route_token<8>(keys, E, k, lane, lds, ctrl, claim, delay, out);
+    return route_token<16>(keys, E, k, lane, lds, ctrl, claim, delay, out);
 }
 
 // x of the T tokens in nibble-pair order (ws.xp) with the sums of its 32-value
@@ -146,18 +167,26 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
     __shared__ uint32_t s_topk[kRtWaves][kTopkLds];
     __shared__ int32_t s_ids[kDecodeMaxTokens * kMaxTopK];
     __shared__ int32_t s_run[kMaxExperts];
+    __shared__ int s_claim[kDecodeMaxTokens];
     const Dims &d = r.d;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const bool publish = r.tail != kTailNone;
 
     if (blockIdx.x == gridDim.x - 1) {
         // ---- routing workgroup ----
+        // (the barrier before the stores of transform_x: a barrier after
+        // them would wait for the stores to complete)
+        if (tid < kDecodeMaxTokens) s_claim[tid] = 0;
+        __syncthreads();
         transform_x(r.x, d, r.ws, tid);
         if (!publish) return;
-        for (int t = wave; t < d.T; t += kRtWaves) {
-            const TopkLane tk = route_token_any(r.ws.dec_keys + (size_t)t * d.E, d.E, d.k, lane,
-                                                s_topk[wave], r.ws.ctrl);
-            if (lane < d.k) {
+        // with fewer tokens than waves, kRtWaves / T waves watch each token
+        const int per = d.T >= kRtWaves ? 1 : kRtWaves / d.T;
+        for (int t = wave / per; t < d.T; t += kRtWaves / per) {
+            TopkLane tk;
+            const bool mine = route_token_any(r.ws.dec_keys + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave],
+                                              r.ws.ctrl, &s_claim[t], (wave % per) * (kPollRoundTrip / per), tk);
+            if (mine && lane < d.k) {
                 const int id = clamp_expert(tk.id, d.E);
                 r.ro.ids[t * d.k + lane] = id;
                 r.ro.weights[t * d.k + lane] = tk.w;
