@@ -185,6 +185,30 @@ int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
                                 size_t workspace_bytes, void *hip_stream,
                                 void *const *events);
 
+/* moe_int4_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; the workspace is a static device array
+ * of MOE_INT4_NOALLOC_SCRATCH_BYTES inside the library, one per device, held
+ * until the process ends.  Shapes whose moe_int4_workspace_bytes() exceeds
+ * that size are rejected with MOE_INT4_EWORKSPACE before anything is
+ * enqueued.  The first call on a device also enqueues, ahead of its own
+ * kernels, one small kernel that clears the scratch's control prefix.  Every
+ * call on a device shares that device's scratch: calls that overlap on one
+ * device (two streams, or two threads) race and their results are
+ * undefined.  The stream must belong to the current device.
+ *   status  uint32 (device memory, 4-byte aligned) or NULL: failed bounded
+ *           waits OR their MOE_INT4_STATUS_* bits into it (never cleared by
+ *           the library); with NULL they are not reported.
+ * Otherwise identical to moe_int4_forward (same kernels, same results). */
+#define MOE_INT4_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t moe_int4_forward_noalloc(const uint16_t *x, const uint16_t *router_w,
+                                 const int32_t *w13_packed, const uint16_t *w13_scales,
+                                 const int32_t *w2_packed, const uint16_t *w2_scales,
+                                 int32_t top_k, uint16_t *out,
+                                 const moe_int4_shape *shape,
+                                 const moe_shared_int6 *shared, uint32_t *status,
+                                 void *hip_stream);
+
 /* Load-time INT4 quantizer ("Running 125B MoE on Three 3090s - vLLM
  * Optimization Edition", section 7, which quantizes the draft head's experts
  * to symmetric INT4 in groups of 128 by rounding to nearest, choosing each

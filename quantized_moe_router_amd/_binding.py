@@ -52,21 +52,23 @@ def lib() -> ctypes.CDLL:
         L.moe_int4_experts.argtypes = [P] * 11 + [ctypes.c_size_t, P]
         L.moe_int4_forward.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P]
         L.moe_int4_forward_traced.argtypes = [P] * 6 + [_c_i32, P, P, P, P, ctypes.c_size_t, P, P]
+        L.moe_int4_forward_noalloc.argtypes = [P] * 6 + [_c_i32, P, P, P, P, P]
         L.moe_int4_quantize.argtypes = [P, _c_i32, _c_i32, _c_i32, P, P, P]
         L.moe_int8_linear_workspace_bytes.argtypes = [_c_i32] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
         L.moe_int8_linear.argtypes = [P, P, P] + [_c_i32] * 4 + [P, P, ctypes.c_size_t, P]
         L.moe_int4_last_error.restype = ctypes.c_char_p
         L.moe_int4_version.restype = ctypes.c_char_p
         for f in ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts", "moe_int4_forward",
-                  "moe_int4_forward_traced", "moe_int4_quantize", "moe_int8_linear_workspace_bytes",
-                  "moe_int8_linear"):
+                  "moe_int4_forward_traced", "moe_int4_forward_noalloc", "moe_int4_quantize",
+                  "moe_int8_linear_workspace_bytes", "moe_int8_linear"):
             getattr(L, f).restype = _c_i32
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_int4_workspace_bytes", "moe_int4_route", "moe_int4_experts",
-            "moe_int4_forward", "moe_int4_forward_traced", "moe_int4_quantize",
+            "moe_int4_forward", "moe_int4_forward_traced", "moe_int4_forward_noalloc",
+            "moe_int4_quantize",
             "moe_int8_linear_workspace_bytes", "moe_int8_linear",
             "moe_int4_last_error", "moe_int4_version")
 
@@ -169,6 +171,20 @@ def moe_int4_forward_traced(x, router_w, w13_packed, w13_scales, w2_packed, w2_s
                                          _ptr(w2_packed), _ptr(w2_scales), int(top_k), _ptr(out),
                                          ctypes.byref(shape), ctypes.byref(shared) if shared else None,
                                          _ptr(workspace), workspace.numel(), _stream(stream), arr))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_INT4_NOALLOC_SCRATCH_BYTES
+
+
+def moe_int4_forward_noalloc(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k: int,
+                             out, shape: MoeShape, shared: MoeSharedInt6 | None, status=None,
+                             stream=None):
+    """moe_int4_forward without a workspace (the library's static per-device
+    scratch); status: optional device uint32 tensor that failed waits OR into."""
+    _check(lib().moe_int4_forward_noalloc(_ptr(x), _ptr(router_w), _ptr(w13_packed), _ptr(w13_scales),
+                                          _ptr(w2_packed), _ptr(w2_scales), int(top_k), _ptr(out),
+                                          ctypes.byref(shape), ctypes.byref(shared) if shared else None,
+                                          _ptr(status), _stream(stream)))
 
 
 def moe_int4_quantize(w, rows: int, cols: int, packed, scales, group: int = 128, stream=None):

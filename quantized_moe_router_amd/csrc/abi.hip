@@ -175,6 +175,7 @@ int32_t check_workspace(const Dims &d, void *ws, size_t bytes, Workspace *out)
     Workspace w{};
     w.dec_keys = reinterpret_cast<uint32_t *>(b + L.dec_keys);
     w.ctrl = reinterpret_cast<uint32_t *>(b + L.ctrl);
+    w.status = w.ctrl;
     w.logits = reinterpret_cast<float *>(b + L.logits);
     w.ids = reinterpret_cast<int32_t *>(b + L.ids);
     w.weights = reinterpret_cast<float *>(b + L.weights);
@@ -228,6 +229,61 @@ static_assert(kKeysBytes + kCtrlBytes == MOE_INT4_WS_PREFIX_BYTES, "control pref
 static_assert(kStatusKeyWait == MOE_INT4_STATUS_KEY_WAIT && kStatusRouteWait == MOE_INT4_STATUS_ROUTE_WAIT &&
                   kStatusHWait == MOE_INT4_STATUS_H_WAIT,
               "status bits");
+
+// ---------------------------------------------------------------------------
+// Static scratch of moe_int4_forward_noalloc: the workspace as a file-scope
+// device array, so that the entry point allocates nothing.  Each device the
+// library runs on holds its own copy (kScratchBytes) until the process ends;
+// host code uses only the per-device address from hipGetSymbolAddress (the
+// array's name in host code is a host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)MOE_INT4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of `scratch` per device, null until set up
+
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch, set up on its first use: the symbol's
+// address on that device, then its control prefix cleared by a fill kernel
+// on the caller's stream, ahead of the first call's kernels.
+int32_t device_scratch(hipStream_t st, void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_INT4_EDEVICE, "no HIP device is current");
+    if (st) {
+        int sdev = -1;
+        if (hipStreamGetDevice(st, &sdev) != hipSuccess)
+            return fail(MOE_INT4_EINVAL, "hipStreamGetDevice failed for the given stream");
+        if (sdev != dev)
+            return fail(MOE_INT4_EINVAL, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_INT4_EDEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        const int words = (int)(MOE_INT4_WS_PREFIX_BYTES / 4);
+        zero_words_kernel<<<(words + 255) / 256, 256, 0, st>>>(reinterpret_cast<uint32_t *>(p), words);
+        int32_t rc = launched(hipGetLastError(), "scratch clear");
+        if (rc) return rc;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MOE_INT4_OK;
+}
+
+}  // namespace
 
 }  // namespace moe
 
@@ -303,27 +359,42 @@ int32_t moe_int4_experts(const uint16_t *x, const int32_t *topk_ids, const float
     return launched(launch_prefill_experts(a, d, ws, ro, st, nullptr), "experts");
 }
 
-static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
-                           const int32_t *w13_packed, const uint16_t *w13_scales,
-                           const int32_t *w2_packed, const uint16_t *w2_scales, int32_t top_k,
-                           uint16_t *out, const moe_int4_shape *shape,
-                           const moe_shared_int6 *shared, void *workspace,
-                           size_t workspace_bytes, void *hip_stream, void *const *events)
+// The host checks of the whole-layer entry points that do not involve the
+// workspace (T = 0 passes without pointer checks: it is a no-op).
+static int32_t forward_args(const uint16_t *x, const uint16_t *router_w, const int32_t *w13_packed,
+                            const uint16_t *w13_scales, const int32_t *w2_packed,
+                            const uint16_t *w2_scales, int32_t top_k, const uint16_t *out,
+                            const moe_int4_shape *shape, const moe_shared_int6 *shared, Dims *d)
 {
-    g_error.clear();
-    Dims d;
-    int32_t rc = check_shape(shape, shared, &d);
+    int32_t rc = check_shape(shape, shared, d);
     if (rc) return rc;
     if (top_k != shape->top_k)
         return fail(MOE_INT4_EINVAL, "top_k=%d differs from shape->top_k=%d", top_k, shape->top_k);
-    if (d.T == 0) return MOE_INT4_OK;
+    if (d->T == 0) return MOE_INT4_OK;
     rc = check_ptrs({{"x", x}, {"router_w", router_w}, {"w13_packed", w13_packed},
                      {"w13_scales", w13_scales}, {"w2_packed", w2_packed},
                      {"w2_scales", w2_scales}, {"out", out}});
     if (rc) return rc;
     if ((const void *)out == (const void *)x) return fail(MOE_INT4_EINVAL, "out aliases x");
+    return MOE_INT4_OK;
+}
+
+static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
+                           const int32_t *w13_packed, const uint16_t *w13_scales,
+                           const int32_t *w2_packed, const uint16_t *w2_scales, int32_t top_k,
+                           uint16_t *out, const moe_int4_shape *shape,
+                           const moe_shared_int6 *shared, void *workspace,
+                           size_t workspace_bytes, void *hip_stream, void *const *events,
+                           uint32_t *status = nullptr)
+{
+    g_error.clear();
+    Dims d;
+    int32_t rc = forward_args(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out,
+                              shape, shared, &d);
+    if (rc || d.T == 0) return rc;
     Workspace ws;
     if ((rc = check_workspace(d, workspace, workspace_bytes, &ws))) return rc;
+    if (status) ws.status = status;
     if ((rc = check_device())) return rc;
     hipStream_t st = (hipStream_t)hip_stream;
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -370,6 +441,33 @@ int32_t moe_int4_forward_traced(const uint16_t *x, const uint16_t *router_w,
     if (!events) return fail(MOE_INT4_EINVAL, "events is NULL");
     return forward_impl(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out,
                         shape, shared, workspace, workspace_bytes, hip_stream, events);
+}
+
+int32_t moe_int4_forward_noalloc(const uint16_t *x, const uint16_t *router_w,
+                                 const int32_t *w13_packed, const uint16_t *w13_scales,
+                                 const int32_t *w2_packed, const uint16_t *w2_scales,
+                                 int32_t top_k, uint16_t *out, const moe_int4_shape *shape,
+                                 const moe_shared_int6 *shared, uint32_t *status,
+                                 void *hip_stream)
+{
+    g_error.clear();
+    Dims d;
+    int32_t rc = forward_args(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out,
+                              shape, shared, &d);
+    if (rc) return rc;
+    const size_t need = workspace_size(d);
+    if (need > kScratchBytes)
+        return fail(MOE_INT4_EWORKSPACE,
+                    "this shape needs %zu bytes of workspace; the static scratch of "
+                    "moe_int4_forward_noalloc holds %zu (use moe_int4_forward with a workspace)",
+                    need, kScratchBytes);
+    if (status && ((uintptr_t)status & 3u)) return fail(MOE_INT4_EALIGN, "status is not 4-byte aligned");
+    if (d.T == 0) return MOE_INT4_OK;
+    if ((rc = check_device())) return rc;
+    void *ws = nullptr;
+    if ((rc = device_scratch((hipStream_t)hip_stream, &ws))) return rc;
+    return forward_impl(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out, shape,
+                        shared, ws, kScratchBytes, hip_stream, nullptr, status);
 }
 
 int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t group,

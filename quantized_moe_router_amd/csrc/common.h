@@ -260,9 +260,9 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v)
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Record a failed bounded wait in the sticky status word (a vector atomic).
-__device__ __forceinline__ void set_status(uint32_t *ctrl, uint32_t bit)
+__device__ __forceinline__ void set_status(uint32_t *status, uint32_t bit)
 {
-    __hip_atomic_fetch_or(ctrl, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Cross-lane sums with DPP lane moves (VALU only; a shuffle would go through
@@ -324,6 +324,7 @@ struct Workspace {
     // zero between calls (a fixed prefix of every layout)
     uint32_t *dec_keys;      // [kDecodeMaxTokens * kMaxExperts] decode router keys, 0 = unset
     uint32_t *ctrl;          // [kCtrlBytes / 4] control words: [0] sticky status, then counters
+    uint32_t *status;        // where failed bounded waits are recorded (ctrl[0] unless redirected)
     // routing
     float *logits;           // [T][E]
     int32_t *ids;            // [T][k]   (forward: internal copy)

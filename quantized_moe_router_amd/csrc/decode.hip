@@ -85,7 +85,7 @@ __device__ __forceinline__ uint32_t logit_key(float l)
 constexpr int kPollRoundTrip = 48;   // s_sleep(1) periods in about one coherent load round trip
 
 template <int KPL>
-__device__ bool route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds, uint32_t *ctrl,
+__device__ bool route_token(uint32_t *keys, int E, int k, int lane, uint32_t *lds, uint32_t *status,
                             int *claim, int delay, TopkLane &out)
 {
     for (int i = 0; i < delay; ++i) __builtin_amdgcn_s_sleep(1);
@@ -107,7 +107,7 @@ __device__ bool route_token(uint32_t *keys, int E, int k, int lane, uint32_t *ld
     int won = 0;
     if (lane == 0) won = atomicCAS(claim, 0, 1) == 0;
     if (!__builtin_amdgcn_readfirstlane(won)) return false;
-    if (missing && lane == 0) set_status(ctrl, kStatusKeyWait);
+    if (missing && lane == 0) set_status(status, kStatusKeyWait);
     out = wave_topk_keys<KPL>(val, k, lane, lds);
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
@@ -118,13 +118,13 @@ __device__ bool route_token(uint32_t *keys, int E, int k, int lane, uint32_t *ld
 }
 
 __device__ __forceinline__ bool route_token_any(uint32_t *keys, int E, int k, int lane, uint32_t *lds,
-                                                uint32_t *ctrl, int *claim, int delay, TopkLane &out)
+                                                uint32_t *status, int *claim, int delay, TopkLane &out)
 {
-    if (E <= 64) return route_token<1>(keys, E, k, lane, lds, ctrl, claim, delay, out);
-    if (E <= 128) return route_token<2>(keys, E, k, lane, lds, ctrl, claim, delay, out);
-    if (E <= 256) return route_token<4>(keys, E, k, lane, lds, ctrl, claim, delay, out);
-    if (E <= 512) return route_token<8>(keys, E, k, lane, lds, ctrl, claim, delay, out);
-    return route_token<16>(keys, E, k, lane, lds, ctrl, claim, delay, out);
+    if (E <= 64) return route_token<1>(keys, E, k, lane, lds, status, claim, delay, out);
+    if (E <= 128) return route_token<2>(keys, E, k, lane, lds, status, claim, delay, out);
+    if (E <= 256) return route_token<4>(keys, E, k, lane, lds, status, claim, delay, out);
+    if (E <= 512) return route_token<8>(keys, E, k, lane, lds, status, claim, delay, out);
+    return route_token<16>(keys, E, k, lane, lds, status, claim, delay, out);
 }
 
 // x of the T tokens in nibble-pair order (ws.xp) with the sums of its 32-value
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kRtWaves *kWave) void router_kernel(RouterArgs r)
         for (int t = wave / per; t < d.T; t += kRtWaves / per) {
             TopkLane tk;
             const bool mine = route_token_any(r.ws.dec_keys + (size_t)t * d.E, d.E, d.k, lane, s_topk[wave],
-                                              r.ws.ctrl, &s_claim[t], (wave % per) * (kPollRoundTrip / per), tk);
+                                              r.ws.status, &s_claim[t], (wave % per) * (kPollRoundTrip / per), tk);
             if (mine && lane < d.k) {
                 const int id = clamp_expert(tk.id, d.E);
                 r.ro.ids[t * d.k + lane] = id;

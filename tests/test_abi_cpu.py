@@ -86,6 +86,31 @@ def test_forward_argument_errors():
     assert _forward(s, {"ws": None}) == B.EINVAL
 
 
+def _noalloc(shape, ptrs=None, top_k=10, status=None):
+    p = dict(x=FAKE, router=FAKE, w13p=FAKE, w13s=FAKE, w2p=FAKE, w2s=FAKE, out=FAKE * 2)
+    p.update(ptrs or {})
+    return B.lib().moe_int4_forward_noalloc(p["x"], p["router"], p["w13p"], p["w13s"], p["w2p"], p["w2s"],
+                                            top_k, p["out"], ctypes.byref(shape), None, status, None)
+
+
+def test_noalloc_argument_errors():
+    L = B.lib()
+    s = _shape()
+    assert _noalloc(s, {"x": None}) == B.EINVAL
+    assert "x is NULL" in L.moe_int4_last_error().decode()
+    assert _noalloc(s, top_k=8) == B.EINVAL
+    assert _noalloc(s, {"out": FAKE}) == B.EINVAL          # out aliases x
+    assert _noalloc(s, status=FAKE + 2) == B.EALIGN
+    big = _shape(tokens=8192)
+    assert B.workspace_bytes(big) > B.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big) == B.EWORKSPACE
+    assert "static scratch" in L.moe_int4_last_error().decode()
+    assert _noalloc(_shape(tokens=0)) == B.OK              # no-op
+    with open(os.path.join(ROOT, "include", "moe_int4.h")) as f:
+        m = re.search(r"#define MOE_INT4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+
+
 def test_route_and_experts_argument_errors():
     s = _shape()
     L = B.lib()
@@ -106,6 +131,7 @@ def test_no_device_is_reported_not_crashed():
         pytest.skip("a GPU is present")
     rc = _forward(_shape())
     assert rc == B.EDEVICE
+    assert _noalloc(_shape()) == B.EDEVICE
 
 
 @pytest.mark.parametrize("rows,cols,group,msg", [
