@@ -490,12 +490,17 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
 // Whole-expert grouped GEMM (many slots per expert).  A workgroup takes one
 // chunk of up to 192 sorted rows of one expert (all of an expert's rows for
 // balanced routing) and one block of 256 weight rows, so every weight is
-// fetched from memory once per chunk.  Eight waves, two per SIMD: wave
-// (g, c) takes the weight rows [64 c, 64 c + 64) of the block (two 32-wide
-// column tiles) and row group g of the chunk: the first ceil(T / 2) of its T
-// 32-row tiles for g = 0, the rest for g = 1, as v_mfma_f32_32x32x16_f16
-// tiles.  The two waves of a SIMD convert the same weights (each for its
-// own rows) and keep the matrix core busy while the other waits.
+// fetched from memory once per chunk.  Wave c of column group c takes the
+// weight rows [64 c, 64 c + 64) of the block (two 32-wide column tiles), as
+// v_mfma_f32_32x32x16_f16 tiles:
+//   * gate/up: four waves, one per SIMD, each with all T 32-row tiles of the
+//     chunk, so every weight is converted once (with two row groups each
+//     weight was converted by both, and the conversions outweighed the
+//     matrix work of a step; one wave per SIMD with up to 6 x 2 accumulator
+//     tiles: 8192 tokens 659 -> 590 us);
+//   * down: eight waves, two per SIMD: row group g takes the first
+//     ceil(T / 2) row tiles for g = 0, the rest for g = 1 (its block loop
+//     does not fit the registers of one wave per SIMD).
 //   * K advances one 128-wide weight group (one scale per row) per stage, with
 //     one barrier per stage.  The chunk's scales are copied to LDS once.
 //   * Weights: each wave loads its own rows straight into registers, two
@@ -512,19 +517,24 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
 //     barriers keep that preparation in the shadow of the step's MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kBigMA = kBigRows / 32;   // row tiles per chunk
-constexpr int kBigWaves = 8;
-constexpr int kBigThreads = kBigWaves * kWave;
 constexpr int kBigKS = 128;             // K per stage (one weight group)
 constexpr int kBigLdsRow = kBigKS + 8;  // padded LDS row (fp16 elements)
 constexpr int kBigMaxGroups = kMaxHidden / kGroup;   // scales per weight row
-constexpr int kBigStageRows = kBigThreads / 8;        // rows one staging pass covers (8 threads per row)
+// waves per workgroup: 4 for the gate/up projection (one per SIMD, each with
+// every row tile of the chunk, so each weight is converted once), 8 for the
+// down projection (two row groups: its block loop needs the registers)
+__host__ __device__ constexpr int big_waves(int mode) { return mode == kRoutedW13 ? 4 : 8; }
 
 template <int MODE>
-__global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g, int nblocks, int nbg)
+__global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void moe_gemm_big_kernel(GemmArgs g, int nblocks, int nbg)
 {
     static_assert(MODE == kRoutedW13 || MODE == kRoutedW2, "routed modes only");
     static_assert(kBigKS == kGroup, "one weight group per stage");
     constexpr bool kW13 = MODE == kRoutedW13;
+    constexpr int kBigWaves = big_waves(MODE);
+    constexpr int kBigThreads = kBigWaves * kWave;
+    constexpr int kRowGroups = kBigWaves / 4;
+    constexpr int kBigStageRows = kBigThreads / 8;   // rows one staging pass covers (8 threads per row)
     // several weight blocks per workgroup only for the down projection (its K
     // is short, so a block's set-up costs as much as a good part of its loop;
     // the gate/up projection's 20 groups of scales fill the LDS for one block)
@@ -545,7 +555,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
     if (tv.x < 0) return;   // empty slot
     const int e = tv.x & 0xFFFF, pbase = tv.y, rows = tv.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-    const int cg = wave & 3, rg = wave >> 2;   // column group, row group
+    const int cg = wave & 3, rg = wave >> 2;   // column group, row group (0 with 4 waves)
     const int K = g.K, nstages = K / kBigKS;
     // weight row of tile column c (0..255) of weight block nb: column group
     // c / 64, column tile (c / 32) & 1; block nb + 1 is kBlockRows rows on
@@ -597,12 +607,13 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
         bq[nt] = reinterpret_cast<const u32x4_t *>(bpe + (size_t)tile_row(b0, 64 * cg + 32 * nt + col) * bstride) + half;
     const int mtiles = (rows + 31) / 32;
     const int t0 = rg == 0 ? 0 : (mtiles + 1) / 2;   // first row tile of this wave's row group
+    constexpr int kMaxMA = kBigMA / kRowGroups;       // most row tiles of one wave
     const int nst_all = nbg * nstages;                // stages over all the workgroup's blocks
 
-    f32x16_t acc[kBigMA / 2][2];
+    f32x16_t acc[kMaxMA][2];
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kBigMA / 2; ++i)
+        for (int i = 0; i < kMaxMA; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -766,13 +777,28 @@ __global__ __launch_bounds__(kBigThreads, 2) void moe_gemm_big_kernel(GemmArgs g
         if (gs + 1 < nst_all) stage(gs + 1, 1, 2);
         if constexpr (!kBlockLoop) store_block(b0);
     };
-    static_assert(kBigMA == 6 && kNO == 3, "K loop variants below");
-    // row tiles: row group 0 takes ceil(T / 2), row group 1 the rest; the
-    // staging passes cover ceil(T / 2) * 64 rows
+    static_assert(kBigMA == 6 && kNO == 6 / kRowGroups, "K loop variants below");
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+    if constexpr (kRowGroups == 1) {
+        // every wave takes all T row tiles; the staging passes cover T * 32 rows
+        using I4 = std::integral_constant<int, 4>;
+        using I5 = std::integral_constant<int, 5>;
+        using I6 = std::integral_constant<int, 6>;
+        switch (mtiles) {
+        case 1: kloop(I1{}, I1{}); break;
+        case 2: kloop(I2{}, I2{}); break;
+        case 3: kloop(I3{}, I3{}); break;
+        case 4: kloop(I4{}, I4{}); break;
+        case 5: kloop(I5{}, I5{}); break;
+        default: kloop(I6{}, I6{}); break;
+        }
+        return;
+    }
+    // row tiles: row group 0 takes ceil(T / 2), row group 1 the rest; the
+    // staging passes cover ceil(T / 2) * 64 rows
     switch (mtiles * 2 + rg) {
     case 2: kloop(I1{}, I1{}); break;   // 1 tile: group 0 has it
     case 3: kloop(I0{}, I1{}); break;
@@ -957,7 +983,7 @@ static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hi
             // chunks: about one per expert for balanced routing (the list has
             // room for at most S / kBigRows + E, about twice that)
             const int nbg = MODE == kRoutedW2 ? big_blocks_per_wg(nblocks, g.K / kBigKS, ntiles_max / 2) : 1;
-            moe_gemm_big_kernel<MODE><<<groups * 8 * (nblocks / nbg), kBigThreads, 0, st>>>(g, nblocks, nbg);
+            moe_gemm_big_kernel<MODE><<<groups * 8 * (nblocks / nbg), big_waves(MODE) * kWave, 0, st>>>(g, nblocks, nbg);
             return hipGetLastError();
         }
         if (g.small_rows > 0) {
