@@ -498,9 +498,13 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
 //     weight was converted by both, and the conversions outweighed the
 //     matrix work of a step; one wave per SIMD with up to 6 x 2 accumulator
 //     tiles: 8192 tokens 659 -> 590 us);
-//   * down: eight waves, two per SIMD: row group g takes the first
+//   * routed down: eight waves, two per SIMD: row group g takes the first
 //     ceil(T / 2) row tiles for g = 0, the rest for g = 1 (its block loop
-//     does not fit the registers of one wave per SIMD).
+//     does not fit the registers of one wave per SIMD);
+//   * the shared expert's gate/up (INT6, group 64; every token a row,
+//     chunk c the tokens [192 c, 192 c + 192)): four waves.  Its down
+//     projection stays with moe_gemm_kernel (K = 640 is short: here it took
+//     66 us against 54 at 8192 tokens).
 //   * K advances one 128-wide weight group (one scale per row) per stage, with
 //     one barrier per stage.  The chunk's scales are copied to LDS once.
 //   * Weights: each wave loads its own rows straight into registers, two
@@ -520,27 +524,34 @@ constexpr int kBigMA = kBigRows / 32;   // row tiles per chunk
 constexpr int kBigKS = 128;             // K per stage (one weight group)
 constexpr int kBigLdsRow = kBigKS + 8;  // padded LDS row (fp16 elements)
 constexpr int kBigMaxGroups = kMaxHidden / kGroup;   // scales per weight row
-// waves per workgroup: 4 for the gate/up projection (one per SIMD, each with
+// waves per workgroup: 4 for the gate/up projections (one per SIMD, each with
 // every row tile of the chunk, so each weight is converted once), 8 for the
-// down projection (two row groups: its block loop needs the registers)
-__host__ __device__ constexpr int big_waves(int mode) { return mode == kRoutedW13 ? 4 : 8; }
+// down projections (two row groups: the block loop needs the registers)
+__host__ __device__ constexpr int big_waves(int mode) { return mode == kRoutedW2 ? 8 : 4; }
+constexpr int kBigMaxGroups6 = kMaxHidden / kShGroup;   // INT6 scales per weight row
 
 template <int MODE>
 __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void moe_gemm_big_kernel(GemmArgs g, int nblocks, int nbg)
 {
-    static_assert(MODE == kRoutedW13 || MODE == kRoutedW2, "routed modes only");
-    static_assert(kBigKS == kGroup, "one weight group per stage");
-    constexpr bool kW13 = MODE == kRoutedW13;
+    static_assert(kBigKS == kGroup, "one INT4 weight group per stage");
+    static_assert(MODE != kSharedW2, "the shared down projection (K = its inter) runs in moe_gemm_kernel");
+    constexpr bool kW13 = MODE == kRoutedW13 || MODE == kSharedW13;
+    // the shared expert: INT6 codes in groups of 64 (two scale groups per
+    // stage), every token a row (chunk c = tokens [192 c, 192 c + 192))
+    constexpr bool kInt6 = MODE == kSharedW13 || MODE == kSharedW2;
+    constexpr int kScPerStage = kInt6 ? 2 : 1;
+    constexpr int kScRows = kInt6 ? kBigMaxGroups6 : kBigMaxGroups;
     constexpr int kBigWaves = big_waves(MODE);
     constexpr int kBigThreads = kBigWaves * kWave;
     constexpr int kRowGroups = kBigWaves / 4;
     constexpr int kBigStageRows = kBigThreads / 8;   // rows one staging pass covers (8 threads per row)
-    // several weight blocks per workgroup only for the down projection (its K
-    // is short, so a block's set-up costs as much as a good part of its loop;
-    // the gate/up projection's 20 groups of scales fill the LDS for one block)
-    constexpr bool kBlockLoop = !kW13;
+    // several weight blocks per workgroup only for the routed down projection
+    // (its K is short, so a block's set-up costs as much as a good part of its
+    // loop; the gate/up projection's 20 groups of scales fill the LDS for one
+    // block); the other modes take nbg = 1
+    constexpr bool kBlockLoop = MODE == kRoutedW2;
     __shared__ __align__(16) _Float16 s_a[2][kBigRows * kBigLdsRow];
-    __shared__ uint16_t s_sc[kBigMaxGroups][kNT];   // [block * groups + group][tile weight row] bf16 scales
+    __shared__ uint16_t s_sc[kScRows][kNT];   // [block * groups + group][tile weight row] bf16 scales
     __shared__ int s_tok[kBigRows];     // token of each chunk row (-1: none)
     __shared__ int s_yrow[kBigRows];    // down mode: row of y that each chunk row writes
     __shared__ float s_wgt[kBigRows];   // down mode: output factor of each chunk row
@@ -551,9 +562,18 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
     const int xcd = wid & 7, r = wid >> 3;
     const int ngroups_b = nblocks / nbg;
     const int b0 = (r % ngroups_b) * nbg, chunk = (r / ngroups_b) * 8 + xcd;
-    const int4 tv = g.tiles[chunk];
-    if (tv.x < 0) return;   // empty slot
-    const int e = tv.x & 0xFFFF, pbase = tv.y, rows = tv.z;
+    int e = 0, pbase, rows;
+    if constexpr (kInt6) {
+        pbase = chunk * kBigRows;
+        if (pbase >= g.T) return;   // past the last token
+        rows = min(kBigRows, g.T - pbase);
+    } else {
+        const int4 tv = g.tiles[chunk];
+        if (tv.x < 0) return;   // empty slot
+        e = tv.x & 0xFFFF;
+        pbase = tv.y;
+        rows = tv.z;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int cg = wave & 3, rg = wave >> 2;   // column group, row group (0 with 4 waves)
     const int K = g.K, nstages = K / kBigKS;
@@ -570,20 +590,25 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
     static_assert(kBigThreads >= kNT && kBigThreads >= kBigRows, "one thread per tile column and chunk row");
     if (tid < kNT) {
         // this thread's tile column's scales, every block of the workgroup -> LDS
+        const int spr = nstages * kScPerStage;   // scale groups per weight row
         for (int bi = 0; bi < nbg; ++bi) {
-            const uint16_t *sr = bse + (size_t)tile_row(b0 + bi, tid) * nstages;
-            for (int q = 0; q < nstages; ++q) s_sc[bi * nstages + q][tid] = sr[q];
+            const uint16_t *sr = bse + (size_t)tile_row(b0 + bi, tid) * spr;
+            for (int q = 0; q < spr; ++q) s_sc[bi * spr + q][tid] = sr[q];
         }
     }
     if (tid < kBigRows) {
         const int i = tid < rows ? tid : 0;
-        const int slot = g.sorted_slots[pbase + i];
-        const int tok = slot / g.k;
-        if constexpr (!kW13) {
-            s_wgt[tid] = g.weights[slot] * kScaleDown;   // routing weight times the 2^-10 of the scales
-            s_yrow[tid] = tok * (g.k + 1) + (slot - tok * g.k);
+        if constexpr (kInt6) {
+            s_tok[tid] = tid < rows ? pbase + i : -1;
+        } else {
+            const int slot = g.sorted_slots[pbase + i];
+            const int tok = slot / g.k;
+            if constexpr (!kW13) {
+                s_wgt[tid] = g.weights[slot] * kScaleDown;   // routing weight times the 2^-10 of the scales
+                s_yrow[tid] = tok * (g.k + 1) + (slot - tok * g.k);
+            }
+            s_tok[tid] = tid < rows ? tok : -1;
         }
-        s_tok[tid] = tid < rows ? tok : -1;
     }
     __syncthreads();
 
@@ -599,12 +624,17 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
                        : (uint32_t)(pbase + arow) * (uint32_t)K + 8 * c8;
     }
     const int col = lane & 31;
-    const size_t bstride = (size_t)K / 8;   // words per weight row
+    // a weight row's stage (128 inputs) is 64 bytes of INT4 or 96 of INT6;
+    // lane half h takes 16-byte pieces h and 2 + h of an INT4 stage, pieces
+    // 3 h .. 3 h + 2 (32-code blocks 2 h and 2 h + 1) of an INT6 one
+    constexpr int kU4Stage = kInt6 ? 6 : 4, kU4Lane = kInt6 ? 3 : 2;
+    const size_t bstride = kInt6 ? (size_t)K / 32 * 6 : (size_t)K / 8;   // words per weight row
     const size_t bblock = (size_t)kBlockRows * bstride / 4;   // 16-byte units from one block to the next
     const u32x4_t *bq[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-        bq[nt] = reinterpret_cast<const u32x4_t *>(bpe + (size_t)tile_row(b0, 64 * cg + 32 * nt + col) * bstride) + half;
+        bq[nt] = reinterpret_cast<const u32x4_t *>(bpe + (size_t)tile_row(b0, 64 * cg + 32 * nt + col) * bstride) +
+                 (kInt6 ? 3 * half : half);
     const int mtiles = (rows + 31) / 32;
     const int t0 = rg == 0 ? 0 : (mtiles + 1) / 2;   // first row tile of this wave's row group
     constexpr int kMaxMA = kBigMA / kRowGroups;       // most row tiles of one wave
@@ -627,7 +657,7 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
         constexpr int MA = decltype(ma_c)::value;
         constexpr int NO = decltype(no_c)::value;
         u32x4_t ra[NO][2];          // the next stage's activations
-        u32x4_t rb[3][2][2];        // weight groups in flight: [set][nt][piece]
+        u32x4_t rb[3][2][kU4Lane];  // weight stages in flight: [set][nt][piece]
         // global stage gs: block gs / nstages of the workgroup, K stage gs % nstages
         auto load_a_pass = [&](int gs, int o) __attribute__((always_inline)) {
             const uint16_t *src = abase + aoff[o] + (gs % nstages) * kBigKS;
@@ -641,21 +671,45 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
         };
         auto load_b_piece = [&](int gs, int set, int nt) __attribute__((always_inline)) {
             const int bi = gs / nstages, grp = gs - bi * nstages;
-            const u32x4_t *q = bq[nt] + bi * bblock + 4 * grp;   // 64 bytes per group; + half applied
-            rb[set][nt][0] = q[0];
-            rb[set][nt][1] = q[2];
+            const u32x4_t *q = bq[nt] + bi * bblock + kU4Stage * grp;   // the lane half's offset applied
+            if constexpr (kInt6) {
+                rb[set][nt][0] = q[0];
+                rb[set][nt][1] = q[1];
+                rb[set][nt][2] = q[2];
+            } else {
+                rb[set][nt][0] = q[0];
+                rb[set][nt][1] = q[2];
+            }
         };
         // fp16 scale pairs of global stage gs for this lane's two rows
         auto scales_of = [&](int gs, h2_t (&s2)[2]) {
+            const int sg = kInt6 ? 2 * gs + half : gs;   // INT6: the lane half's group of 64
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) s2[nt] = scale_pair(s_sc[gs][64 * cg + 32 * nt + col]);
+            for (int nt = 0; nt < 2; ++nt) s2[nt] = scale_pair(s_sc[sg][64 * cg + 32 * nt + col]);
         };
         // weight operands of MFMA step j (0..7) of the weight group in `set`
         auto dequant_step = [&](int set, const h2_t (&s2)[2], int j, f16x8_t (&out)[2]) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const u32x4_t v = rb[set][nt][j >> 2];
-                out[nt] = dequant_int4_f16(v[j & 3], s2[nt]);
+                if constexpr (kInt6) {
+                    // octet j & 3 of the lane's 32-code block j >> 2
+                    uint32_t w7[7];
+#pragma unroll
+                    for (int q = 0; q < 6; ++q) {
+                        const int dw = 6 * (j >> 2) + q;
+                        w7[q] = rb[set][nt][dw >> 2][dw & 3];
+                    }
+                    w7[6] = 0;
+                    switch (j & 3) {
+                    case 0: out[nt] = dequant_int6_octet<0>(w7, s2[nt]); break;
+                    case 1: out[nt] = dequant_int6_octet<1>(w7, s2[nt]); break;
+                    case 2: out[nt] = dequant_int6_octet<2>(w7, s2[nt]); break;
+                    default: out[nt] = dequant_int6_octet<3>(w7, s2[nt]); break;
+                    }
+                } else {
+                    const u32x4_t v = rb[set][nt][j >> 2];
+                    out[nt] = dequant_int4_f16(v[j & 3], s2[nt]);
+                }
             }
         };
         // outputs of weight block b from the accumulators
@@ -693,7 +747,10 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
             const int ngs = min(gs + 2, nst_all - 1);
             h2_t s2c[2];
             scales_of(gs, s2c);
-            const _Float16 *A = s_a[gs & 1] + (32 * t0 + col) * kBigLdsRow + 32 * half;
+            // the activations in the weights' K order: step j of half h is
+            // K = 64 (j / 4) + 32 h + 8 (j % 4) for INT4, 64 h + 32 (j / 4) +
+            // 8 (j % 4) for INT6
+            const _Float16 *A = s_a[gs & 1] + (32 * t0 + col) * kBigLdsRow + (kInt6 ? 64 : 32) * half;
             f16x8_t af[2][MA > 0 ? MA : 1];
 #pragma unroll
             for (int mt = 0; mt < MA; ++mt)
@@ -711,7 +768,7 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
                 if constexpr (MA > 0) {
                     f16x8_t bnext[2];
                     if (j < 7) {
-                        const int ko = 64 * ((j + 1) >> 2) + 8 * ((j + 1) & 3);
+                        const int ko = (kInt6 ? 32 : 64) * ((j + 1) >> 2) + 8 * ((j + 1) & 3);
 #pragma unroll
                         for (int mt = 0; mt < MA; ++mt)
                             af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kBigLdsRow + ko);
@@ -819,6 +876,7 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
 // at least kBigMinWgs workgroups for the given chunk count, so the block loop
 // shares one set-up among several blocks where K is short.
 constexpr long kBigMinWgs = 512;
+constexpr int kBigSharedMinTokens = 6144;   // the shared expert's whole-chunk gate/up GEMM from this many tokens (32 chunks)
 static int big_blocks_per_wg(int nblocks, int groups_per_block, int chunks)
 {
     int best = 1;
@@ -1041,10 +1099,18 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
         GemmArgs gs{};
         gs.x = ws.xh; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
         gs.T = d.T; gs.H = d.H; gs.I = d.sh_I; gs.k = d.k; gs.K = d.H;
-        if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) return e;
         GemmArgs gs2{};
         gs2.a16 = ws.sh_h; gs2.bp = a.sh_w2p; gs2.bs = a.sh_w2s; gs2.gate = ws.shared_gate; gs2.y_out = y;
         gs2.T = d.T; gs2.H = d.H; gs2.I = d.sh_I; gs2.k = d.k; gs2.K = d.sh_I;
+        if (d.T >= kBigSharedMinTokens) {
+            // whole-chunk gate/up GEMM: 192 tokens per workgroup and weight block
+            const int groups = (d.T + 8 * kBigRows - 1) / (8 * kBigRows);
+            const int nb13 = d.sh_I / 128;
+            moe_gemm_big_kernel<kSharedW13><<<groups * 8 * nb13, big_waves(kSharedW13) * kWave, 0, st>>>(gs, nb13, 1);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) {
+            return e;
+        }
         if ((e = launch_gemm<kSharedW2>(gs2, (d.T + kMT - 1) / kMT, d.H / kNT, st)) != hipSuccess) return e;
     }
     const size_t n8 = (size_t)d.T * d.H / 8;

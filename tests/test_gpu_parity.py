@@ -184,6 +184,20 @@ def test_many_rows_per_expert(T, shared):
     run_and_check(host, label=f"many rows per expert T={T} shared={shared}")
 
 
+def test_shared_expert_whole_chunk_gemm_ragged():
+    """From 6144 tokens the shared expert's gate/up runs as the whole-chunk
+    GEMM (192 tokens per workgroup): 6211 tokens end in a ragged chunk of 67.
+    Tokens of the first chunk, the last full one, the ragged one and random
+    ones are checked against the oracle."""
+    T = 6211
+    shape = synth.LayerShape(tokens=T, hidden=512, experts=16, top_k=2, inter=128)
+    host = synth.make_layer(shape, seed=61, shared=True)
+    rng = np.random.default_rng(61)
+    tokens = np.unique(np.concatenate([[0, 1, 191, 192], np.arange(5952, 5952 + 3), np.arange(T - 67, T),
+                                       rng.choice(T, 24, replace=False)]))
+    run_and_check(host, tokens=tokens, label="shared whole-chunk ragged T=6211")
+
+
 @pytest.mark.parametrize("H,I", [(256, 128), (768, 384)])
 def test_whole_expert_gemm_row_counts(H, I):
     """Caller routing that gives the experts every row count the whole-expert
