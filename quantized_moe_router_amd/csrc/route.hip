@@ -188,16 +188,35 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
     __shared__ int s_sum[16], s_nz[16];
     const int e = threadIdx.x, lane = e & (kWave - 1), wave = e >> 6;
     const int ec = e < d.E ? e : 0;
-    // kScanBatch chunks' loads in flight per pass (clamped addresses), summed
-    // in order
-    constexpr int kScanBatch = 32;
+    // Up to kScanKeep chunks: every count of the expert loaded at once and
+    // kept in registers for the bases (two 16-bit counts per register: a
+    // count is at most kPermChunk), so the pass costs one round of loads
+    // instead of one per batch and pass.  More chunks: kScanBatch loads in
+    // flight per batch (clamped addresses), summed in order, and loaded again
+    // for the bases.
+    constexpr int kScanKeep = 128, kScanBatch = 32;
+    static_assert(kPermChunk < 65536, "16-bit counts");
+    const bool keep = nchunks <= kScanKeep;
+    uint32_t kv[kScanKeep / 2];
     int total = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
-        int v[kScanBatch];
+    if (keep) {
 #pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + ec];
+        for (int u = 0; u < kScanKeep / 2; ++u) {
+            const int c = 2 * u;
+            const uint32_t a = (uint32_t)ws.chunk_hist[(size_t)min(c, nchunks - 1) * d.E + ec];
+            const uint32_t b = (uint32_t)ws.chunk_hist[(size_t)min(c + 1, nchunks - 1) * d.E + ec];
+            kv[u] = (c < nchunks ? a : 0u) | ((c + 1 < nchunks ? b : 0u) << 16);
+        }
 #pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) total += c0 + u < nchunks ? v[u] : 0;
+        for (int u = 0; u < kScanKeep / 2; ++u) total += (int)(kv[u] & 0xFFFFu) + (int)(kv[u] >> 16);
+    } else {
+        for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + ec];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) total += c0 + u < nchunks ? v[u] : 0;
+        }
     }
     if (e >= d.E) total = 0;
     int nz = (e < d.E && total > 0) ? 1 : 0;
@@ -213,16 +232,27 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(Dims d, Workspace ws, R
         ro.offsets[e] = off;
         if (nz) ws.active[1 + nz_pos] = e;
         int run = off;
-        for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
-            int v[kScanBatch];
+        if (keep) {
 #pragma unroll
-            for (int u = 0; u < kScanBatch; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + e];
+            for (int u = 0; u < kScanKeep / 2; ++u) {
+                const int c = 2 * u;
+                if (c < nchunks) ws.chunk_hist[(size_t)c * d.E + e] = run;
+                run += (int)(kv[u] & 0xFFFFu);
+                if (c + 1 < nchunks) ws.chunk_hist[(size_t)(c + 1) * d.E + e] = run;
+                run += (int)(kv[u] >> 16);
+            }
+        } else {
+            for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+                int v[kScanBatch];
 #pragma unroll
-            for (int u = 0; u < kScanBatch; ++u)
-                if (c0 + u < nchunks) {
-                    ws.chunk_hist[(size_t)(c0 + u) * d.E + e] = run;
-                    run += v[u];
-                }
+                for (int u = 0; u < kScanBatch; ++u) v[u] = ws.chunk_hist[(size_t)min(c0 + u, nchunks - 1) * d.E + e];
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u)
+                    if (c0 + u < nchunks) {
+                        ws.chunk_hist[(size_t)(c0 + u) * d.E + e] = run;
+                        run += v[u];
+                    }
+            }
         }
     }
     if (e == d.E - 1) {

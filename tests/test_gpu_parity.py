@@ -173,6 +173,26 @@ def test_caller_routing_entry(T):
     assert_workspaces_clean(L)
 
 
+@pytest.mark.parametrize("T", [10240, 17000])
+def test_large_permutation_against_stable_sort(T):
+    """The three-pass permutation of many slots (S = 81920: 128 chunks, whose
+    counts the scan keeps in registers; S = 136000: 133 chunks, the batched
+    scan) against numpy's stable argsort of the returned ids: bit-exact
+    counts, offsets and sorted slots (integer work, one correct answer)."""
+    shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=8, inter=128)
+    host = synth.make_layer(shape, seed=90 + T)
+    dev = synth.to_device(host)
+    L = MoeInt4Layer(dev, 8)
+    r = L.route(dev["x"])
+    torch.cuda.synchronize()
+    ids = r["ids"].cpu().numpy().reshape(-1)
+    counts = np.bincount(ids, minlength=16)
+    assert np.array_equal(r["counts"].cpu().numpy(), counts)
+    assert np.array_equal(r["offsets"].cpu().numpy(), np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(r["sorted_slots"].cpu().numpy(), np.argsort(ids, kind="stable"))
+    assert_workspaces_clean(L)
+
+
 @pytest.mark.parametrize("T,shared", [(600, False), (1111, False), (700, True)])
 def test_many_rows_per_expert(T, shared):
     """Over 128 rows per expert on average: every expert spans several
