@@ -73,7 +73,8 @@ struct GemmArgs {
     const float *weights;      // routing weights per slot
     const float *gate;         // shared-expert gate logits [T]
     uint16_t *h_out;           // fp16 activation out (gate/up modes)
-    uint16_t *y_out;           // fp16 weighted down-projection rows [T][k+1][H]
+    uint16_t *y_out;           // fp16 weighted down-projection rows [T][k+1][H], columns interleaved
+                               // (column n at 64 (n / 64) + 2 (n % 32) + (n % 64) / 32)
     int T, H, I, k;            // I: intermediate of this expert kind
     int K;                     // reduction length
     size_t b_words;            // words of packed weights per expert
@@ -478,9 +479,9 @@ __global__ __launch_bounds__(kGemmThreads, MAXMA <= 2 ? 3 : 2) void moe_gemm_ker
                 const int ip = (i & ~7) | pair_pos(i & 7);
                 g.h_out[(size_t)rowv[j] * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
             } else {
-                uint16_t *yr = g.y_out + (size_t)rowv[j] * g.H + kNT * nb + 64 * wave + col;
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) yr[32 * nt] = (uint16_t)f32_to_f16_sat(wv[j] * acc[mt][nt][j]);
+                // the lane's columns of both column tiles as one word (interleaved columns)
+                uint32_t *yr = reinterpret_cast<uint32_t *>(g.y_out + (size_t)rowv[j] * g.H + kNT * nb + 64 * wave) + col;
+                *yr = f32_to_f16_sat(wv[j] * acc[mt][0][j]) | (f32_to_f16_sat(wv[j] * acc[mt][1][j]) << 16);
             }
         }
     }
@@ -727,9 +728,11 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
                         g.h_out[(size_t)(pbase + m) * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
                     } else {
                         const float wv = s_wgt[m];
-                        uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * b + 64 * cg + col;
+                        // the lane's columns of both column tiles side by side (interleaved
+                        // columns; two 16-bit stores: a packed word costs this kernel spills)
+                        uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * b + 64 * cg + 2 * col;
                         yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
-                        yr[32] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
+                        yr[1] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
                     }
                 }
             }
@@ -889,41 +892,58 @@ static int big_blocks_per_wg(int nblocks, int groups_per_block, int chunks)
 }
 
 // out[t][n] = bf16( sum_j y[t][j][n] (+ y[t][k][n] for the shared expert) ),
-// fixed order; one thread per 8 outputs.  The slot rows are loaded four at a
-// time, all four in flight together (clamped, unconditional loads; a clamped
-// duplicate adds +0), instead of one load waited for per slot.
+// fixed order.  The down GEMMs store a lane's columns of its two 32-wide
+// column tiles as one word, so a y row holds column n at position
+// 64 (n / 64) + 2 (n % 32) + (n % 64) / 32: one thread takes 16 positions,
+// i.e. columns c .. c + 7 and c + 32 .. c + 39 of a 64-column group.  The
+// slot rows are loaded four at a time, all in flight together (clamped,
+// unconditional loads; a clamped duplicate adds +0), instead of one load
+// waited for per slot.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ y, int T, int H,
                                                       int k, int nslots, uint16_t *__restrict__ out)
 {
     const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-    const size_t n8 = (size_t)T * H / 8;
-    if (i >= n8) return;
-    const size_t t = i / (H / 8), c = i % (H / 8);
-    const uint4 *src = reinterpret_cast<const uint4 *>(y + t * (k + 1) * H) + c;
+    const size_t n16 = (size_t)T * H / 16;
+    if (i >= n16) return;
+    const size_t t = i / (H / 16), c = i % (H / 16);
+    const uint4 *src = reinterpret_cast<const uint4 *>(y + t * (k + 1) * H) + 2 * c;
     const size_t stride = H / 8;   // 16-byte pieces per slot row
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j0 = 0; j0 < nslots; j0 += 4) {
-        uint4 v[4];
+    float acc[16];                 // position p of the 16: column 8 (c % 4) + p / 2 of tile p % 2
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = src[(size_t)min(j0 + u, nslots - 1) * stride];
+    for (int p = 0; p < 16; ++p) acc[p] = 0.f;
+    for (int j0 = 0; j0 < nslots; j0 += 4) {
+        uint4 v[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) v[u][h] = src[(size_t)min(j0 + u, nslots - 1) * stride + h];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             // a duplicate adds +0 (a select, not a branch, so the loads stay
             // ahead of the first use)
             const bool dup = j0 + u >= nslots;
-            const uint32_t w[4] = {dup ? 0u : v[u].x, dup ? 0u : v[u].y, dup ? 0u : v[u].z, dup ? 0u : v[u].w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const h2_t hv = __builtin_bit_cast(h2_t, w[q]);
-                acc[2 * q] += (float)hv[0];
-                acc[2 * q + 1] += (float)hv[1];
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w[4] = {dup ? 0u : v[u][h].x, dup ? 0u : v[u][h].y, dup ? 0u : v[u][h].z,
+                                       dup ? 0u : v[u][h].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const h2_t hv = __builtin_bit_cast(h2_t, w[q]);
+                    acc[8 * h + 2 * q] += (float)hv[0];
+                    acc[8 * h + 2 * q + 1] += (float)hv[1];
+                }
             }
         }
     }
-    uint32_t o[4];
+    uint32_t o0[4], o1[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = f32_to_bf16(acc[2 * q]) | (f32_to_bf16(acc[2 * q + 1]) << 16);
-    reinterpret_cast<uint4 *>(out + t * H)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int r = 0; r < 4; ++r) {
+        o0[r] = f32_to_bf16(acc[4 * r]) | (f32_to_bf16(acc[4 * r + 2]) << 16);
+        o1[r] = f32_to_bf16(acc[4 * r + 1]) | (f32_to_bf16(acc[4 * r + 3]) << 16);
+    }
+    uint16_t *orow = out + t * H + 64 * (c / 4) + 8 * (c % 4);
+    *reinterpret_cast<uint4 *>(orow) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+    *reinterpret_cast<uint4 *>(orow + 32) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1113,8 +1133,8 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
         }
         if ((e = launch_gemm<kSharedW2>(gs2, (d.T + kMT - 1) / kMT, d.H / kNT, st)) != hipSuccess) return e;
     }
-    const size_t n8 = (size_t)d.T * d.H / 8;
-    combine_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(y, d.T, d.H, d.k,
+    const size_t n16 = (size_t)d.T * d.H / 16;
+    combine_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(y, d.T, d.H, d.k,
                                                                  d.k + (d.sh_I > 0 ? 1 : 0), a.out);
     return hipGetLastError();
 }
