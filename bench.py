@@ -313,12 +313,15 @@ def main():
         trf_key = dom
     else:
         achieved = w13_flops / (w13_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": "moe_gemm_kernel<kRoutedW13> (routed gate/up grouped GEMM, "
-                                           "fp16 MFMA, INT4 weight groups staged through LDS and "
-                                           "dequantised in registers) + tile list",
+        roof = {"bound": "mfma", "kernel": "moe_gemm_big_kernel<kRoutedW13> (whole-expert gate/up grouped "
+                                           "GEMM: one workgroup per chunk of up to 192 rows of one expert and "
+                                           "256 weight rows, fp16 MFMA 32x32x16 on INT4 weights dequantised "
+                                           "exactly in registers, SiLU-gate epilogue)",
                 "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "algorithmic_flops_per_launch": w13_flops, "launch_us": round(w13_us, 3)}
+                "algorithmic_flops_per_launch": w13_flops,
+                "algorithmic_bytes_per_launch": round(stage_bytes["gate_up"]),
+                "launch_us": round(w13_us, 3)}
         trf_key = "gate_up"
     trf = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
     if os.path.exists(trf):
