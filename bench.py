@@ -313,10 +313,14 @@ def main():
         trf_key = dom
     else:
         achieved = w13_flops / (w13_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": "moe_gemm_big_kernel<kRoutedW13> (whole-expert gate/up grouped "
-                                           "GEMM: one workgroup per chunk of up to 192 rows of one expert and "
-                                           "256 weight rows, fp16 MFMA 32x32x16 on INT4 weights dequantised "
-                                           "exactly in registers, SiLU-gate epilogue)",
+        # the whole-expert GEMM runs from 64 slots per expert on average at group 128
+        big = args.group == 128 and S >= 64 * E
+        kname = ("moe_gemm_big_kernel<kRoutedW13> (whole-expert gate/up grouped GEMM: one workgroup per "
+                 "chunk of up to 192 rows of one expert and 256 weight rows, fp16 MFMA 32x32x16 on INT4 "
+                 "weights dequantised exactly in registers, SiLU-gate epilogue)" if big else
+                 "moe_gemm_kernel<kRoutedW13> (gate/up grouped GEMM over 128- or 64-row tiles of sorted "
+                 "rows, fp16 MFMA 32x32x16, INT4 weight groups staged through LDS, SiLU-gate epilogue)")
+        roof = {"bound": "mfma", "kernel": kname,
                 "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": w13_flops,
