@@ -279,6 +279,11 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within each 8
 constexpr int kDppMirror = 0x140;      // lane 15 - i within each 16
 
+// Word 3 of a CDNA buffer resource for raw (stride 0) accesses, 32-bit data
+// format.  The hardware drops a store whose offset lies at or beyond the
+// resource's num_records bytes, which bounds a tile's stores without a branch.
+constexpr int kBufferWord3 = 0x00020000;
+
 // Sum over the 4 lanes of a quad.
 __device__ __forceinline__ float quad_sum(float v)
 {

@@ -715,25 +715,40 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
         };
         // outputs of weight block b from the accumulators
         auto store_block = [&](int b) __attribute__((always_inline)) {
+            if constexpr (kW13) {
+                // h rows of the chunk through a buffer resource that covers
+                // exactly its rows: the stores of rows past the chunk fall
+                // outside it and are dropped, so no row test and no 64-bit
+                // address per value; the lane's column is the same for all
+                const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+                    g.h_out + (size_t)pbase * g.I, (short)0, rows * g.I * 2, kBufferWord3);
+                const int i = 128 * b + 32 * cg + col;
+                const int lane_off = ((32 * t0 + 4 * half) * g.I + ((i & ~7) | pair_pos(i & 7))) * 2;
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int mrow = 32 * mt + 8 * (j >> 2) + (j & 3);   // the same for the wave
+                        const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_f16_sat(silu(gv) * uv), hrs,
+                                                              lane_off + mrow * g.I * 2, 0, 0);
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int mt = 0; mt < MA; ++mt) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int m = 32 * (t0 + mt) + 8 * (j >> 2) + 4 * half + (j & 3);
                     if (m >= rows) continue;
-                    if constexpr (kW13) {
-                        const float gv = acc[mt][0][j] * kScaleDown, uv = acc[mt][1][j] * kScaleDown;
-                        const int i = 128 * b + 32 * cg + col;
-                        const int ip = (i & ~7) | pair_pos(i & 7);
-                        g.h_out[(size_t)(pbase + m) * g.I + ip] = (uint16_t)f32_to_f16_sat(silu(gv) * uv);
-                    } else {
-                        const float wv = s_wgt[m];
-                        // the lane's columns of both column tiles side by side (interleaved
-                        // columns; two 16-bit stores: a packed word costs this kernel spills)
-                        uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * b + 64 * cg + 2 * col;
-                        yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
-                        yr[1] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
-                    }
+                    const float wv = s_wgt[m];
+                    // the lane's columns of both column tiles side by side (interleaved
+                    // columns; two 16-bit stores: a packed word costs this kernel spills;
+                    // a buffer resource over y, as for h above, measured slower here)
+                    uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + kNT * b + 64 * cg + 2 * col;
+                    yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
+                    yr[1] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
                 }
             }
         };
