@@ -889,6 +889,228 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Routed down projection with the activation rows resident in LDS.
+//
+// Its K (the intermediate size) is short, so half a chunk's h rows (at most
+// three 32-row tiles) fit in LDS for the whole K.  A workgroup loads them
+// once and its 8 waves (two per SIMD) then run independently, with no
+// barrier: wave w takes the 64-column output groups w, w + 8, ...; for each
+// it streams that group's 64 weight rows over K (INT4 codes and scales two
+// K stages ahead in registers, dequantised exactly to fp16 as in the other
+// GEMMs), accumulates 3 x 2 MFMA tiles and stores its weighted y values.
+// The two halves of a chunk are dispatched next to each other on one XCD,
+// so they read each weight from HBM once between them.  Against a kernel
+// that stages the rows per weight block this reads h from L2 once instead
+// of once per block, and no wave waits on another.
+// ---------------------------------------------------------------------------
+constexpr int kDnWaves = 8;
+constexpr int kDnThreads = kDnWaves * kWave;
+constexpr int kDnMaxTiles = 3;                 // row tiles of a workgroup (half of a kBigRows chunk)
+constexpr int kDnRows = 32 * kDnMaxTiles;
+constexpr int kDnMaxK = 768;                   // longest K held in LDS
+constexpr int kDnLdsRow = kDnMaxK + 8;         // padded row, fp16 elements
+static_assert(2 * kDnRows == kBigRows, "two halves per chunk");
+
+__global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmArgs g)
+{
+    __shared__ __align__(16) _Float16 s_h[kDnRows * kDnLdsRow];
+    __shared__ float s_wgt[kDnRows];   // routing weight x 2^-10 per row
+    __shared__ int s_yrow[kDnRows];    // row of y per row
+    __shared__ uint32_t s_yoff[kDnRows];   // its byte offset in y (2^31 past the rows; y under 2^31 bytes)
+
+    const int wid = blockIdx.x, xcd = wid & 7, r = wid >> 3;
+    const int chunk = (r >> 1) * 8 + xcd, part = r & 1;
+    const int4 tv = g.tiles[chunk];
+    if (tv.x < 0) return;   // empty slot
+    const int ctiles = (tv.z + 31) / 32;
+    const int tfirst = part == 0 ? 0 : (ctiles + 1) / 2;
+    const int ntiles = part == 0 ? (ctiles + 1) / 2 : ctiles / 2;
+    if (ntiles == 0) return;   // a one-tile chunk has no second half
+    const int e = tv.x & 0xFFFF;
+    const int pbase = tv.y + 32 * tfirst, rows = min(32 * ntiles, tv.z - 32 * tfirst);
+    const int K = g.K, ldsrow = K + 8, nst = K / kBigKS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+
+    // while y is under 2^31 bytes its stores go through one buffer resource
+    // over y, and a row past the workgroup's has offset 2^31, outside it, so
+    // the hardware drops those stores (no row test, no 64-bit addresses)
+    const long ybytes = (long)g.T * (g.k + 1) * g.H * 2;
+    const bool ybuf = ybytes < 0x80000000L;
+    if (tid < 32 * ntiles) {
+        s_yoff[tid] = 0x80000000u;
+        if (tid < rows) {
+            const int slot = g.sorted_slots[pbase + tid];
+            const int tok = slot / g.k;
+            const int yrow = tok * (g.k + 1) + (slot - tok * g.k);
+            s_wgt[tid] = g.weights[slot] * kScaleDown;
+            s_yrow[tid] = yrow;
+            if (ybuf) s_yoff[tid] = (uint32_t)yrow * (uint32_t)g.H * 2u;
+        }
+    }
+    // the rows' h (K fp16 each) -> LDS, 16-byte pieces, eight loads in flight per thread
+    {
+        const uint32_t pr = (uint32_t)K / 8, npieces = (uint32_t)rows * pr;
+        const uint32_t inv = (uint32_t)((0x100000000ull + pr - 1) / pr);   // exact p / pr for p < 2^16
+        const uint16_t *src = g.a16 + (size_t)pbase * K;
+        for (uint32_t p0 = 0; p0 < npieces; p0 += 8 * kDnThreads) {
+            u32x4_t v[8];
+            int dst[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t p = p0 + u * kDnThreads + tid, pc = p < npieces ? p : 0;
+                const uint32_t rr = __umulhi(pc, inv), c = pc - rr * pr;
+                v[u] = *reinterpret_cast<const u32x4_t *>(src + rr * (uint32_t)K + 8 * c);
+                dst[u] = p < npieces ? (int)(rr * (uint32_t)ldsrow + 8 * c) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (dst[u] >= 0) *reinterpret_cast<u32x4_t *>(s_h + dst[u]) = v[u];
+        }
+    }
+    __syncthreads();
+
+    const int ngroups = g.H / 64;   // 64-column output groups
+    const int npass = ngroups > wave ? (ngroups - wave + kDnWaves - 1) / kDnWaves : 0;
+    if (npass == 0) return;
+    const int nst_all = npass * nst;
+    const size_t bstride = (size_t)K / 8;   // words per weight row
+    const int32_t *bpe = g.bp + (size_t)e * g.b_words;
+    const uint16_t *bse = g.bs + (size_t)e * g.b_scales;
+
+    auto kloop = [&](auto ma_c) __attribute__((always_inline)) {
+        constexpr int MA = decltype(ma_c)::value;
+        f32x16_t acc[MA][2];
+        auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < MA; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        };
+        zero_acc();
+        u32x4_t rb[3][2][2];   // weight stages in flight: [set][nt][piece]
+        uint16_t rs[3][2];     // their bf16 scales
+        // global stage gs: pass gs / nst (output group wave + 8 pass), K stage gs % nst
+        auto load_b = [&](int gs, int set) __attribute__((always_inline)) {
+            const int ps = gs / nst, s = gs - ps * nst;
+            const int n0 = 64 * (wave + kDnWaves * ps) + col;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int n = n0 + 32 * nt;
+                const u32x4_t *q = reinterpret_cast<const u32x4_t *>(bpe + (size_t)n * bstride) + 4 * s + half;
+                rb[set][nt][0] = q[0];
+                rb[set][nt][1] = q[2];
+                rs[set][nt] = bse[(size_t)n * nst + s];
+            }
+        };
+        auto dequant_step = [&](int set, const h2_t (&s2)[2], int j, f16x8_t (&out)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) out[nt] = dequant_int4_f16(rb[set][nt][j >> 2][j & 3], s2[nt]);
+        };
+        auto store_pass = [&](int ps) __attribute__((always_inline)) {
+            const int n0 = 64 * (wave + kDnWaves * ps);
+            if (ybuf) {
+                const __amdgpu_buffer_rsrc_t yrs =
+                    __builtin_amdgcn_make_buffer_rsrc(g.y_out, (short)0, (int)ybytes, kBufferWord3);
+                const uint32_t lane_off = (uint32_t)(n0 + 2 * col) * 2u;
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int m = 32 * mt + 8 * (j >> 2) + 4 * half + (j & 3);
+                        const float wv = s_wgt[m];
+                        // the lane's columns of both tiles side by side: one word
+                        const uint32_t pk = f32_to_f16_sat(wv * acc[mt][0][j]) | f32_to_f16_sat(wv * acc[mt][1][j]) << 16;
+                        __builtin_amdgcn_raw_buffer_store_b32(pk, yrs, (int)(s_yoff[m] + lane_off), 0, 0);
+                    }
+                }
+                return;
+            }
+#pragma unroll
+            for (int mt = 0; mt < MA; ++mt) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int m = 32 * mt + 8 * (j >> 2) + 4 * half + (j & 3);
+                    if (m >= rows) continue;
+                    const float wv = s_wgt[m];
+                    // interleaved columns: the lane's columns of both tiles side by side
+                    uint16_t *yr = g.y_out + (size_t)s_yrow[m] * g.H + n0 + 2 * col;
+                    yr[0] = (uint16_t)f32_to_f16_sat(wv * acc[mt][0][j]);
+                    yr[1] = (uint16_t)f32_to_f16_sat(wv * acc[mt][1][j]);
+                }
+            }
+        };
+        f16x8_t bcur[2];
+        auto stage = [&](int gs, int set, int nset) __attribute__((always_inline)) {
+            load_b(min(gs + 2, nst_all - 1), (set + 2) % 3);
+            const int ps = gs / nst, s = gs - ps * nst;
+            const h2_t s2c[2] = {scale_pair(rs[set][0]), scale_pair(rs[set][1])};
+            // step j of lane half h reads K = 64 (j / 4) + 32 h + 8 (j % 4) of the stage
+            const _Float16 *A = s_h + col * ldsrow + kBigKS * s + 32 * half;
+            f16x8_t af[2][MA];
+#pragma unroll
+            for (int mt = 0; mt < MA; ++mt) af[0][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * ldsrow);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                f16x8_t bnext[2];
+                if (j < 7) {
+                    const int ko = 64 * ((j + 1) >> 2) + 8 * ((j + 1) & 3);
+#pragma unroll
+                    for (int mt = 0; mt < MA; ++mt)
+                        af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * ldsrow + ko);
+                    dequant_step(set, s2c, j + 1, bnext);
+                } else {
+                    const h2_t s2n[2] = {scale_pair(rs[nset][0]), scale_pair(rs[nset][1])};
+                    dequant_step(nset, s2n, 0, bnext);   // the next stage's first step
+                }
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt) {
+                    acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bcur[0], acc[mt][0], 0, 0, 0);
+                    acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mt], bcur[1], acc[mt][1], 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 2 * MA; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    if (j < 7 && i < MA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, (30 + 2 * MA - 1) / (2 * MA), 0);   // VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                bcur[0] = bnext[0];
+                bcur[1] = bnext[1];
+            }
+            if (s == nst - 1) {
+                store_pass(ps);
+                zero_acc();
+            }
+        };
+        load_b(0, 0);
+        load_b(min(1, nst_all - 1), 1);
+        {
+            const h2_t s20[2] = {scale_pair(rs[0][0]), scale_pair(rs[0][1])};
+            dequant_step(0, s20, 0, bcur);
+        }
+        int gs = 0;
+        for (; gs + 3 <= nst_all; gs += 3) {
+            stage(gs, 0, 1);
+            stage(gs + 1, 1, 2);
+            stage(gs + 2, 2, 0);
+        }
+        if (gs < nst_all) stage(gs, 0, 1);
+        if (gs + 1 < nst_all) stage(gs + 1, 1, 2);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    switch (ntiles) {
+    case 1: kloop(I1{}); break;
+    case 2: kloop(I2{}); break;
+    default: kloop(I3{}); break;
+    }
+}
+
 // Weight blocks per workgroup of the whole-expert GEMM: the most that divide
 // the block count, keep every block's scales in LDS (kBigMaxGroups) and leave
 // at least kBigMinWgs workgroups for the given chunk count, so the block loop
@@ -1072,6 +1294,11 @@ static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hi
     const int groups = (ntiles_max + 7) / 8;
     if constexpr (MODE == kRoutedW13 || MODE == kRoutedW2) {
         const unsigned grid = groups * 8 * nblocks;
+        if (MODE == kRoutedW2 && big && g.K <= kDnMaxK) {
+            // two workgroups per chunk slot, one per half of its row tiles
+            moe_down_resident_kernel<<<groups * 8 * 2, kDnThreads, 0, st>>>(g);
+            return hipGetLastError();
+        }
         if (big) {
             // chunks: about one per expert for balanced routing (the list has
             // room for at most S / kBigRows + E, about twice that)

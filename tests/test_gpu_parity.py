@@ -218,12 +218,15 @@ def test_shared_expert_whole_chunk_gemm_ragged():
     run_and_check(host, tokens=tokens, label="shared whole-chunk ragged T=6211")
 
 
-@pytest.mark.parametrize("H,I", [(256, 128), (768, 384)])
+@pytest.mark.parametrize("H,I", [(256, 128), (768, 384), (512, 768), (512, 896)])
 def test_whole_expert_gemm_row_counts(H, I):
     """Caller routing that gives the experts every row count the whole-expert
     grouped GEMM distinguishes: 0, 1 and 2 to 6 row tiles of 32 (ragged and
     full), exactly one chunk (192 rows) and counts that split into two or
-    three chunks; ids may repeat within a token.  Every token is checked."""
+    three chunks; ids may repeat within a token.  Every token is checked.
+    The down projection keeps half a chunk's h rows in LDS up to I = 768
+    (with fewer 64-column output groups than waves at H = 256, and an uneven
+    share at H = 768); I = 896 takes the block-loop kernel instead."""
     counts = [0, 1, 5, 31, 32, 33, 63, 64, 96, 150, 160, 191, 192, 193, 300, 385]
     k = 4
     S = sum(counts)
