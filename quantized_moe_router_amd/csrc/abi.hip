@@ -283,6 +283,41 @@ int32_t device_scratch(hipStream_t st, void **out)
     return MOE_INT4_OK;
 }
 
+// A second stream per device, with a fork and a join event, on which a
+// many-token forward runs its shared expert: that work needs only x and the
+// shared gate logits (both written by the top-k kernel), so it overlaps the
+// permutation (a few workgroups) and the routed GEMMs' tails instead of
+// following them.  Made on the first forward that can use it; a forward whose
+// stream is being captured before then, or that may not allocate, runs the
+// shared expert on its own stream.  The mutex keeps each forward's fork,
+// shared launches and join together when several host threads enqueue.
+struct SideStream {
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+const SideStream *side_stream(hipStream_t main)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream &s = g_side[dev];
+    if (s.st) return &s;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+        if (n.fork) (void)hipEventDestroy(n.fork);
+        (void)hipStreamDestroy(n.st);
+        return nullptr;
+    }
+    s = n;
+    return &s;
+}
+
 }  // namespace
 
 }  // namespace moe
@@ -385,7 +420,7 @@ static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
                            uint16_t *out, const moe_int4_shape *shape,
                            const moe_shared_int6 *shared, void *workspace,
                            size_t workspace_bytes, void *hip_stream, void *const *events,
-                           uint32_t *status = nullptr)
+                           uint32_t *status = nullptr, bool side = true)
 {
     g_error.clear();
     Dims d;
@@ -413,9 +448,25 @@ static int32_t forward_impl(const uint16_t *x, const uint16_t *router_w,
             return rc;
     } else {
         RouteOut ro{ws.ids, ws.weights, ws.counts, ws.offsets, ws.sorted_slots};
-        if ((rc = launched(launch_route(x, router_w, d, ws, ro, st, true, a.sh_gate), "route"))) return rc;
+        std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+        const SideStream *ss = nullptr;
+        if (side && d.sh_I > 0) {
+            lock.lock();
+            ss = side_stream(st);
+        }
+        if ((rc = launched(launch_route(x, router_w, d, ws, ro, st, true, a.sh_gate, ss ? ss->fork : nullptr),
+                           "route")))
+            return rc;
+        if (ss) {
+            // the shared expert on the side stream from the top-k kernel on
+            if ((rc = launched(hipStreamWaitEvent(ss->st, ss->fork, 0), "side stream wait"))) return rc;
+            if ((rc = launched(launch_shared_expert(a, d, ws, ss->st, true), "shared expert"))) return rc;
+            if ((rc = launched(hipEventRecord(ss->join, ss->st), "event"))) return rc;
+        }
         if (ev[1] && (rc = launched(hipEventRecord(ev[1], st), "event"))) return rc;
-        if ((rc = launched(launch_prefill_experts(a, d, ws, ro, st, ev[2], true), "experts"))) return rc;
+        if ((rc = launched(launch_prefill_experts(a, d, ws, ro, st, ev[2], true, ss ? ss->join : nullptr),
+                           "experts")))
+            return rc;
     }
     if (ev[3] && (rc = launched(hipEventRecord(ev[3], st), "event"))) return rc;
     return MOE_INT4_OK;
@@ -466,8 +517,9 @@ int32_t moe_int4_forward_noalloc(const uint16_t *x, const uint16_t *router_w,
     if ((rc = check_device())) return rc;
     void *ws = nullptr;
     if ((rc = device_scratch((hipStream_t)hip_stream, &ws))) return rc;
+    // everything on the caller's stream: no side stream is made here
     return forward_impl(x, router_w, w13_packed, w13_scales, w2_packed, w2_scales, top_k, out, shape,
-                        shared, ws, kScratchBytes, hip_stream, nullptr, status);
+                        shared, ws, kScratchBytes, hip_stream, nullptr, status, false);
 }
 
 int32_t moe_int4_quantize(const uint16_t *w, int32_t rows, int32_t cols, int32_t group,

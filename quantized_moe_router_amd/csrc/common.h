@@ -442,10 +442,11 @@ struct RouteOut {
 
 // convert_x (many-token routing only): the top-k kernel also writes x in the
 // gate/up GEMMs' fp16 pair order to ws.xh and, given gate_w, the shared
-// expert's gate logits to ws.shared_gate
+// expert's gate logits to ws.shared_gate.  ev_topk (may be null) is recorded
+// on st right after the top-k kernel, ahead of the permutation.
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                         const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x = false,
-                        const uint16_t *gate_w = nullptr);
+                        const uint16_t *gate_w = nullptr, hipEvent_t ev_topk = nullptr);
 hipError_t launch_permute(const Dims &d, const Workspace &ws, const RouteOut &ro,
                           hipStream_t st);
 
@@ -469,10 +470,17 @@ struct ExpertArgs {
 // shared expert when present.  `ev_mid` (may be null) is recorded between the
 // gate/up and down projections.
 // x_converted: ws.xh already holds x in fp16 pair order (from the routing),
-// and ws.shared_gate the shared expert's gate logits when it has one
+// and ws.shared_gate the shared expert's gate logits when it has one.
+// ev_shared: null, or the shared expert was enqueued on another stream by
+// launch_shared_expert and ev_shared recorded there after it; the combine
+// then waits on it instead of running the shared expert on st.
 hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
                                   const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid,
-                                  bool x_converted = false);
+                                  bool x_converted = false, hipEvent_t ev_shared = nullptr);
+// The shared expert of a many-token forward (gate logits unless x_converted,
+// gate/up -> ws.sh_h, down -> its y rows); it needs ws.xh in pair order.
+hipError_t launch_shared_expert(const ExpertArgs &a, const Dims &d, const Workspace &ws, hipStream_t st,
+                                bool x_converted);
 
 // bf16 octet (natural order) -> fp16 octet in pair order.
 __device__ __forceinline__ uint4 bf16_octet_to_f16_pairs(uint4 v)

@@ -1320,8 +1320,33 @@ static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hi
     return hipGetLastError();
 }
 
+hipError_t launch_shared_expert(const ExpertArgs &a, const Dims &d, const Workspace &ws, hipStream_t st,
+                                bool x_converted)
+{
+    // gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
+    hipError_t e;
+    if (!x_converted && (e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess) return e;
+    GemmArgs gs{};
+    gs.x = ws.xh; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
+    gs.T = d.T; gs.H = d.H; gs.I = d.sh_I; gs.k = d.k; gs.K = d.H;
+    GemmArgs gs2{};
+    gs2.a16 = ws.sh_h; gs2.bp = a.sh_w2p; gs2.bs = a.sh_w2s; gs2.gate = ws.shared_gate; gs2.y_out = ws.y;
+    gs2.T = d.T; gs2.H = d.H; gs2.I = d.sh_I; gs2.k = d.k; gs2.K = d.sh_I;
+    if (d.T >= kBigSharedMinTokens) {
+        // whole-chunk gate/up GEMM: 192 tokens per workgroup and weight block
+        const int groups = (d.T + 8 * kBigRows - 1) / (8 * kBigRows);
+        const int nb13 = d.sh_I / 128;
+        moe_gemm_big_kernel<kSharedW13><<<groups * 8 * nb13, big_waves(kSharedW13) * kWave, 0, st>>>(gs, nb13, 1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) {
+        return e;
+    }
+    return launch_gemm<kSharedW2>(gs2, (d.T + kMT - 1) / kMT, d.H / kNT, st);
+}
+
 hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Workspace &ws,
-                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid, bool x_converted)
+                                  const RouteOut &ro, hipStream_t st, hipEvent_t ev_mid, bool x_converted,
+                                  hipEvent_t ev_shared)
 {
     hipError_t e;
     const size_t xn8 = (size_t)d.T * d.H / 8;
@@ -1355,25 +1380,11 @@ hipError_t launch_prefill_experts(const ExpertArgs &a, const Dims &d, const Work
     g2.b_words = (size_t)d.H * d.I / 8; g2.b_scales = (size_t)d.H * (d.I >> (d.gsh + 5));
     if ((e = launch_gemm<kRoutedW2>(g2, tmax, d.H / kNT, st, d.gsh == 1, big)) != hipSuccess) return e;
     if (d.sh_I > 0) {
-        // shared expert: gate logits, gate/up -> sh_h, down -> y[t][k] = sigmoid(g) * ys
-        if (!x_converted && (e = launch_shared_gate(a.x, a.sh_gate, d, ws.shared_gate, st)) != hipSuccess)
-            return e;
-        GemmArgs gs{};
-        gs.x = ws.xh; gs.bp = a.sh_w13p; gs.bs = a.sh_w13s; gs.h_out = ws.sh_h;
-        gs.T = d.T; gs.H = d.H; gs.I = d.sh_I; gs.k = d.k; gs.K = d.H;
-        GemmArgs gs2{};
-        gs2.a16 = ws.sh_h; gs2.bp = a.sh_w2p; gs2.bs = a.sh_w2s; gs2.gate = ws.shared_gate; gs2.y_out = y;
-        gs2.T = d.T; gs2.H = d.H; gs2.I = d.sh_I; gs2.k = d.k; gs2.K = d.sh_I;
-        if (d.T >= kBigSharedMinTokens) {
-            // whole-chunk gate/up GEMM: 192 tokens per workgroup and weight block
-            const int groups = (d.T + 8 * kBigRows - 1) / (8 * kBigRows);
-            const int nb13 = d.sh_I / 128;
-            moe_gemm_big_kernel<kSharedW13><<<groups * 8 * nb13, big_waves(kSharedW13) * kWave, 0, st>>>(gs, nb13, 1);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        } else if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) {
+        if (ev_shared) {
+            if ((e = hipStreamWaitEvent(st, ev_shared, 0)) != hipSuccess) return e;
+        } else if ((e = launch_shared_expert(a, d, ws, st, x_converted)) != hipSuccess) {
             return e;
         }
-        if ((e = launch_gemm<kSharedW2>(gs2, (d.T + kMT - 1) / kMT, d.H / kNT, st)) != hipSuccess) return e;
     }
     const size_t n16 = (size_t)d.T * d.H / 16;
     combine_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(y, d.T, d.H, d.k,

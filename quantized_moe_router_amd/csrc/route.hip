@@ -304,7 +304,7 @@ hipError_t launch_router_mfma(const uint16_t *x, const uint16_t *router_w, const
 
 hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims &d,
                         const Workspace &ws, const RouteOut &ro, hipStream_t st, bool convert_x,
-                        const uint16_t *gate_w)
+                        const uint16_t *gate_w, hipEvent_t ev_topk)
 {
     if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
     hipError_t e = launch_router_mfma(x, router_w, d, ws.logits, st);
@@ -312,6 +312,7 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims 
     topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, router_ksplit(d), d, ro.ids, ro.weights, x,
                                                convert_x ? ws.xh : nullptr, convert_x ? gate_w : nullptr,
                                                ws.shared_gate);
+    if (ev_topk && (e = hipEventRecord(ev_topk, st)) != hipSuccess) return e;
     return launch_permute(d, ws, ro, st);
 }
 

@@ -424,15 +424,18 @@ def test_real_prefill8192_shared(real_weights):
     run_and_check(host, tokens=tokens, real_dev=dev, label="prefill 8192 + shared")
 
 
-@pytest.mark.parametrize("T", [1, 5, 40])
-def test_graph_replay_matches_eager(T):
+@pytest.mark.parametrize("T,shared", [(1, False), (5, False), (40, False), (40, True), (300, True)])
+def test_graph_replay_matches_eager(T, shared):
     """The forward captured in a HIP graph gives the eager result on every
     replay, with other eager work in between (no memset nodes; the
-    workspace counters return to zero after each call)."""
+    workspace counters return to zero after each call).  With the shared
+    expert, a many-token forward forks it onto a second stream and joins it
+    before the combine; the capture records that fork and join."""
     shape = synth.LayerShape(tokens=T, hidden=256, experts=16, top_k=2, inter=128)
-    a = synth.to_device(synth.make_layer(shape, seed=11))
-    b = synth.to_device(synth.make_layer(shape, seed=12))
-    La, Lb = MoeInt4Layer(a, 2), MoeInt4Layer(b, 2)
+    a = synth.to_device(synth.make_layer(shape, seed=11, shared=shared))
+    b = synth.to_device(synth.make_layer(shape, seed=12, shared=shared))
+    La = MoeInt4Layer(a, 2, shared=a.get("shared"))
+    Lb = MoeInt4Layer(b, 2, shared=b.get("shared"))
     eager = La.forward(a["x"]).clone()
     other = Lb.forward(b["x"]).clone()
     out = torch.empty_like(eager)
