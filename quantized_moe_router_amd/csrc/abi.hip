@@ -67,7 +67,8 @@ Layout layout(const Dims &d)
     L.chunk_hist = take(4 * nchunks * d.E);
     L.tiles = take(16 * routed_tile_slots(d));
     L.h = take(2 * S * d.I);
-    L.y = take(2 * T * ((size_t)d.k + 1) * d.H);
+    // y: fp16 rows per slot (many tokens), fp32 per slot and shared row (decode)
+    L.y = take((d.T <= kDecodeMaxTokens ? 4 : 2) * T * ((size_t)d.k + 1) * d.H);
     L.shared_gate = take(4 * T);
     L.sh_h = take(2 * T * (size_t)d.sh_I);
     L.xh = take(d.T > kDecodeMaxTokens ? 2 * T * (size_t)d.H : 0);

@@ -424,7 +424,7 @@ __global__ __launch_bounds__(256) void w13_slot_kernel(ExpertArgs a, Dims d, Wor
 }
 
 // ---------------------------------------------------------------------------
-// 3. down projection + combine.  Each workgroup owns kDnRows output rows and
+// 3a. down projection + combine for one token.  Each workgroup owns kDnRows output rows and
 //    every slot.  A lane group of 32 lanes takes one slot at a time (4 lanes
 //    per row; lane q reads chunks q + 4c of the row), 2 groups per wave, so a
 //    workgroup has 16 groups; group g takes the slots g, g + 16, ...  Each
@@ -581,6 +581,125 @@ __global__ __launch_bounds__(kDnWaves *kWave, (CPL <= 5 && SHCPL <= 5) ? 4 : 2) 
 }
 
 // ---------------------------------------------------------------------------
+// 3b. down projection per slot, then the combine (two or more tokens).  Grid (H / 64, S + T_sh):
+//    workgroup (x, s) computes rows [64 x, 64 x + 64) of slot s's expert (4
+//    waves of 16 rows, 4 lanes per row, lane q reading chunks q + 4c), times
+//    the slot's routing weight, into yp[s] (fp32); slot S + t holds the shared
+//    expert's rows of token t (INT6, weight sigmoid(gate)).  Each workgroup
+//    issues its weight loads at once, so the projection costs one round of
+//    memory latency however many slots a token group has; then
+//    w2_combine_kernel sums each token's k (+1) rows in slot order and rounds
+//    once to bf16 (a fixed order: deterministic).  h arrives in nibble-pair
+//    order; each 32-value chunk's sum (for the +8 code bias) is formed once,
+//    by the four threads that stage the chunk.
+// ---------------------------------------------------------------------------
+constexpr int kDsRows = 64;
+
+template <int CPL, int SHCPL>
+__global__ __launch_bounds__(256) void w2_slot_kernel(ExpertArgs a, Dims d, Workspace ws,
+                                                      const int32_t *__restrict__ ids,
+                                                      const float *__restrict__ wts, float *__restrict__ yp)
+{
+    __shared__ __align__(16) uint16_t s_h[1024];   // one slot's h (I <= 1024)
+    __shared__ float s_hs[32];                      // its chunk sums
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int rl = lane >> 2, q = lane & 3;
+    const int row = blockIdx.x * kDsRows + wave * 16 + rl;
+    const int s = blockIdx.y;
+    if (s < d.S) {
+        // the expert id as a vector load, used only after the activation load
+        // is issued (a scalar load would hold the activation load back)
+        const uint32_t e_raw = load_coherent(reinterpret_cast<const uint32_t *>(ids) + s);
+        const float wt = wts[s];
+        const int nck = d.I / 32, words = d.I / 8, nsc = d.I >> (d.gsh + 5), n16 = d.I / 8;
+        const uint4 hv = reinterpret_cast<const uint4 *>(ws.h + (size_t)s * d.I)[min(tid, n16 - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = clamp_expert(__builtin_amdgcn_readfirstlane((int)e_raw), d.E);
+        const size_t r = (size_t)e * d.H + row;
+        const uint4 *wrow = reinterpret_cast<const uint4 *>(a.w2p + r * words);
+        uint4 w[CPL];
+        float sc[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int kc = q + 4 * c, ok = kc < nck, kcl = ok ? kc : 0;
+            w[c] = load_stream(wrow + kcl);
+            const float sv = bf16_to_f32(a.w2s[r * nsc + (kcl >> d.gsh)]);
+            sc[c] = ok ? sv : 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // every weight load issued before the wait for h
+        // threads 4c .. 4c + 3 hold chunk c: its sum over the quad
+        float hsum = dot2h(hv.x, 0x3C003C00u, 0.f);
+        hsum = dot2h(hv.y, 0x3C003C00u, hsum);
+        hsum = dot2h(hv.z, 0x3C003C00u, hsum);
+        hsum = dot2h(hv.w, 0x3C003C00u, hsum);
+        hsum = quad_sum(hsum);
+        if (tid < n16) {
+            reinterpret_cast<uint4 *>(s_h)[tid] = hv;
+            if ((tid & 3) == 0) s_hs[tid >> 2] = hsum;
+        }
+        __syncthreads();
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int kc = q + 4 * c, kcl = kc < nck ? kc : 0;
+            const uint4 *hp = reinterpret_cast<const uint4 *>(s_h + kcl * 32);
+            uint32_t hw[16];
+#pragma unroll
+            for (int o = 0; o < 4; ++o) {
+                const uint4 v = hp[o];
+                hw[4 * o] = v.x; hw[4 * o + 1] = v.y; hw[4 * o + 2] = v.z; hw[4 * o + 3] = v.w;
+            }
+            acc = fmaf(sc[c], chunk_dot_h(w[c], hw) - 136.f * s_hs[kcl], acc);
+        }
+        acc = quad_sum(acc);
+        if (q == 0) yp[(size_t)s * d.H + row] = wt * acc;
+    } else if constexpr (SHCPL > 0) {
+        // the shared expert's rows for token t (INT6 in groups of 64, h in natural order)
+        const int t = s - d.S;
+        const int snck = d.sh_I / 32, swords = d.sh_I / 32 * 6, snsc = d.sh_I / kShGroup;
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < SHCPL; ++c) {
+            const int kc = q + 4 * c, ok = kc < snck, kcl = ok ? kc : 0;
+            uint32_t wv[7];
+            load_block6(a.sh_w2p + (size_t)row * swords + kcl * 6, wv);
+            const float sv = bf16_to_f32(a.sh_w2s[(size_t)row * snsc + kcl / 2]);
+            uint32_t hw[16];
+            const float hs = load_act_natural<true>(ws.sh_h + (size_t)t * d.sh_I + kcl * 32, hw);
+            acc = fmaf(ok ? sv : 0.f, chunk_dot6<true>(wv, hw) - 160.f * hs, acc);
+        }
+        acc = quad_sum(acc);
+        const float g = 1.f / (1.f + expf(-ws.shared_gate[t]));
+        if (q == 0) yp[(size_t)s * d.H + row] = g * acc;
+    }
+}
+
+// out[t][n] = bf16(sum_j yp[t k + j][n] (+ yp[S + t][n])), j ascending, the
+// shared row last; four columns per thread.
+__global__ __launch_bounds__(256) void w2_combine_kernel(const float *__restrict__ yp, Dims d,
+                                                         uint16_t *__restrict__ out)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int n4 = d.H / 4;
+    if (i >= d.T * n4) return;
+    const int t = i / n4, c = i - t * n4;
+    const float4 *col = reinterpret_cast<const float4 *>(yp) + c;
+    float4 acc = col[(size_t)t * d.k * n4];
+    for (int j = 1; j < d.k; ++j) {
+        const float4 v = col[(size_t)(t * d.k + j) * n4];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (d.sh_I > 0) {
+        const float4 v = col[(size_t)(d.S + t) * n4];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    uint2 o;
+    o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+    o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+    reinterpret_cast<uint2 *>(out + (size_t)t * d.H)[c] = o;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static int cpl_of(int chunks, int lanes) { return (chunks + lanes - 1) / lanes; }
@@ -649,6 +768,39 @@ static hipError_t launch_w2_rows(const ExpertArgs &a, const Dims &d, const Works
     return hipErrorInvalidValue;
 }
 
+static hipError_t launch_w2_slots(const ExpertArgs &a, const Dims &d, const Workspace &ws,
+                                  const int32_t *ids, const float *wts, hipStream_t st)
+{
+    float *yp = reinterpret_cast<float *>(ws.y);
+    dim3 grid(d.H / kDsRows, d.S + (d.sh_I > 0 ? d.T : 0));
+    const int cpl = cpl_of(d.I / 32, 4);
+    const int shcpl = d.sh_I ? cpl_of(d.sh_I / 32, 4) : 0;
+    bool launched = false;
+#define MOE_CASE(N, M) \
+    if (cpl == N && shcpl == M) { w2_slot_kernel<N, M><<<grid, 256, 0, st>>>(a, d, ws, ids, wts, yp); launched = true; }
+#define MOE_ROW(N) MOE_CASE(N, 0) MOE_CASE(N, 1) MOE_CASE(N, 2) MOE_CASE(N, 3) MOE_CASE(N, 4) MOE_CASE(N, 5) MOE_CASE(N, 6) MOE_CASE(N, 7) MOE_CASE(N, 8)
+    MOE_ROW(1) MOE_ROW(2) MOE_ROW(3) MOE_ROW(4) MOE_ROW(5) MOE_ROW(6) MOE_ROW(7) MOE_ROW(8)
+#undef MOE_ROW
+#undef MOE_CASE
+    if (!launched) return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n4 = d.T * d.H / 4;
+    w2_combine_kernel<<<(n4 + 255) / 256, 256, 0, st>>>(yp, d, a.out);
+    return hipGetLastError();
+}
+
+// One token: the row kernel (the whole down projection and combine in one
+// launch, its 10 slots in one round of its 16 lane groups).  More tokens: the
+// per-slot kernel and the combine (measured per layer, same box: 2 tokens
+// 28.7 -> 28.3 us, 4 tokens 40.4 -> 37.1, 8 tokens 66.2 -> 55.7, 16 tokens
+// 122.0 -> 95.9; 1 token 20.1 against 21.9 us).
+static hipError_t launch_w2(const ExpertArgs &a, const Dims &d, const Workspace &ws, const int32_t *ids,
+                            const float *wts, hipStream_t st)
+{
+    return d.T == 1 ? launch_w2_rows(a, d, ws, ids, wts, st) : launch_w2_slots(a, d, ws, ids, wts, st);
+}
+
 hipError_t launch_decode_forward(const uint16_t *x, const uint16_t *router_w, const ExpertArgs &a,
                                  const Dims &d, const Workspace &ws, hipEvent_t ev_route,
                                  hipEvent_t ev_mid, hipStream_t st)
@@ -659,7 +811,7 @@ hipError_t launch_decode_forward(const uint16_t *x, const uint16_t *router_w, co
     if (ev_route && (e = hipEventRecord(ev_route, st)) != hipSuccess) return e;
     if ((e = launch_w13_slots(a, d, ws, ws.ids, st)) != hipSuccess) return e;
     if (ev_mid && (e = hipEventRecord(ev_mid, st)) != hipSuccess) return e;
-    return launch_w2_rows(a, d, ws, ws.ids, ws.weights, st);
+    return launch_w2(a, d, ws, ws.ids, ws.weights, st);
 }
 
 hipError_t launch_decode_experts(const ExpertArgs &a, const int32_t *ids, const float *wts,
@@ -671,7 +823,7 @@ hipError_t launch_decode_experts(const ExpertArgs &a, const int32_t *ids, const 
     e = launch_router(RouterArgs{a.x, nullptr, a.sh_gate, 0, d, ws, none, kTailNone}, st);
     if (e != hipSuccess) return e;
     if ((e = launch_w13_slots(a, d, ws, ids, st)) != hipSuccess) return e;
-    return launch_w2_rows(a, d, ws, ids, wts, st);
+    return launch_w2(a, d, ws, ids, wts, st);
 }
 
 }  // namespace moe
