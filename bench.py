@@ -301,7 +301,9 @@ def main():
     decode = T <= 16
     kernels = {"route": "router_kernel (router GEMV; top-k in one extra routing workgroup)",
                "gate_up": "w13_slot_kernel (INT4 gate/up dequant GEMV + SiLU-gate)",
-               "down_combine": "w2_rows_kernel (INT4 down dequant GEMV + weighted combine)"}
+               "down_combine": ("w2_rows_kernel (INT4 down dequant GEMV + weighted combine)" if T == 1 else
+                                "w2_slot_kernel + w2_combine_kernel (INT4 down dequant GEMV per slot, then the "
+                                "weighted combine)")}
     if decode:
         dom = max(stage_us, key=stage_us.get)
         achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
