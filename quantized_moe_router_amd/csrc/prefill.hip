@@ -1190,7 +1190,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 // ---------------------------------------------------------------------------
 constexpr int kRT_N = 128;
 
-__global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(kRouterThreads, 4) void router_mfma_kernel(const uint16_t *__restrict__ x,
                                                                    const uint16_t *__restrict__ rw,
                                                                    int T, int H, int E,
                                                                    float *__restrict__ logits)
@@ -1207,37 +1207,44 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint1
     // thread: rows br and br + 64)
     const int ar = tid >> 2, apart = tid & 3;
     const int br = tid >> 3, bpart = tid & 7;
-    const bool aok = m0 + ar < T, bok0 = e0 + br < E, bok1 = e0 + br + 64 < E;
-    uint4 ra[2], rb[2];
-    auto load_stage = [&](int s) {
-        const int k0 = s * kKS;
-        if (aok) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(m0 + ar) * H + k0 + 16 * apart);
-            ra[0] = src[0];
-            ra[1] = src[1];
-        } else {
-            ra[0] = ra[1] = make_uint4(0, 0, 0, 0);
-        }
-        rb[0] = bok0 ? reinterpret_cast<const uint4 *>(rw + (size_t)(e0 + br) * H + k0)[bpart] : make_uint4(0, 0, 0, 0);
-        rb[1] = bok1 ? reinterpret_cast<const uint4 *>(rw + (size_t)(e0 + br + 64) * H + k0)[bpart] : make_uint4(0, 0, 0, 0);
+    // rows past T or E load the last valid row (their sums are not stored), so
+    // every load is unconditional and the compiler counts them exactly
+    const uint16_t *arow = x + (size_t)min(m0 + ar, T - 1) * H + 16 * apart;
+    const uint16_t *brow0 = rw + (size_t)min(e0 + br, E - 1) * H + 8 * bpart;
+    const uint16_t *brow1 = rw + (size_t)min(e0 + br + 64, E - 1) * H + 8 * bpart;
+    // kRtDepth stages in flight in registers: a stage's MFMAs (8 per wave)
+    // take far less than a memory round trip
+    constexpr int kRtDepth = 3;
+    u32x4_t ra[kRtDepth][2], rb[kRtDepth][2];
+    auto load_stage = [&](int s, int slot) __attribute__((always_inline)) {
+        const int k0 = (s0 + min(s, nsteps - 1)) * kKS;   // past the last stage: reload it (unused)
+        ra[slot][0] = *reinterpret_cast<const u32x4_t *>(arow + k0);
+        ra[slot][1] = *reinterpret_cast<const u32x4_t *>(arow + k0 + 8);
+        rb[slot][0] = *reinterpret_cast<const u32x4_t *>(brow0 + k0);
+        rb[slot][1] = *reinterpret_cast<const u32x4_t *>(brow1 + k0);
     };
-    auto store_stage = [&](int buf) {
-        *reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 16 * apart) = ra[0];
-        *reinterpret_cast<uint4 *>(s_a[buf] + ar * kLdsRow + 16 * apart + 8) = ra[1];
-        *reinterpret_cast<uint4 *>(s_b[buf] + br * kLdsRow + 8 * bpart) = rb[0];
-        *reinterpret_cast<uint4 *>(s_b[buf] + (br + 64) * kLdsRow + 8 * bpart) = rb[1];
+    auto store_stage = [&](int slot, int buf) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4_t *>(s_a[buf] + ar * kLdsRow + 16 * apart) = ra[slot][0];
+        *reinterpret_cast<u32x4_t *>(s_a[buf] + ar * kLdsRow + 16 * apart + 8) = ra[slot][1];
+        *reinterpret_cast<u32x4_t *>(s_b[buf] + br * kLdsRow + 8 * bpart) = rb[slot][0];
+        *reinterpret_cast<u32x4_t *>(s_b[buf] + (br + 64) * kLdsRow + 8 * bpart) = rb[slot][1];
     };
     f32x16_t acc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
-    load_stage(s0);
-    store_stage(0);
+    // stage j lives in register slot j % kRtDepth until it is stored to LDS
+    // buffer j & 1 (at the end of step j - 1), which frees the slot for stage
+    // j + kRtDepth
+#pragma unroll
+    for (int j = 0; j < kRtDepth; ++j) load_stage(j, j);
+    store_stage(0, 0);
+    load_stage(kRtDepth, 0);
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
+    auto step = [&](int s, auto slot_c) __attribute__((always_inline)) {
+        constexpr int nslot = (decltype(slot_c)::value + 1) % kRtDepth;   // slot of stage s + 1
         const int buf = s & 1;
-        if (s + 1 < nsteps) load_stage(s0 + s + 1);
 #pragma unroll
         for (int ks = 0; ks < kKS / 16; ++ks) {
             const int kk = 16 * ks + 8 * (lane >> 5);
@@ -1250,9 +1257,22 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(const uint1
             for (int mt = 0; mt < 2; ++mt)
                 acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr, acc[mt], 0, 0, 0);
         }
-        if (s + 1 < nsteps) store_stage(buf ^ 1);
+        store_stage(nslot, buf ^ 1);   // stage s + 1 (past the end: a reload nobody reads)
+        load_stage(s + 1 + kRtDepth, nslot);
         __syncthreads();
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    static_assert(kRtDepth == 3, "the step loop below rotates three slots");
+    int s = 0;
+    for (; s + 3 <= nsteps; s += 3) {
+        step(s, C0{});
+        step(s + 1, C1{});
+        step(s + 2, C2{});
     }
+    if (s < nsteps) step(s, C0{});
+    if (s + 1 < nsteps) step(s + 1, C1{});
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
