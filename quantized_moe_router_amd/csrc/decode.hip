@@ -684,14 +684,21 @@ __global__ __launch_bounds__(256) void w2_combine_kernel(const float *__restrict
     if (i >= d.T * n4) return;
     const int t = i / n4, c = i - t * n4;
     const float4 *col = reinterpret_cast<const float4 *>(yp) + c;
-    float4 acc = col[(size_t)t * d.k * n4];
-    for (int j = 1; j < d.k; ++j) {
-        const float4 v = col[(size_t)(t * d.k + j) * n4];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    if (d.sh_I > 0) {
-        const float4 v = col[(size_t)(d.S + t) * n4];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    // rows of slots t k .. t k + k - 1, then the shared row: eight loads in
+    // flight at a time (clamped, unconditional; a clamped duplicate is not
+    // added), summed in slot order
+    const int nrows = d.k + (d.sh_I > 0 ? 1 : 0);
+    auto row_of = [&](int j) { return j < d.k ? (size_t)(t * d.k + j) : (size_t)(d.S + t); };
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < nrows; j0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = col[row_of(min(j0 + u, nrows - 1)) * n4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < nrows) {
+                acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+            }
     }
     uint2 o;
     o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);

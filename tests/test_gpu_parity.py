@@ -453,6 +453,43 @@ def test_graph_replay_matches_eager(T, shared):
         torch.cuda.synchronize()
 
 
+def test_shared_expert_side_stream_from_two_threads():
+    """Many-token forwards with the shared expert fork it onto one side stream
+    per device.  Two host threads enqueue forwards of two layers (own
+    workspaces) on two torch streams at once, several times each: every
+    result equals that layer's result computed alone."""
+    import threading
+    shape = synth.LayerShape(tokens=300, hidden=256, experts=16, top_k=2, inter=128)
+    devs = [synth.to_device(synth.make_layer(shape, seed=70 + i, shared=True)) for i in range(2)]
+    layers = [MoeInt4Layer(d, 2, shared=d.get("shared")) for d in devs]
+    want = [layers[i].forward(devs[i]["x"]).clone() for i in range(2)]
+    torch.cuda.synchronize()
+    got = [[], []]
+    errors = []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(6):
+                    got[i].append(layers[i].forward(devs[i]["x"]).clone())
+            st.synchronize()
+        except Exception as exc:   # reported below, in the test's thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert len(got[i]) == 6
+        for r in got[i]:
+            assert torch.equal(r, want[i])
+
+
 # ---- INT4 group 64 on the same kernels ("Running 125B MoE on Three 3090s -
 # vLLM Edition", section 2: the group-64 alternative to group 128) ----
 
