@@ -509,6 +509,20 @@ def test_group64_real_width(T, shared):
     run_and_check(host, tokens=toks, label=f"group64 real-width T={T}")
 
 
+def test_y_past_2gib_sampled():
+    """16384 tokens at top-32 over 64 experts (hidden 2048, intermediate 128):
+    524,288 slots, so y (T x 33 rows x 2048 fp16) is 2.2 GB, past the 2^31
+    bytes the resident down GEMM addresses through a buffer resource; it
+    stores through 64-bit addresses instead.  The permutation runs its
+    batched scan (more than 128 chunks).  Routing is checked for every token,
+    outputs for sampled ones."""
+    shape = synth.LayerShape(tokens=16384, hidden=2048, experts=64, top_k=32, inter=128)
+    host = synth.make_layer(shape, seed=91)
+    rng = np.random.default_rng(91)
+    tokens = np.unique(np.concatenate([[0, 1, 8191, 16383], rng.choice(16384, 24, replace=False)]))
+    run_and_check(host, tokens=tokens, label="y past 2 GiB, T=16384 k=32")
+
+
 def test_large_permutation_many_experts():
     # 700 tokens x top-32 over 1000 experts: 22400 slots, past the
     # one-workgroup permutation (16384), so the three-pass path runs with
