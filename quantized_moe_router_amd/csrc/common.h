@@ -513,6 +513,7 @@ struct Int8Plan {
     bool gemv;
     bool rowsplit;       // GEMV with one row per workgroup (narrow matrices)
     bool mfma;           // matrix-core GEMV (5..16 tokens, wide matrices)
+    bool short_k;        // GEMM whose whole K range is loaded at once (K <= 320)
     int mtiles, ntiles, ksplit, kslice;
     size_t pstride;      // floats per split in the partials (T * N rounded up to 4)
     size_t part_bytes;   // fp32 split-K partials (workspace)

@@ -498,6 +498,10 @@ constexpr int kGmN = 128;           // weight rows per tile (4 waves x 32)
 constexpr int kGmKS = 64;           // K per stage
 constexpr int kGmLds = kGmKS + 8;   // padded LDS row (fp16 elements)
 constexpr int kGmThreads = 256;
+constexpr int kGmCs = kGmN + 8;     // padded LDS row of the epilogue (fp32 words)
+constexpr int kGmScGroups = 64;     // scale groups of the tile's rows staged in LDS at a time
+constexpr int kGmScRegs = 8;        // of those, per thread, loaded with the prologue's loads
+constexpr int kSumThreads = 64;     // split-K sum: four outputs per thread
 
 struct Int8GemmArgs {
     const uint16_t *x;        // bf16 [T][K]
@@ -519,6 +523,7 @@ struct Int8GemmArgs {
 template <int GS>
 __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g)
 {
+    constexpr int D = 2;   // register sets of loads in flight
     __shared__ __align__(16) _Float16 s_a[2][kGmM * kGmLds];
 
     // ---- tile (XCD-aware: each XCD takes a contiguous range of tiles, the
@@ -545,16 +550,30 @@ __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g
         const int row = r8 + 32 * o;
         asrc[o] = g.x + (size_t)(m0 + (row < rows ? row : 0)) * g.K + k0 + 8 * c8;
     }
-    u32x4_t ra[2][4];
+    u32x4_t ra[D][4];
 
     // ---- weights: lane -> row n0 + 32 wave + lane % 32 (clamped to N - 1),
     // bytes [32 half, +32) of each stage ----
     const int n = n0 + 32 * wave + (lane & 31);
     const int nrow = min(n, g.N - 1);
     const u32x4_t *bsrc = reinterpret_cast<const u32x4_t *>(g.wq + (size_t)nrow * (g.K / 4) + k0 / 4) + 2 * half;
-    const uint16_t *ssrc = g.ws + (size_t)nrow * (g.K >> g.gshift) + (k0 >> g.gshift);
-    u32x4_t rb[2][2];
-    uint16_t rs[2];
+    u32x4_t rb[D][2];
+
+    // ---- scales: the tile's rows x up to kGmScGroups groups in LDS, [group]
+    // [row], so that no scale value is carried in registers from one stage
+    // to the next (a loop-carried load result ends up copied at the loop's
+    // back edge, which waits for every load in flight) ----
+    __shared__ uint16_t s_sc[kGmScGroups * kGmN];
+    const int ngroups = len >> g.gshift;
+    const uint16_t *sbase = g.ws + (k0 >> g.gshift);
+    const size_t spitch = (size_t)(g.K >> g.gshift);
+    auto scale_src = [&](int i, int g0) {   // element i = row + kGmN * group of the chunk at g0
+        return sbase + (size_t)min(n0 + (i & (kGmN - 1)), g.N - 1) * spitch + g0 + i / kGmN;
+    };
+    auto load_scales_sync = [&](int g0) {
+        const int cnt = min(kGmScGroups, ngroups - g0) * kGmN;
+        for (int i = tid; i < cnt; i += kGmThreads) s_sc[i] = *scale_src(i, g0);
+    };
 
     f32x16_t acc[4], tmp[4];
 #pragma unroll
@@ -577,20 +596,26 @@ __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g
         auto load_b = [&](int s, int p) {
             rb[p][0] = bsrc[4 * s];
             rb[p][1] = bsrc[4 * s + 1];
-            rs[p] = ssrc[(s * kGmKS) >> g.gshift];
         };
 
-        // stage s (register set q = s % 2, LDS buffer q): stage s+1's
-        // activations are stored, stages s+3 (activations) and s+2
+        // stage s (register set q = s % D, LDS buffer s % 2): stage s+1's
+        // activations are stored, stages s+1+D (activations) and s+D
         // (weights) are loaded
-        auto stage = [&](int s, int q) {
-            if (s + 1 < nsteps) store_a(q ^ 1, q ^ 1);
+        auto stage = [&](int s, auto qc) {
+            constexpr int q = decltype(qc)::value, q1 = (q + 1) % D;
+            const int grp = (s * kGmKS) >> g.gshift;   // scale group within the K range
+            if (s > 0 && (s * kGmKS) % (kGmScGroups << g.gshift) == 0) {
+                // the next chunk of scales (every wave is past the previous
+                // stage's barrier, so none still reads the old chunk)
+                load_scales_sync(grp);
+                __syncthreads();
+            }
+            if (s + 1 < nsteps) store_a((q + 1) & 1, q1);
             const u32x4_t w0 = rb[q][0], w1 = rb[q][1];
-            const float sf = bf16_to_f32(rs[q]);
-            load_a(min(s + 3, nsteps - 1), q ^ 1);
-            load_b(min(s + 2, nsteps - 1), q);
+            load_a(min(s + 1 + D, nsteps - 1), q1);
+            load_b(min(s + D, nsteps - 1), q);
             const bool gfirst = (q % GS) == 0, glast = (q % GS) == GS - 1;
-            const _Float16 *A = s_a[q] + (lane & 31) * kGmLds + 32 * half;
+            const _Float16 *A = s_a[q & 1] + (lane & 31) * kGmLds + 32 * half;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t wa = j < 2 ? w0[2 * j] : w1[2 * j - 4];
@@ -610,6 +635,7 @@ __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g
                 }
             }
             if (glast) {
+                const float sf = bf16_to_f32(s_sc[(grp % kGmScGroups) * kGmN + 32 * wave + (lane & 31)]);
 #pragma unroll
                 for (int mt = 0; mt < MA; ++mt)
 #pragma unroll
@@ -618,21 +644,40 @@ __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g
             __syncthreads();
         };
 
-        // prologue: stage 0's activations in LDS, stages 1 and 2 in
-        // registers, weights of stages 0 and 1 in flight
+        // prologue: stage 0's activations in LDS, stages 1 .. D in
+        // registers, weights of stages 0 .. D-1 in flight, the first chunk of
+        // scales in LDS (its first kGmScRegs * kGmThreads values loaded
+        // alongside, the rest, if any, after)
+        const int sc0 = min(kGmScGroups, ngroups) * kGmN;
+        uint32_t sv[kGmScRegs];
         load_a(0, 0);
         load_b(0, 0);
-        load_b(min(1, nsteps - 1), 1);
-        load_a(min(1, nsteps - 1), 1);
+#pragma unroll
+        for (int u = 0; u < kGmScRegs; ++u) {
+            const int i = tid + kGmThreads * u;
+            sv[u] = i < sc0 ? *scale_src(i, 0) : 0u;
+        }
+#pragma unroll
+        for (int j = 1; j < D; ++j) load_b(min(j, nsteps - 1), j);
+#pragma unroll
+        for (int j = 1; j < D; ++j) load_a(min(j, nsteps - 1), j);
         store_a(0, 0);
-        load_a(min(2, nsteps - 1), 0);
+        load_a(min(D, nsteps - 1), 0);
+#pragma unroll
+        for (int u = 0; u < kGmScRegs; ++u) {
+            const int i = tid + kGmThreads * u;
+            if (i < sc0) s_sc[i] = (uint16_t)sv[u];
+        }
+        for (int i = tid + kGmThreads * kGmScRegs; i < sc0; i += kGmThreads) s_sc[i] = *scale_src(i, 0);
         __syncthreads();
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
         int s = 0;
         for (; s + 1 < nsteps; s += 2) {
-            stage(s, 0);
-            stage(s + 1, 1);
+            stage(s, I0{});
+            stage(s + 1, I1{});
         }
-        if (s < nsteps) stage(s, 0);
+        if (s < nsteps) stage(s, I0{});
     };
     switch (mtiles) {
     case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -641,39 +686,243 @@ __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g
     default: kloop(std::integral_constant<int, 4>{}); break;
     }
 
-    // ---- epilogue: lane holds column n for 16 rows of each row tile ----
-    if (n >= g.N) return;
+    // ---- epilogue: the accumulators pass through LDS, 64 tokens at a time
+    // in fp32 (rows padded to kGmCs words, so the two half-waves' rows fall
+    // in different banks); then each thread writes four consecutive outputs
+    // of one token: a 16-byte partial store or an 8-byte bf16 store, whole
+    // rows of the tile coalesced ----
+    float *s_c = reinterpret_cast<float *>(&s_a[0][0]);
+    static_assert(64 * kGmCs * sizeof(float) <= sizeof(s_a), "64 fp32 token rows fit the activation buffers");
+    const bool vec = (g.N & 3) == 0;   // every 4-column group starts 8-byte aligned (bf16) / 16-byte (fp32)
+    float *part = g.part + (size_t)split * g.pstride;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        if (mt >= mtiles) continue;
+    for (int hp = 0; hp < 2; ++hp) {
+        if (64 * hp >= rows) break;   // uniform over the workgroup
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int m = 32 * mt + 8 * (j >> 2) + 4 * half + (j & 3);
-            if (m >= rows) continue;
-            const size_t o = (size_t)(m0 + m) * g.N + n;
-            if (g.ksplit == 1) g.out[o] = (uint16_t)f32_to_bf16(acc[mt][j]);
-            else g.part[(size_t)split * g.pstride + o] = acc[mt][j];
+        for (int u = 0; u < 2; ++u) {
+            if (2 * hp + u >= mtiles) continue;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                s_c[(32 * u + 8 * (j >> 2) + 4 * half + (j & 3)) * kGmCs + 32 * wave + (lane & 31)] =
+                    acc[2 * hp + u][j];
         }
+        __syncthreads();
+        for (int it = tid; it < 64 * (kGmN / 4); it += kGmThreads) {
+            const int r = it / (kGmN / 4), c4 = 4 * (it % (kGmN / 4));
+            const int m = 64 * hp + r, nn = n0 + c4;
+            if (m >= rows || nn >= g.N) continue;
+            const float4 v = *reinterpret_cast<const float4 *>(s_c + r * kGmCs + c4);
+            const size_t o = (size_t)(m0 + m) * g.N + nn;
+            if (vec) {
+                if (g.ksplit == 1)
+                    *reinterpret_cast<uint2 *>(g.out + o) =
+                        make_uint2(f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16));
+                else
+                    *reinterpret_cast<float4 *>(part + o) = v;
+            } else {
+                const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (nn + e >= g.N) break;
+                    if (g.ksplit == 1) g.out[o + e] = (uint16_t)f32_to_bf16(e4[e]);
+                    else part[o + e] = e4[e];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
-// out[i] = bf16( sum_s part[s][i] ), splits in order; 4 outputs per thread
-// (pstride is a multiple of 4, so every 16-byte load is aligned).
-__global__ __launch_bounds__(256) void int8_splitk_sum_kernel(const float *__restrict__ part, size_t count,
-                                                              size_t pstride, int ksplit,
-                                                              uint16_t *__restrict__ out)
+// ---------------------------------------------------------------------------
+// GEMM over a short K range (NS <= kGoMaxSteps stages of 64 inputs): every
+// load of the tile is issued at the start (weights into registers, the
+// activation tile into registers and then, as fp16, into LDS), so a
+// workgroup waits for memory once instead of once per stage, and the stage
+// loop is unrolled with no value carried from one iteration to the next.
+// Tile: 128 tokens x 256 weight rows, wave w all tokens x rows [32 w, +32),
+// the same MFMA step layout and per-group fold as int8_gemm_kernel.
+// ---------------------------------------------------------------------------
+constexpr int kGoWaves = 8;
+constexpr int kGoThreads = kGoWaves * 64;
+constexpr int kGoN = 32 * kGoWaves;    // weight rows per tile
+constexpr int kGoMaxSteps = 5;         // K <= 320
+constexpr int kGoCs = kGoN + 8;        // padded epilogue row (fp32 words)
+
+template <int NS>
+constexpr size_t go_lds_bytes()
+{
+    const size_t x = (size_t)kGmM * (NS * kGmKS + 8) * 2, c = (size_t)64 * kGoCs * 4;
+    return x > c ? x : c;
+}
+
+template <int NS, int GS>
+__global__ __launch_bounds__(kGoThreads, 1) void int8_gemm_short_kernel(Int8GemmArgs g)
+{
+    constexpr int LR = NS * kGmKS + 8;    // padded activation row (fp16)
+    constexpr int CH = NS * 8;            // 16-byte chunks per activation row
+    constexpr int XPER = (kGmM * CH + kGoThreads - 1) / kGoThreads;
+    constexpr int NG = NS / GS;           // scale groups
+    constexpr int SPER = (NG * kGoN + kGoThreads - 1) / kGoThreads;
+    static_assert(NS % GS == 0, "whole groups");
+    __shared__ __align__(16) unsigned char s_raw[go_lds_bytes<NS>()];
+    __shared__ uint16_t s_sc[NG * kGoN];   // [group][row]
+    _Float16 *s_x = reinterpret_cast<_Float16 *>(s_raw);
+
+    // ---- tile (XCD-aware as in int8_gemm_kernel) ----
+    const int per = gridDim.x >> 3;
+    const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (tile >= g.mtiles * g.ntiles) return;
+    const int nt_i = tile % g.ntiles, mt_i = tile / g.ntiles;
+    const int m0 = mt_i * kGmM, n0 = nt_i * kGoN;
+    const int rows = min(kGmM, g.T - m0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+
+    // ---- every load at once: weights (lane -> row n0 + 32 wave + lane % 32,
+    // clamped to N - 1; bytes [32 half, +32) of each stage), the activation
+    // chunks (rows past T read row 0 of the tile, never stored), the scales ----
+    const int n = n0 + 32 * wave + (lane & 31);
+    const u32x4_t *bsrc = reinterpret_cast<const u32x4_t *>(g.wq + (size_t)min(n, g.N - 1) * (g.K / 4)) + 2 * half;
+    u32x4_t rb[NS][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        rb[s][0] = bsrc[4 * s];
+        rb[s][1] = bsrc[4 * s + 1];
+    }
+    u32x4_t rx[XPER];
+#pragma unroll
+    for (int u = 0; u < XPER; ++u) {
+        const int c = min(tid + kGoThreads * u, kGmM * CH - 1), r = c / CH, col = c % CH;
+        rx[u] = *reinterpret_cast<const u32x4_t *>(g.x + (size_t)(m0 + (r < rows ? r : 0)) * g.K + 8 * col);
+    }
+    const int gpr = g.K >> g.gshift;   // groups per weight row
+    uint32_t rsc[SPER];
+#pragma unroll
+    for (int u = 0; u < SPER; ++u) {
+        const int i = min(tid + kGoThreads * u, NG * kGoN - 1);
+        rsc[u] = g.ws[(size_t)min(n0 + i % kGoN, g.N - 1) * gpr + i / kGoN];
+    }
+#pragma unroll
+    for (int u = 0; u < XPER; ++u) {
+        const int c = tid + kGoThreads * u;
+        if (c < kGmM * CH)
+            *reinterpret_cast<u32x4_t *>(s_x + (c / CH) * LR + 8 * (c % CH)) = bf16x8_to_f16x8(rx[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < SPER; ++u) {
+        const int i = tid + kGoThreads * u;
+        if (i < NG * kGoN) s_sc[i] = (uint16_t)rsc[u];
+    }
+    __syncthreads();
+
+    f32x16_t acc[4], tmp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+    const int mtiles = (rows + 31) / 32;
+
+    auto compute = [&](auto ma_c) {
+        constexpr int MA = decltype(ma_c)::value;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const bool gfirst = s % GS == 0, glast = s % GS == GS - 1;
+            const u32x4_t w0 = rb[s][0], w1 = rb[s][1];
+            const _Float16 *A = s_x + (lane & 31) * LR + kGmKS * s + 32 * half;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t wa = j < 2 ? w0[2 * j] : w1[2 * j - 4];
+                const uint32_t wb = j < 2 ? w0[2 * j + 1] : w1[2 * j - 3];
+                const h2_t p0 = code_pair<0>(wa), p1 = code_pair<1>(wa);
+                const h2_t p2 = code_pair<0>(wb), p3 = code_pair<1>(wb);
+                const f16x8_t bf = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt) {
+                    const f16x8_t af = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * LR + 8 * j);
+                    if (gfirst && j == 0) {
+                        const f32x16_t z = {};
+                        tmp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, z, 0, 0, 0);
+                    } else {
+                        tmp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, tmp[mt], 0, 0, 0);
+                    }
+                }
+            }
+            if (glast) {
+                const float sf = bf16_to_f32(s_sc[(s / GS) * kGoN + 32 * wave + (lane & 31)]);
+#pragma unroll
+                for (int mt = 0; mt < MA; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mt][v] = fmaf(sf, tmp[mt][v], acc[mt][v]);
+            }
+        }
+    };
+    switch (mtiles) {
+    case 1: compute(std::integral_constant<int, 1>{}); break;
+    case 2: compute(std::integral_constant<int, 2>{}); break;
+    case 3: compute(std::integral_constant<int, 3>{}); break;
+    default: compute(std::integral_constant<int, 4>{}); break;
+    }
+
+    // ---- epilogue through LDS, 64 tokens at a time (as in int8_gemm_kernel) ----
+    __syncthreads();   // every wave is done reading the activations
+    float *s_c = reinterpret_cast<float *>(s_raw);
+    const bool vec = (g.N & 3) == 0;
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+        if (64 * hp >= rows) break;   // uniform over the workgroup
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (2 * hp + u >= mtiles) continue;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                s_c[(32 * u + 8 * (j >> 2) + 4 * half + (j & 3)) * kGoCs + 32 * wave + (lane & 31)] =
+                    acc[2 * hp + u][j];
+        }
+        __syncthreads();
+        for (int it = tid; it < 64 * (kGoN / 4); it += kGoThreads) {
+            const int r = it / (kGoN / 4), c4 = 4 * (it % (kGoN / 4));
+            const int m = 64 * hp + r, nn = n0 + c4;
+            if (m >= rows || nn >= g.N) continue;
+            const float4 v = *reinterpret_cast<const float4 *>(s_c + r * kGoCs + c4);
+            const size_t o = (size_t)(m0 + m) * g.N + nn;
+            if (vec) {
+                *reinterpret_cast<uint2 *>(g.out + o) =
+                    make_uint2(f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16));
+            } else {
+                const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (nn + e >= g.N) break;
+                    g.out[o + e] = (uint16_t)f32_to_bf16(e4[e]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// out[i] = bf16( sum_s part[s][i] ), splits in order; 4 outputs per thread,
+// every split's load issued before the first add (pstride is a multiple of
+// 4, so every 16-byte load is aligned).
+__global__ __launch_bounds__(kSumThreads) void int8_splitk_sum_kernel(const float *__restrict__ part, size_t count,
+                                                                      size_t pstride, int ksplit,
+                                                                      uint16_t *__restrict__ out)
 {
     const size_t i = (blockIdx.x * (size_t)blockDim.x + threadIdx.x) * 4;
     if (i >= count) return;
     if (i + 4 <= count) {
-        float4 a = *reinterpret_cast<const float4 *>(part + i);
-        for (int s = 1; s < ksplit; ++s) {
-            const float4 b = *reinterpret_cast<const float4 *>(part + (size_t)s * pstride + i);
-            a.x += b.x;
-            a.y += b.y;
-            a.z += b.z;
-            a.w += b.w;
-        }
+        float4 v[kInt8MaxSplitK];
+#pragma unroll
+        for (int s = 0; s < kInt8MaxSplitK; ++s)
+            if (s < ksplit) v[s] = *reinterpret_cast<const float4 *>(part + (size_t)s * pstride + i);
+        float4 a = v[0];
+#pragma unroll
+        for (int s = 1; s < kInt8MaxSplitK; ++s)
+            if (s < ksplit) {
+                a.x += v[s].x;
+                a.y += v[s].y;
+                a.z += v[s].z;
+                a.w += v[s].w;
+            }
         const uint32_t lo = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
         const uint32_t hi = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
         if ((reinterpret_cast<uintptr_t>(out + i) & 7) == 0) {
@@ -712,6 +961,15 @@ Int8Plan int8_plan(int T, int N, int K, int G)
     }
     if (p.gemv || T == 0) return p;
     p.mtiles = (T + kGmM - 1) / kGmM;
+    if (K <= kGoMaxSteps * kGmKS) {   // the whole K range at once, no split
+        p.short_k = true;
+        p.ntiles = (N + kGoN - 1) / kGoN;
+        p.ksplit = 1;
+        p.kslice = K;
+        p.pstride = ((size_t)T * N + 3) / 4 * 4;
+        p.part_bytes = 0;
+        return p;
+    }
     p.ntiles = (N + kGmN - 1) / kGmN;
     const int unit = G > kGmKS ? G : kGmKS;   // a K split is whole groups and whole stages
     const int units = K / unit;
@@ -786,13 +1044,29 @@ hipError_t launch_int8_linear(const uint16_t *x, const int32_t *wq, const uint16
     a.pstride = p.pstride;
     const long tiles = (long)p.mtiles * p.ntiles * p.ksplit;
     const int grid = (int)((tiles + 7) / 8 * 8);
+    if (p.short_k) {
+        const int ns = K / kGmKS;
+        if (G == 64) {
+            switch (ns) {
+            case 1: int8_gemm_short_kernel<1, 1><<<grid, kGoThreads, 0, st>>>(a); break;
+            case 2: int8_gemm_short_kernel<2, 1><<<grid, kGoThreads, 0, st>>>(a); break;
+            case 3: int8_gemm_short_kernel<3, 1><<<grid, kGoThreads, 0, st>>>(a); break;
+            case 4: int8_gemm_short_kernel<4, 1><<<grid, kGoThreads, 0, st>>>(a); break;
+            default: int8_gemm_short_kernel<5, 1><<<grid, kGoThreads, 0, st>>>(a); break;
+            }
+        } else {
+            if (ns == 2) int8_gemm_short_kernel<2, 2><<<grid, kGoThreads, 0, st>>>(a);
+            else int8_gemm_short_kernel<4, 2><<<grid, kGoThreads, 0, st>>>(a);
+        }
+        return hipGetLastError();
+    }
     if (G == 64) int8_gemm_kernel<1><<<grid, kGmThreads, 0, st>>>(a);
     else int8_gemm_kernel<2><<<grid, kGmThreads, 0, st>>>(a);
     if (p.ksplit > 1) {
         const size_t count = (size_t)T * N;
         const size_t threads = (count + 3) / 4;
-        int8_splitk_sum_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a.part, count, p.pstride,
-                                                                                 p.ksplit, out);
+        int8_splitk_sum_kernel<<<(unsigned)((threads + kSumThreads - 1) / kSumThreads), kSumThreads, 0, st>>>(
+            a.part, count, p.pstride, p.ksplit, out);
     }
     return hipGetLastError();
 }

@@ -94,9 +94,14 @@ SMALL = [
     (1, 5, 65536, 64),     # GEMM: one token past every GEMV's LDS limit
     (33, 129, 1024, 128),  # GEMM: ragged row and weight-row tiles
     (130, 333, 1024, 64),
-    (300, 256, 256, 128),
+    (300, 256, 256, 128),  # short-K GEMM (K <= 320 loaded at once): 4 stages, group 128
     (64, 1000, 2560, 128),
     (200, 96, 4096, 64),   # GEMM: narrow, split K
+    (17, 9, 64, 64),       # short-K GEMM: one stage, one ragged token tile, 9 rows
+    (129, 130, 128, 128),  # short-K GEMM: one group of 128, ragged tokens, N not a multiple of 4
+    (200, 333, 192, 64),   # short-K GEMM: three stages, ragged row tile
+    (77, 1000, 320, 64),   # short-K GEMM: the hyper-connection up row length
+    (260, 513, 256, 64),   # short-K GEMM: three token tiles, N = 2 x 256 + 1
 ]
 
 
