@@ -756,10 +756,23 @@ def cpu_baseline(layer, xs, T, k, budget_s, synth):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
+    # the same calls on one thread, for a quarter of the budget (at least one call)
+    n1, t1 = 0, time.perf_counter()
+    while True:
+        n = min(T, 8)
+        host["x"] = synth.to_host(xs[i % len(xs)][:n])
+        oracle.forward(host, nthreads=1)
+        n1 += n
+        i += 1
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    el1 = time.perf_counter() - t1
     return {"value": round(n_tok / el, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"{n_tok} whole tokens (the first min(T, 8) of each of the benchmark's T={T} "
-                      f"activation sets; routing, experts, combine), layer 0 weights, {el:.1f} s"}
+                      f"activation sets; routing, experts, combine), layer 0 weights, {el:.1f} s",
+            "one_thread": {"value": round(n1 / el1, 3), "unit": "tokens/s", "cores": 1,
+                           "sample": f"{n1} whole tokens the same way, {el1:.1f} s"}}
 
 
 if __name__ == "__main__":

@@ -300,9 +300,9 @@ void oracle_experts(const uint16_t *x, const int32_t *ids,
     int64_t w13_words = 2 * I * (H / 8), w13_nsc = 2 * I * (H / group);
     int64_t w2_words = H * (I / 8), w2_nsc = H * (I / group);
 #ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#pragma omp parallel
+    /* a clause, not omp_set_num_threads: the thread count applies to this
+     * call only and later calls keep the OpenMP default */
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
 #endif
     {
         double *act = (double *)malloc((size_t)I * sizeof(double));
@@ -340,9 +340,9 @@ void oracle_shared_int6(const uint16_t *x, const uint16_t *gate_w,
                         int nthreads)
 {
 #ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#pragma omp parallel
+    /* a clause, not omp_set_num_threads: the thread count applies to this
+     * call only and later calls keep the OpenMP default */
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
 #endif
     {
         double *act = (double *)malloc((size_t)I * sizeof(double));
