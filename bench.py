@@ -135,7 +135,7 @@ def kernel_source_hash() -> str:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer would shard by experts across GPUs, which is not implemented here.",
               file=sys.stderr)
         sys.exit(2)
