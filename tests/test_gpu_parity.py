@@ -529,3 +529,34 @@ def test_large_permutation_many_experts():
     # nearly the largest expert count
     shape = synth.LayerShape(tokens=700, hidden=256, experts=1000, top_k=32, inter=128)
     run_and_check(synth.make_layer(shape, seed=4242), label="large permutation, E=1000, k=32")
+
+
+# ---- seeded sweep over random legal shapes ----
+def _sweep_cases(n=32, seed=2026):
+    """Shapes drawn uniformly from what the boundary accepts (hidden a
+    multiple of 256 up to 4096, intermediate a multiple of 128 up to 1024,
+    1-1024 experts, top-k up to 32, group 64 or 128, with or without the
+    shared expert), tokens log-uniform in [1, 700]; draws whose host weights
+    or oracle work would be large are skipped, so the sweep stays a few
+    seconds per case."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        H = 256 * int(rng.integers(1, 17))
+        I = 128 * int(rng.integers(1, 9))
+        E = int(rng.integers(1, 1025))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(np.exp(rng.uniform(0.0, np.log(700.0))))
+        shared = bool(rng.integers(0, 2))
+        group = int(rng.choice([64, 128]))
+        if E * I * H > 1.3e8 or T * k * H * I * 3 > 3e9:
+            continue
+        out.append((T, H, I, E, k, shared, group))
+    return out
+
+
+@pytest.mark.parametrize("T,H,I,E,k,shared,group", _sweep_cases())
+def test_random_shape_sweep(T, H, I, E, k, shared, group):
+    shape = synth.LayerShape(tokens=T, hidden=H, experts=E, top_k=k, inter=I, group=group)
+    host = synth.make_layer(shape, seed=7000 + T + E, shared=shared)
+    run_and_check(host, label=f"sweep T={T} H={H} I={I} E={E} k={k} shared={shared} group={group}")
