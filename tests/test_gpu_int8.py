@@ -20,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+from parity import bf16_half_ulp
 from quantized_moe_router_amd import _binding as B
 from quantized_moe_router_amd import synth
 
@@ -65,7 +66,10 @@ def compare(g: np.ndarray, o: np.ndarray, label: str):
     bad = np.argwhere(err > bound)
     assert bad.size == 0, (f"{label}: {len(bad)} outputs off, first {bad[:3].tolist()} "
                            f"gpu {g[tuple(bad[0])]} oracle {o[tuple(bad[0])]}")
-    assert err.max() <= 2e-2 * rms, label
+    # the output is bf16: its own rounding of the exact value (half an ulp at
+    # the oracle's value) is not counted against the fp32 accumulation
+    beyond = np.maximum(err - bf16_half_ulp(o), 0.0)
+    assert beyond.max() <= 2e-2 * rms, (label, float(beyond.max()), rms)
     assert err.sum() <= 5e-3 * np.abs(o).sum(), label
 
 
@@ -242,3 +246,32 @@ def test_int8_maximum_sizes(T, N, K, G):
     compare(g, o, label)
     del p, s, x, out
     torch.cuda.empty_cache()
+
+
+def _sweep_cases(n=24, seed=77):
+    """Random legal shapes over every plan: tokens log-uniform in [1, 600],
+    rows log-uniform in [1, 20000], group 64 or 128, K a multiple of the
+    group up to 4096 (a third of the draws at most 320, the load-at-once
+    GEMM); draws whose oracle work would be large are skipped."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(np.exp(rng.uniform(0.0, np.log(600.0))))
+        N = int(np.exp(rng.uniform(0.0, np.log(20000.0))))
+        G = int(rng.choice([64, 128]))
+        kmax = 320 if rng.uniform() < 1 / 3 else 4096
+        K = G * int(rng.integers(1, kmax // G + 1))
+        if T * N * K > 3e9:
+            continue
+        out.append((T, N, K, G))
+    return out
+
+
+@pytest.mark.parametrize("T,N,K,G", _sweep_cases())
+def test_int8_random_shape_sweep(T, N, K, G):
+    label = f"int8 sweep T={T} N={N} K={K} G={G}"
+    say(label)
+    layer = synth.make_int8_linear(T, N, K, G, seed=T * 7919 + N * 31 + K)
+    g = as_f64(run(*to_dev(layer), T, N, K, G))
+    o = oracle.int8_linear(layer["x"], layer["packed"], layer["scales"], G)
+    compare(g, o, label)
