@@ -30,11 +30,15 @@ namespace moe {
 // The logits arrive as nsplit partial sums over H ([split][T][E]), added here
 // in split order.
 // With xh given, the wave also writes its token's x row to xh in the gate/up
-// GEMMs' fp16 pair order: the row's loads are issued before the selection
-// and stored after it, so the conversion rides on the selection's latency
-// instead of taking a kernel of its own.  With gate_w given as well, it also
-// forms the shared expert's gate logit x . gate_w from the same registers
-// (bf16 products, fp32 sums in the order of the stand-alone gate kernel).
+// GEMMs' fp16 pair order: the row's loads are issued with the logits' loads,
+// so the conversion rides on their latency instead of taking a kernel of its
+// own, and the row is stored before the selection, which then runs without
+// the row's registers.  With gate_w given as well, it also forms the shared
+// expert's gate logit x . gate_w from the same registers (bf16 products, fp32
+// sums in the order of the stand-alone gate kernel).  KPL = ceil(E / 64) and
+// NB (the logit splits loaded per pass) are template arguments, so a launch
+// holds the registers of its own variant only.
+template <int KPL, int NB>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int nsplit, Dims d,
                                                    int32_t *ids, float *weights,
                                                    const uint16_t *__restrict__ x, uint16_t *__restrict__ xh,
@@ -47,39 +51,68 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (t >= d.T) return;
     constexpr int kXo = kMaxHidden / 8 / kWave;   // octets of a row per lane
     const int n8 = d.H / 8;
-    uint4 xo[kXo];
+    const bool gate = xh && gate_w;
+    uint4 xo[kXo], gv[kXo];
     if (xh) {
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d.H);
 #pragma unroll
         for (int j = 0; j < kXo; ++j) xo[j] = src[min(lane + kWave * j, n8 - 1)];
+        if (gate) {
+#pragma unroll
+            for (int j = 0; j < kXo; ++j) gv[j] = reinterpret_cast<const uint4 *>(gate_w)[min(lane + kWave * j, n8 - 1)];
+        }
     }
-    const TopkLane r = topk_any(logits + (size_t)t * d.E, nsplit, (size_t)d.T * d.E, d.E, d.k, lane,
-                                s_topk[wave]);
-    if (lane < d.k) {
-        ids[(size_t)t * d.k + lane] = r.id;
-        weights[(size_t)t * d.k + lane] = r.w;
-    }
+    uint32_t val[KPL];
+    logit_keys<KPL, NB>(logits + (size_t)t * d.E, nsplit, (size_t)d.T * d.E, d.E, lane, val);
     if (xh) {
         uint4 *dst = reinterpret_cast<uint4 *>(xh + (size_t)t * d.H);
 #pragma unroll
         for (int j = 0; j < kXo; ++j)
             if (lane + kWave * j < n8) dst[lane + kWave * j] = bf16_octet_to_f16_pairs(xo[j]);
-        if (gate_w) {
+        if (gate) {
             float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < kXo; ++j) {
                 if (lane + kWave * j < n8) {
-                    const uint4 gv = reinterpret_cast<const uint4 *>(gate_w)[lane + kWave * j];
-                    acc = dot2(gv.x, xo[j].x, acc);
-                    acc = dot2(gv.y, xo[j].y, acc);
-                    acc = dot2(gv.z, xo[j].z, acc);
-                    acc = dot2(gv.w, xo[j].w, acc);
+                    acc = dot2(gv[j].x, xo[j].x, acc);
+                    acc = dot2(gv[j].y, xo[j].y, acc);
+                    acc = dot2(gv[j].z, xo[j].z, acc);
+                    acc = dot2(gv[j].w, xo[j].w, acc);
                 }
             }
             acc = wave_sum(acc);
             if (lane == 0) gate_out[t] = acc;
         }
     }
+    const TopkLane r = wave_topk_keys<KPL>(val, d.k, lane, s_topk[wave]);
+    if (lane < d.k) {
+        ids[(size_t)t * d.k + lane] = r.id;
+        weights[(size_t)t * d.k + lane] = r.w;
+    }
+}
+
+template <int KPL>
+static void launch_topk_kpl(const float *logits, int nsplit, const Dims &d, int32_t *ids, float *weights,
+                            const uint16_t *x, uint16_t *xh, const uint16_t *gate_w, float *gate_out,
+                            hipStream_t st)
+{
+    const unsigned grid = (unsigned)((d.T + 3) / 4);
+    if (nsplit <= 1)
+        topk_kernel<KPL, 1><<<grid, 256, 0, st>>>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out);
+    else if (nsplit == 2)
+        topk_kernel<KPL, 2><<<grid, 256, 0, st>>>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out);
+    else
+        topk_kernel<KPL, 4><<<grid, 256, 0, st>>>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out);
+}
+
+static void launch_topk(const float *logits, int nsplit, const Dims &d, int32_t *ids, float *weights,
+                        const uint16_t *x, uint16_t *xh, const uint16_t *gate_w, float *gate_out, hipStream_t st)
+{
+    if (d.E <= 64) launch_topk_kpl<1>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out, st);
+    else if (d.E <= 128) launch_topk_kpl<2>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out, st);
+    else if (d.E <= 256) launch_topk_kpl<4>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out, st);
+    else if (d.E <= 512) launch_topk_kpl<8>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out, st);
+    else launch_topk_kpl<16>(logits, nsplit, d, ids, weights, x, xh, gate_w, gate_out, st);
 }
 
 // Small permutation (one wave): used when routing is given by the caller.
@@ -309,9 +342,9 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *router_w, const Dims 
     if (d.T <= kDecodeMaxTokens) return launch_decode_route(x, router_w, d, ws, ro, st);
     hipError_t e = launch_router_mfma(x, router_w, d, ws.logits, st);
     if (e != hipSuccess) return e;
-    topk_kernel<<<(d.T + 3) / 4, 256, 0, st>>>(ws.logits, router_ksplit(d), d, ro.ids, ro.weights, x,
-                                               convert_x ? ws.xh : nullptr, convert_x ? gate_w : nullptr,
-                                               ws.shared_gate);
+    launch_topk(ws.logits, router_ksplit(d), d, ro.ids, ro.weights, x, convert_x ? ws.xh : nullptr,
+                convert_x ? gate_w : nullptr, ws.shared_gate, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_topk && (e = hipEventRecord(ev_topk, st)) != hipSuccess) return e;
     return launch_permute(d, ws, ro, st);
 }

@@ -177,44 +177,34 @@ __device__ TopkLane wave_topk_keys(const uint32_t (&val)[KPL], int k_in, int lan
     return out;
 }
 
-// Top-k of one token's E fp32 logits, given as nsplit partial rows (lrow,
-// lrow + split_stride, ...) that are added in split order; KPL = ceil(E / 64).
-template <int KPL>
-__device__ TopkLane wave_topk(const float *lrow, int nsplit, size_t split_stride, int E, int k, int lane,
-                              uint32_t *lds)
+// One token's E fp32 logits, given as nsplit partial rows (lrow, lrow +
+// split_stride, ...) added in split order, as order-preserving keys: val[i] =
+// key of expert lane + 64 i (0 where the expert does not exist); KPL =
+// ceil(E / 64).  NB splits' loads are in flight per pass (clamped addresses,
+// no branch around a load); NB matches the split count up to 4, so no
+// register holds a repeated load.
+template <int KPL, int NB>
+__device__ __forceinline__ void logit_keys(const float *lrow, int nsplit, size_t split_stride, int E, int lane,
+                                           uint32_t (&val)[KPL])
 {
-    // four splits' loads in flight per pass (clamped addresses, no branch
-    // around a load), added in split order
     float l[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) l[i] = 0.f;
-    for (int z0 = 0; z0 < nsplit; z0 += 4) {
-        float v[KPL][4];
+    for (int z0 = 0; z0 < nsplit; z0 += NB) {
+        float v[KPL][NB];
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
             const int e = lane + kWave * i, ec = e < E ? e : 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[i][u] = lrow[(size_t)min(z0 + u, nsplit - 1) * split_stride + ec];
+            for (int u = 0; u < NB; ++u) v[i][u] = lrow[(size_t)min(z0 + u, nsplit - 1) * split_stride + ec];
         }
 #pragma unroll
         for (int i = 0; i < KPL; ++i)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) l[i] += z0 + u < nsplit ? v[i][u] : 0.f;
+            for (int u = 0; u < NB; ++u) l[i] += z0 + u < nsplit ? v[i][u] : 0.f;
     }
-    uint32_t val[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) val[i] = lane + kWave * i < E ? float_order(l[i]) : 0u;
-    return wave_topk_keys<KPL>(val, k, lane, lds);
-}
-
-__device__ __forceinline__ TopkLane topk_any(const float *lrow, int nsplit, size_t split_stride, int E,
-                                             int k, int lane, uint32_t *lds)
-{
-    if (E <= 64) return wave_topk<1>(lrow, nsplit, split_stride, E, k, lane, lds);
-    if (E <= 128) return wave_topk<2>(lrow, nsplit, split_stride, E, k, lane, lds);
-    if (E <= 256) return wave_topk<4>(lrow, nsplit, split_stride, E, k, lane, lds);
-    if (E <= 512) return wave_topk<8>(lrow, nsplit, split_stride, E, k, lane, lds);
-    return wave_topk<16>(lrow, nsplit, split_stride, E, k, lane, lds);
 }
 
 }  // namespace moe
