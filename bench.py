@@ -657,16 +657,14 @@ def bench_int8(args):
 
     dom = int(np.argmax(launch_us))
     name, n, kk, g = launches[dom]
-    plan_gemv = T <= 4 and T * kk <= 32768
-    kname = ("int8_gemv_kernel<%d> (x in LDS, fp16 dot2 on byte-permuted codes)" % T if plan_gemv else
-             "int8_gemm_kernel (fp16 MFMA, exact per-group scaling) + split-K sum")
+    kname, uses_mfma = int8_kernel_label(T, n, kk, g)
     byt = alg_bytes(n, kk, g)
     fl = 2.0 * T * n * kk
     hbm = byt / (launch_us[dom] * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": f"{name}: {kname}", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": None,
             "algorithmic_bytes_per_launch": byt, "launch_us": round(float(launch_us[dom]), 3)}
-    if not plan_gemv:
+    if uses_mfma:
         tf = fl / (launch_us[dom] * 1e-6) / 1e12
         roof["mfma_tflops"] = round(tf, 2)
         roof["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
@@ -730,6 +728,34 @@ def bench_int8(args):
         result["cpu_baseline"] = {"value": round(tok_s, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
                                   "kind": "oracle", "sample": sample}
     print(json.dumps(result), flush=True)
+
+
+def int8_kernel_label(T, N, K, G):
+    """(name, uses matrix cores) of what moe_int8_linear runs for a shape: the
+    library's plan rules (few tokens: a GEMV, the row-split one on narrow
+    matrices; 5-16 tokens on wide matrices: the matrix-core GEMV; otherwise
+    the GEMM, loading its whole K range at once up to K = 320, else split
+    over K while the output tiles alone would leave the chip idle)."""
+    narrow = (N + 3) // 4 < 2048 and K >= 1024
+    if 1 <= T <= 4 and narrow:
+        return f"int8_gemv_rowsplit_kernel<{T}> (one weight row per workgroup, K split over its waves)", False
+    if 1 <= T <= 4 and T * K * 2 + T * (K // 16) * 4 <= 65536:
+        return f"int8_gemv_kernel<{T}> (x in LDS, fp16 dot2 on byte-permuted codes)", False
+    if 4 < T <= 16 and not narrow and T * (K // 8 + 1) * 16 <= 65536:
+        return "int8_gemv_mfma_kernel (matrix-core GEMV, codes as the B operand)", True
+    if K <= 320:
+        return (f"int8_gemm_short_kernel<{K // 64}, {G // 64}> (fp16 MFMA, exact per-group scaling, "
+                "every load of the tile at once)"), True
+    tiles = -(-T // 128) * -(-N // 128)
+    unit = max(G, 64)
+    units = K // unit
+    ks = 1
+    if tiles < 256:
+        ks = min(-(-256 // tiles), units // max(256 // unit, 1), 16)
+        ks = max(ks, 1)
+    kslice = -(-units // ks) * unit
+    split = -(-K // kslice) > 1
+    return ("int8_gemm_kernel (fp16 MFMA, exact per-group scaling)" + (" + split-K sum" if split else "")), True
 
 
 def cpu_baseline(layer, xs, T, k, budget_s, synth):
