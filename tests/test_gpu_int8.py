@@ -275,3 +275,28 @@ def test_int8_random_shape_sweep(T, N, K, G):
     g = as_f64(run(*to_dev(layer), T, N, K, G))
     o = oracle.int8_linear(layer["x"], layer["packed"], layer["scales"], G)
     compare(g, o, label)
+
+
+@pytest.mark.parametrize("T,N,K,G", [(512, 8192, 8192, 64), (512, 8192, 16384, 128)])
+def test_int8_gemm_scale_chunks(T, N, K, G):
+    # 256 output tiles, so K is not split: one workgroup's K range holds 128
+    # scale groups, and the GEMM restages its rows' scales in LDS after the
+    # first 64; the oracle on a seeded sample of outputs
+    label = f"int8 scale chunks T={T} N={N} K={K} G={G}"
+    say(label)
+    rng = np.random.default_rng(K + G)
+    gen = torch.Generator(device="cuda").manual_seed(K + G)
+    p = torch.randint(-2**31, 2**31 - 1, (N, K // 4), dtype=torch.int32, device="cuda", generator=gen)
+    s = (torch.randn(N, K // G, device="cuda", generator=gen).abs() * 4e-4).to(torch.bfloat16).view(torch.int16)
+    x = torch.randn(T, K, device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+    out = run(x, p, s, T, N, K, G)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 16)]))
+    rows = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.integers(0, N, 384)]))
+    xs = x[torch.from_numpy(toks).cuda()].cpu().numpy().view(np.uint16)
+    ps = p[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ss = s[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)
+    o = oracle.int8_linear(xs, ps, ss, G)
+    g = as_f64(out[torch.from_numpy(toks).cuda()][:, torch.from_numpy(rows).cuda()])
+    compare(g, o, label)
+    del p, s, x, out
+    torch.cuda.empty_cache()
