@@ -560,3 +560,15 @@ def test_random_shape_sweep(T, H, I, E, k, shared, group):
     shape = synth.LayerShape(tokens=T, hidden=H, experts=E, top_k=k, inter=I, group=group)
     host = synth.make_layer(shape, seed=7000 + T + E, shared=shared)
     run_and_check(host, label=f"sweep T={T} H={H} I={I} E={E} k={k} shared={shared} group={group}")
+
+
+def test_topk_one_split_many_experts():
+    """8192 tokens over 1024 experts (hidden 256): 512 router output tiles, so
+    the router GEMM does not split K and the top-k kernel runs its one-split
+    variant with 16 experts per lane.  Routing is checked for every token,
+    outputs for sampled ones."""
+    shape = synth.LayerShape(tokens=8192, hidden=256, experts=1024, top_k=8, inter=128)
+    host = synth.make_layer(shape, seed=8192)
+    rng = np.random.default_rng(8192)
+    tokens = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 30, replace=False)]))
+    run_and_check(host, tokens=tokens, label="top-k one split, T=8192 E=1024")
