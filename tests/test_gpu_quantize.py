@@ -97,3 +97,39 @@ def test_quantized_weights_drive_the_layer():
     clip = np.abs(x).reshape(256, 2, 128) > 7.5 * s[:, :, None]
     # unclipped inputs are within half a level of their code
     assert np.all(err[~clip] <= 0.5 * np.broadcast_to(s[:, :, None], err.shape)[~clip] * (1 + 1e-12))
+
+
+def _sweep_weights(rows, cols, kind, seed):
+    """Seeded bf16 weights of one distribution: normal, heavy-tailed
+    (Student t, 2 degrees of freedom), sparse (90 % exact zeros), row scales
+    spread over 10^-15 .. 10^15, or near-constant groups."""
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        w = rng.standard_normal((rows, cols)) * 0.02
+    elif kind == "heavy":
+        w = rng.standard_t(2.0, (rows, cols)) * 0.01
+    elif kind == "sparse":
+        w = rng.standard_normal((rows, cols)) * (rng.random((rows, cols)) < 0.1)
+    elif kind == "scaled":
+        w = rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-15.0, 15.0, (rows, 1))
+    else:
+        w = 0.5 + 1e-3 * rng.standard_normal((rows, cols))
+    return synth.bf16_bits(w.astype(np.float32))
+
+
+def _sweep_cases(n=20, seed=99):
+    rng = np.random.default_rng(seed)
+    kinds = ["normal", "heavy", "sparse", "scaled", "near-constant"]
+    out = []
+    for i in range(n):
+        group = int(rng.choice([64, 128]))
+        out.append((int(rng.integers(1, 200)), group * int(rng.integers(1, 4096 // group + 1)), group,
+                    kinds[i % len(kinds)], 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("rows,cols,group,kind,seed", _sweep_cases())
+def test_quantize_random_sweep(rows, cols, group, kind, seed):
+    # the GPU quantizer bit-exact against the oracle on random shapes and
+    # value distributions
+    check(_sweep_weights(rows, cols, kind, seed), f"sweep {kind} {rows}x{cols}", group)
