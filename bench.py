@@ -316,7 +316,7 @@ def main():
     else:
         achieved = w13_flops / (w13_us * 1e-6) / 1e12
         # the whole-expert GEMM runs from 64 slots per expert on average at group 128
-        big = args.group == 128 and S >= 64 * E
+        big = S >= 64 * E
         kname = ("moe_gemm_big_kernel<kRoutedW13> (whole-expert gate/up grouped GEMM: one workgroup per "
                  "chunk of up to 192 rows of one expert and 256 weight rows, fp16 MFMA 32x32x16 on INT4 "
                  "weights dequantised exactly in registers, SiLU-gate epilogue)" if big else

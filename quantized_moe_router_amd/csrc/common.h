@@ -401,7 +401,7 @@ constexpr int kBigRows = 192;
 constexpr int kBigMinRowsPerExpert = 64;
 inline bool routed_big(const Dims &d)
 {
-    return d.gsh == 2 && (long)d.S >= (long)kBigMinRowsPerExpert * d.E;   // group 128
+    return (long)d.S >= (long)kBigMinRowsPerExpert * d.E;   // group 128 or 64
 }
 // Rows per routed tile list entry.
 inline int routed_tile_rows(const Dims &d)

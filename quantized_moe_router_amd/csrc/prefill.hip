@@ -531,7 +531,8 @@ constexpr int kBigMaxGroups = kMaxHidden / kGroup;   // scales per weight row
 __host__ __device__ constexpr int big_waves(int mode) { return mode == kRoutedW2 ? 8 : 4; }
 constexpr int kBigMaxGroups6 = kMaxHidden / kShGroup;   // INT6 scales per weight row
 
-template <int MODE>
+// QG: INT4 scale groups per 128-input stage (1: group 128, 2: group 64).
+template <int MODE, int QG>
 __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void moe_gemm_big_kernel(GemmArgs g, int nblocks, int nbg)
 {
     static_assert(kBigKS == kGroup, "one INT4 weight group per stage");
@@ -540,8 +541,9 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
     // the shared expert: INT6 codes in groups of 64 (two scale groups per
     // stage), every token a row (chunk c = tokens [192 c, 192 c + 192))
     constexpr bool kInt6 = MODE == kSharedW13 || MODE == kSharedW2;
-    constexpr int kScPerStage = kInt6 ? 2 : 1;
-    constexpr int kScRows = kInt6 ? kBigMaxGroups6 : kBigMaxGroups;
+    static_assert(QG == 1 || (QG == 2 && !kInt6), "INT6 groups are set by the lane half");
+    constexpr int kScPerStage = kInt6 ? 2 : QG;
+    constexpr int kScRows = kInt6 ? kBigMaxGroups6 : kBigMaxGroups * QG;
     constexpr int kBigWaves = big_waves(MODE);
     constexpr int kBigThreads = kBigWaves * kWave;
     constexpr int kRowGroups = kBigWaves / 4;
@@ -682,14 +684,27 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
                 rb[set][nt][1] = q[2];
             }
         };
-        // fp16 scale pairs of global stage gs for this lane's two rows
-        auto scales_of = [&](int gs, h2_t (&s2)[2]) {
-            const int sg = kInt6 ? 2 * gs + half : gs;   // INT6: the lane half's group of 64
+        // fp16 scale pairs of global stage gs for this lane's two rows:
+        // [inputs 0-63 / 64-127 of the stage][nt].  INT6: the lane half's group
+        // of 64 (both entries); INT4 group 64: groups 2 gs and 2 gs + 1 (MFMA
+        // step j reads group j / 4); INT4 group 128: the stage's one group.
+        auto scales_of = [&](int gs, h2_t (&s2)[2][2]) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) s2[nt] = scale_pair(s_sc[sg][64 * cg + 32 * nt + col]);
+            for (int nt = 0; nt < 2; ++nt) {
+                const int c = 64 * cg + 32 * nt + col;
+                if constexpr (kInt6) {
+                    s2[0][nt] = s2[1][nt] = scale_pair(s_sc[2 * gs + half][c]);
+                } else if constexpr (QG == 2) {
+                    s2[0][nt] = scale_pair(s_sc[2 * gs][c]);
+                    s2[1][nt] = scale_pair(s_sc[2 * gs + 1][c]);
+                } else {
+                    s2[0][nt] = s2[1][nt] = scale_pair(s_sc[gs][c]);
+                }
+            }
         };
         // weight operands of MFMA step j (0..7) of the weight group in `set`
-        auto dequant_step = [&](int set, const h2_t (&s2)[2], int j, f16x8_t (&out)[2]) {
+        auto dequant_step = [&](int set, const h2_t (&s2g)[2][2], int j, f16x8_t (&out)[2]) {
+            const h2_t (&s2)[2] = s2g[j >> 2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 if constexpr (kInt6) {
@@ -763,7 +778,7 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
         // are loaded during the previous block's last ones.
         auto stage = [&](int gs, int set, int nset) __attribute__((always_inline)) {
             const int ngs = min(gs + 2, nst_all - 1);
-            h2_t s2c[2];
+            h2_t s2c[2][2];
             scales_of(gs, s2c);
             // the activations in the weights' K order: step j of half h is
             // K = 64 (j / 4) + 32 h + 8 (j % 4) for INT4, 64 h + 32 (j / 4) +
@@ -792,7 +807,7 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
                             af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * kBigLdsRow + ko);
                         dequant_step(set, s2c, j + 1, bnext);
                     } else {
-                        h2_t s2n[2];
+                        h2_t s2n[2][2];
                         scales_of(min(gs + 1, nst_all - 1), s2n);
                         dequant_step(nset, s2n, 0, bnext);   // the next stage's first step
                     }
@@ -837,7 +852,7 @@ __global__ __launch_bounds__(big_waves(MODE) * kWave, 8 / big_waves(MODE)) void 
 #pragma unroll
         for (int o = 0; o < NO; ++o) load_a_pass(min(1, nst_all - 1), o);
         if constexpr (MA > 0) {
-            h2_t s20[2];
+            h2_t s20[2][2];
             scales_of(0, s20);
             dequant_step(0, s20, 0, bcur);
         }
@@ -912,6 +927,7 @@ constexpr int kDnMaxK = 768;                   // longest K held in LDS
 constexpr int kDnLdsRow = kDnMaxK + 8;         // padded row, fp16 elements
 static_assert(2 * kDnRows == kBigRows, "two halves per chunk");
 
+template <int QG>
 __global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmArgs g)
 {
     __shared__ __align__(16) _Float16 s_h[kDnRows * kDnLdsRow];
@@ -991,7 +1007,7 @@ __global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmAr
         };
         zero_acc();
         u32x4_t rb[3][2][2];   // weight stages in flight: [set][nt][piece]
-        uint16_t rs[3][2];     // their bf16 scales
+        uint32_t rs[3][2];     // their bf16 scales: the stage's first and second 64 inputs
         // global stage gs: pass gs / nst (output group wave + 8 pass), K stage gs % nst
         auto load_b = [&](int gs, int set) __attribute__((always_inline)) {
             const int ps = gs / nst, s = gs - ps * nst;
@@ -1002,12 +1018,26 @@ __global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmAr
                 const u32x4_t *q = reinterpret_cast<const u32x4_t *>(bpe + (size_t)n * bstride) + 4 * s + half;
                 rb[set][nt][0] = q[0];
                 rb[set][nt][1] = q[2];
-                rs[set][nt] = bse[(size_t)n * nst + s];
+                if constexpr (QG == 2) {
+                    // groups 2 s and 2 s + 1 of the row: one aligned word (a row holds 2 nst scales)
+                    rs[set][nt] = reinterpret_cast<const uint32_t *>(bse)[(size_t)n * nst + s];
+                } else {
+                    rs[set][nt] = bse[(size_t)n * nst + s];
+                }
             }
         };
-        auto dequant_step = [&](int set, const h2_t (&s2)[2], int j, f16x8_t (&out)[2]) __attribute__((always_inline)) {
+        // the stage's fp16 scale pairs: [inputs 0-63 / 64-127][nt] (the same scale at group 128)
+        auto stage_scales = [&](int set, h2_t (&s2)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) out[nt] = dequant_int4_f16(rb[set][nt][j >> 2][j & 3], s2[nt]);
+            for (int nt = 0; nt < 2; ++nt) {
+                s2[0][nt] = scale_pair((uint16_t)rs[set][nt]);
+                s2[1][nt] = QG == 2 ? scale_pair((uint16_t)(rs[set][nt] >> 16)) : s2[0][nt];
+            }
+        };
+        // step j reads inputs 64 (j / 4) + 32 h + 8 (j % 4) of the stage: group j / 4 of 64
+        auto dequant_step = [&](int set, const h2_t (&s2)[2][2], int j, f16x8_t (&out)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) out[nt] = dequant_int4_f16(rb[set][nt][j >> 2][j & 3], s2[j >> 2][nt]);
         };
         auto store_pass = [&](int ps) __attribute__((always_inline)) {
             const int n0 = 64 * (wave + kDnWaves * ps);
@@ -1046,7 +1076,8 @@ __global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmAr
         auto stage = [&](int gs, int set, int nset) __attribute__((always_inline)) {
             load_b(min(gs + 2, nst_all - 1), (set + 2) % 3);
             const int ps = gs / nst, s = gs - ps * nst;
-            const h2_t s2c[2] = {scale_pair(rs[set][0]), scale_pair(rs[set][1])};
+            h2_t s2c[2][2];
+            stage_scales(set, s2c);
             // step j of lane half h reads K = 64 (j / 4) + 32 h + 8 (j % 4) of the stage
             const _Float16 *A = s_h + col * ldsrow + kBigKS * s + 32 * half;
             f16x8_t af[2][MA];
@@ -1063,7 +1094,8 @@ __global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmAr
                         af[(j + 1) & 1][mt] = *reinterpret_cast<const f16x8_t *>(A + 32 * mt * ldsrow + ko);
                     dequant_step(set, s2c, j + 1, bnext);
                 } else {
-                    const h2_t s2n[2] = {scale_pair(rs[nset][0]), scale_pair(rs[nset][1])};
+                    h2_t s2n[2][2];
+                    stage_scales(nset, s2n);
                     dequant_step(nset, s2n, 0, bnext);   // the next stage's first step
                 }
 #pragma unroll
@@ -1089,7 +1121,8 @@ __global__ __launch_bounds__(kDnThreads, 1) void moe_down_resident_kernel(GemmAr
         load_b(0, 0);
         load_b(min(1, nst_all - 1), 1);
         {
-            const h2_t s20[2] = {scale_pair(rs[0][0]), scale_pair(rs[0][1])};
+            h2_t s20[2][2];
+            stage_scales(0, s20);
             dequant_step(0, s20, 0, bcur);
         }
         int gs = 0;
@@ -1316,14 +1349,17 @@ static hipError_t launch_gemm(const GemmArgs &g, int ntiles_max, int nblocks, hi
         const unsigned grid = groups * 8 * nblocks;
         if (MODE == kRoutedW2 && big && g.K <= kDnMaxK) {
             // two workgroups per chunk slot, one per half of its row tiles
-            moe_down_resident_kernel<<<groups * 8 * 2, kDnThreads, 0, st>>>(g);
+            if (g64) moe_down_resident_kernel<2><<<groups * 8 * 2, kDnThreads, 0, st>>>(g);
+            else moe_down_resident_kernel<1><<<groups * 8 * 2, kDnThreads, 0, st>>>(g);
             return hipGetLastError();
         }
         if (big) {
             // chunks: about one per expert for balanced routing (the list has
             // room for at most S / kBigRows + E, about twice that)
             const int nbg = MODE == kRoutedW2 ? big_blocks_per_wg(nblocks, g.K / kBigKS, ntiles_max / 2) : 1;
-            moe_gemm_big_kernel<MODE><<<groups * 8 * (nblocks / nbg), big_waves(MODE) * kWave, 0, st>>>(g, nblocks, nbg);
+            const unsigned bgrid = groups * 8 * (nblocks / nbg);
+            if (g64) moe_gemm_big_kernel<MODE, 2><<<bgrid, big_waves(MODE) * kWave, 0, st>>>(g, nblocks, nbg);
+            else moe_gemm_big_kernel<MODE, 1><<<bgrid, big_waves(MODE) * kWave, 0, st>>>(g, nblocks, nbg);
             return hipGetLastError();
         }
         if (g.small_rows > 0) {
@@ -1356,7 +1392,7 @@ hipError_t launch_shared_expert(const ExpertArgs &a, const Dims &d, const Worksp
         // whole-chunk gate/up GEMM: 192 tokens per workgroup and weight block
         const int groups = (d.T + 8 * kBigRows - 1) / (8 * kBigRows);
         const int nb13 = d.sh_I / 128;
-        moe_gemm_big_kernel<kSharedW13><<<groups * 8 * nb13, big_waves(kSharedW13) * kWave, 0, st>>>(gs, nb13, 1);
+        moe_gemm_big_kernel<kSharedW13, 1><<<groups * 8 * nb13, big_waves(kSharedW13) * kWave, 0, st>>>(gs, nb13, 1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if ((e = launch_gemm<kSharedW13>(gs, (d.T + kMT - 1) / kMT, d.sh_I / 128, st)) != hipSuccess) {
         return e;

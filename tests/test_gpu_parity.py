@@ -218,15 +218,18 @@ def test_shared_expert_whole_chunk_gemm_ragged():
     run_and_check(host, tokens=tokens, label="shared whole-chunk ragged T=6211")
 
 
+@pytest.mark.parametrize("group", [128, 64])
 @pytest.mark.parametrize("H,I", [(256, 128), (768, 384), (512, 768), (512, 896)])
-def test_whole_expert_gemm_row_counts(H, I):
+def test_whole_expert_gemm_row_counts(H, I, group):
     """Caller routing that gives the experts every row count the whole-expert
     grouped GEMM distinguishes: 0, 1 and 2 to 6 row tiles of 32 (ragged and
     full), exactly one chunk (192 rows) and counts that split into two or
     three chunks; ids may repeat within a token.  Every token is checked.
     The down projection keeps half a chunk's h rows in LDS up to I = 768
     (with fewer 64-column output groups than waves at H = 256, and an uneven
-    share at H = 768); I = 896 takes the block-loop kernel instead."""
+    share at H = 768); I = 896 takes the block-loop kernel instead.  At group
+    64 a 128-input stage holds two scale groups (MFMA step j reads group
+    j / 4)."""
     counts = [0, 1, 5, 31, 32, 33, 63, 64, 96, 150, 160, 191, 192, 193, 300, 385]
     k = 4
     S = sum(counts)
@@ -234,18 +237,19 @@ def test_whole_expert_gemm_row_counts(H, I):
     S = sum(counts)
     T = S // k
     assert S >= 64 * 16   # the whole-expert path is the one taken
-    shape = synth.LayerShape(tokens=T, hidden=H, experts=16, top_k=k, inter=I)
-    host = synth.make_layer(shape, seed=77 + H)
+    shape = synth.LayerShape(tokens=T, hidden=H, experts=16, top_k=k, inter=I, group=group)
+    host = synth.make_layer(shape, seed=77 + H + group)
     rng = np.random.default_rng(H)
     ids = rng.permutation(np.repeat(np.arange(16), counts)).astype(np.int32).reshape(T, k)
     w = rng.random((T, k)).astype(np.float32)
     dev = synth.to_device(host)
-    L = MoeInt4Layer(dev, k)
+    L = MoeInt4Layer(dev, k, group=group)
     out = L.experts(dev["x"], torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
     torch.cuda.synchronize()
     ref = oracle.experts(host["x"], ids, w.astype(np.float64), host["w13_packed"], host["w13_scales"],
-                         host["w2_packed"], host["w2_scales"])
-    check_output(bf16_to_f64(out.cpu().numpy()), ref, label=f"whole-expert GEMM row counts H={H} I={I}")
+                         host["w2_packed"], host["w2_scales"], group=group)
+    check_output(bf16_to_f64(out.cpu().numpy()), ref,
+                 label=f"whole-expert GEMM row counts H={H} I={I} group={group}")
     assert_workspaces_clean(L)
 
 
@@ -572,3 +576,14 @@ def test_topk_one_split_many_experts():
     rng = np.random.default_rng(8192)
     tokens = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 30, replace=False)]))
     run_and_check(host, tokens=tokens, label="top-k one split, T=8192 E=1024")
+
+
+def test_group64_prefill8192_share():
+    """Group 64 through the whole-expert GEMMs at the real width: 8192 tokens,
+    top-10 over 64 experts (1,280 rows per expert, seven chunks each) and the
+    shared expert; routing for every token, outputs for sampled ones."""
+    shape = synth.LayerShape(tokens=8192, experts=64, group=64)
+    host = synth.make_layer(shape, seed=6464, shared=True)
+    rng = np.random.default_rng(6464)
+    tokens = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 30, replace=False)]))
+    run_and_check(host, tokens=tokens, label="group64 real-width T=8192 E=64 shared")
