@@ -701,18 +701,18 @@ __global__ __launch_bounds__(256) void w2_combine_kernel(const float *__restrict
     if (i >= d.T * n4) return;
     const int t = i / n4, c = i - t * n4;
     const float4 *col = reinterpret_cast<const float4 *>(yp) + c;
-    // rows of slots t k .. t k + k - 1, then the shared row: eight loads in
-    // flight at a time (clamped, unconditional; a clamped duplicate is not
-    // added), summed in slot order
+    // rows of slots t k .. t k + k - 1, then the shared row: twelve loads in
+    // flight at a time (top-10 and the shared row in one round trip; clamped,
+    // unconditional; a clamped duplicate is not added), summed in slot order
     const int nrows = d.k + (d.sh_I > 0 ? 1 : 0);
     auto row_of = [&](int j) { return j < d.k ? (size_t)(t * d.k + j) : (size_t)(d.S + t); };
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < nrows; j0 += 8) {
-        float4 v[8];
+    for (int j0 = 0; j0 < nrows; j0 += 12) {
+        float4 v[12];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = col[row_of(min(j0 + u, nrows - 1)) * n4];
+        for (int u = 0; u < 12; ++u) v[u] = col[row_of(min(j0 + u, nrows - 1)) * n4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 12; ++u)
             if (j0 + u < nrows) {
                 acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
             }
