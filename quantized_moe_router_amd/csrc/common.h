@@ -18,6 +18,7 @@ constexpr int kShGroup = 64;     // INT6 group (shared expert)
 constexpr int kDecodeMaxTokens = 16;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte load of data read exactly once (weights): non-temporal hint.
@@ -35,11 +36,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, round to nearest even (inputs are finite).
+// fp32 -> bf16 with round to nearest even, by the packed hardware convert
+// (v_cvt_pk_bf16_f32): the same bits as adding 0x7FFF plus the kept lsb and
+// truncating, for every non-NaN input; a NaN stays a NaN.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi)
+{
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return f32x2_to_bf16x2(f, 0.f) & 0xFFFFu;
 }
 
 // c + a.lo*b.lo + a.hi*b.hi on bf16 pairs (v_dot2c_f32_bf16).

@@ -718,8 +718,8 @@ __global__ __launch_bounds__(256) void w2_combine_kernel(const float *__restrict
             }
     }
     uint2 o;
-    o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
-    o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+    o.x = f32x2_to_bf16x2(acc.x, acc.y);
+    o.y = f32x2_to_bf16x2(acc.z, acc.w);
     reinterpret_cast<uint2 *>(out + (size_t)t * d.H)[c] = o;
 }
 

@@ -716,7 +716,7 @@ __global__ __launch_bounds__(kGmThreads, 2) void int8_gemm_kernel(Int8GemmArgs g
             if (vec) {
                 if (g.ksplit == 1)
                     *reinterpret_cast<uint2 *>(g.out + o) =
-                        make_uint2(f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16));
+                        make_uint2(f32x2_to_bf16x2(v.x, v.y), f32x2_to_bf16x2(v.z, v.w));
                 else
                     *reinterpret_cast<float4 *>(part + o) = v;
             } else {
@@ -886,7 +886,7 @@ __global__ __launch_bounds__(kGoThreads, 1) void int8_gemm_short_kernel(Int8Gemm
             const size_t o = (size_t)(m0 + m) * g.N + nn;
             if (vec) {
                 *reinterpret_cast<uint2 *>(g.out + o) =
-                    make_uint2(f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16), f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16));
+                    make_uint2(f32x2_to_bf16x2(v.x, v.y), f32x2_to_bf16x2(v.z, v.w));
             } else {
                 const float e4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -923,8 +923,8 @@ __global__ __launch_bounds__(kSumThreads) void int8_splitk_sum_kernel(const floa
                 a.z += v[s].z;
                 a.w += v[s].w;
             }
-        const uint32_t lo = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
-        const uint32_t hi = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+        const uint32_t lo = f32x2_to_bf16x2(a.x, a.y);
+        const uint32_t hi = f32x2_to_bf16x2(a.z, a.w);
         if ((reinterpret_cast<uintptr_t>(out + i) & 7) == 0) {
             *reinterpret_cast<uint2 *>(out + i) = make_uint2(lo, hi);
         } else {

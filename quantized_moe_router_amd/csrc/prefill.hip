@@ -1208,8 +1208,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     uint32_t o0[4], o1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        o0[r] = f32_to_bf16(acc[4 * r]) | (f32_to_bf16(acc[4 * r + 2]) << 16);
-        o1[r] = f32_to_bf16(acc[4 * r + 1]) | (f32_to_bf16(acc[4 * r + 3]) << 16);
+        o0[r] = f32x2_to_bf16x2(acc[4 * r], acc[4 * r + 2]);
+        o1[r] = f32x2_to_bf16x2(acc[4 * r + 1], acc[4 * r + 3]);
     }
     uint16_t *orow = out + t * H + 64 * (c / 4) + 8 * (c % 4);
     *reinterpret_cast<uint4 *>(orow) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
