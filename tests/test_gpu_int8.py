@@ -106,6 +106,10 @@ SMALL = [
     (200, 333, 192, 64),   # short-K GEMM: three stages, ragged row tile
     (77, 1000, 320, 64),   # short-K GEMM: the hyper-connection up row length
     (260, 513, 256, 64),   # short-K GEMM: three token tiles, N = 2 x 256 + 1
+    (96, 300, 320, 64),    # short-K GEMM: 96 tokens, three 32-row MFMA tiles
+    (512, 10240, 320, 64), # short-K GEMM: the hyper-connection up projection at 512 tokens
+    (2100, 8192, 320, 64), # short-K GEMM: 17 x 32 tiles, 52-token tail
+    (1000, 16384, 256, 128),  # short-K GEMM, group 128: 8 x 64 tiles, 104-token tail
 ]
 
 
