@@ -304,3 +304,40 @@ def test_int8_gemm_scale_chunks(T, N, K, G):
     compare(g, o, label)
     del p, s, x, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,N,K,G", [
+    (1, 2000, 128, 64),     # dot-product GEMV
+    (4, 2000, 1152, 128),   # row-split GEMV
+    (8, 777, 256, 64),      # matrix-core GEMV
+    (40, 300, 320, 64),     # short-K GEMM
+    (200, 96, 4096, 64),    # GEMM with its K split and the partial sum
+])
+def test_int8_bf16_rounding_ties_exact(T, N, K, G):
+    # One-hot activations (x[t, c_t] = 1): every output is code * scale,
+    # exact in fp32 whatever the summation order (at most 16 significant
+    # bits), so the one bf16 rounding of the output must be round to nearest
+    # even of the oracle's exact value, bit for bit.  Scales (1 + m/128) 2^e
+    # make many of those values fall exactly halfway between two bf16 values.
+    label = f"int8 ties T={T} N={N} K={K} G={G}"
+    say(label)
+    rng = np.random.default_rng(T * 131 + K)
+    x = np.zeros((T, K), dtype=np.uint16)
+    x[np.arange(T), rng.integers(0, K, T)] = 0x3F80
+    q = rng.integers(-128, 128, (N, K))
+    packed = np.ascontiguousarray((q + 128).astype(np.uint8)).view("<i4").reshape(N, K // 4)
+    e = rng.integers(-6, 3, (N, K // G))
+    scales = (((e + 127) << 7) | rng.integers(0, 128, (N, K // G))).astype(np.uint16)
+    g = as_f64(run(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(packed).cuda(),
+                   torch.from_numpy(scales.view(np.int16)).cuda(), T, N, K, G))
+    o = oracle.int8_linear(x, packed, scales, G)
+    o32 = o.astype(np.float32)
+    assert np.array_equal(o32.astype(np.float64), o), "every exact value fits fp32"
+    want = torch.from_numpy(o32).to(torch.bfloat16).double().numpy()   # round to nearest even
+    bits = o32.view(np.uint32)
+    tie = (bits & 0xFFFF) == 0x8000
+    up = tie & ((bits >> 16) & 1 == 1)
+    assert tie.sum() >= 50 and up.sum() >= 10 and (tie & ~up).sum() >= 10, (label, int(tie.sum()), int(up.sum()))
+    bad = np.argwhere(g != want)
+    assert bad.size == 0, (f"{label}: {len(bad)} outputs differ, first {bad[:3].tolist()} "
+                           f"gpu {g[tuple(bad[0])]} exact {o[tuple(bad[0])]} rne {want[tuple(bad[0])]}")
